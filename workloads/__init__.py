@@ -1,0 +1,213 @@
+"""Seeded synthetic inputs for the block-restricted sparse-MoE FFN.
+
+This module only draws random numbers and casts them to the storage formats
+the operation consumes (fp32, bf16, OCP fp8 e4m3 with fp32 128x128 block
+scales).  It holds none of the operation's arithmetic: no routing, no
+softmax, no FFN.  Both the CPU oracle and the HIP library receive exactly the
+bytes produced here.
+
+Workload shapes follow the Clover-35B-A3B-Preview model card (CMF files page,
+introduction): 256 routed experts, top-8 per token, one shared expert, answers
+written in 32-token blocks whose experts are restricted to the set carrying 90%
+of the block's routing ("Usage" section).  Hidden and intermediate sizes are
+not given on the pages; the sizes below are the synthetic stand-ins used
+throughout this repository.  The fp8 format (E4M3 weights in 128x128 blocks,
+bf16 activations) follows InfiniLM PR #584 ("Benchmark" section).
+
+Recipe (per workload): ``numpy.random.default_rng(seed)``; draws in the order
+x, router_w, router_b (skewed workloads only), then for each routed expert e in
+ascending order its W13[e] and W2[e] are drawn after all W13 (i.e. all W13
+first, expert by expert, then all W2 expert by expert), then shared W13, shared
+W2.  Every draw is ``standard_normal(shape, float32) * sigma``; the router bias
+uses sigma = ``bias_sigma``.  Router weights are rounded to bf16 and stored as
+fp32 (bf16-valued) whenever activations are bf16.
+"""
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import numpy as np
+
+# Storage dtype names shared by the oracle wrapper and the binding.
+F32 = "f32"
+BF16 = "bf16"
+FP8 = "fp8_e4m3"
+
+FP8_BLOCK = 128          # 128x128 weight blocks with one fp32 scale each
+FP8_MAX = 448.0          # largest finite OCP e4m3fn magnitude
+
+
+@dataclass(frozen=True)
+class Workload:
+    """Shape, dtypes and seed of one synthetic workload."""
+    name: str
+    num_blocks: int       # B
+    block_rows: int       # R_blk (8, 16 or 32)
+    hidden: int           # H
+    num_experts: int      # E
+    top_k: int            # k
+    inter: int            # I  (routed expert intermediate size)
+    shared_inter: int     # Is (shared expert intermediate size, 0 = none)
+    act_dtype: str        # F32 or BF16
+    weight_dtype: str     # F32, BF16 or FP8
+    mass_threshold: float
+    seed: int
+    sigma: float = 0.02
+    bias_sigma: Optional[float] = None
+
+    @property
+    def rows(self) -> int:
+        return self.num_blocks * self.block_rows
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    # one 8-row block, fp32 everywhere: the case the oracle finishes in well under a second
+    "tiny_fp32": Workload("tiny_fp32", 1, 8, 256, 16, 4, 128, 128, F32, F32, 0.9, seed=0),
+    # one 32-row block at the model's routing shape, bf16: weight-streaming bound
+    "block32_bf16": Workload("block32_bf16", 1, 32, 2048, 256, 8, 512, 512, BF16, BF16, 0.9, seed=1),
+    # same shapes with a per-expert router bias ~N(0,1): coreset sizes vary widely
+    "block32_skewed": Workload("block32_skewed", 1, 32, 2048, 256, 8, 512, 512, BF16, BF16, 0.9,
+                               seed=2, bias_sigma=1.0),
+    # 16 independent 32-row blocks per call, bf16
+    "blocks16_bf16": Workload("blocks16_bf16", 16, 32, 2048, 256, 8, 512, 512, BF16, BF16, 0.9, seed=3),
+    # 64 blocks x 32 rows, fp8 e4m3 expert weights with fp32 128x128 block scales
+    "blocks64_fp8": Workload("blocks64_fp8", 64, 32, 2048, 256, 8, 512, 512, BF16, FP8, 0.9, seed=4),
+}
+
+# Threshold / top-k sweep run on the skewed workload (1.0 = unrestricted top-k;
+# k = 4 is the "preview" routing variant).
+SKEWED_SWEEP = [(1.0, 8), (0.95, 8), (0.9, 8), (0.8, 8), (1.0, 4), (0.95, 4), (0.9, 4), (0.8, 4)]
+
+
+@dataclass
+class MoEInputs:
+    """Host copies of every input of one call, in storage format.
+
+    bf16 arrays hold raw uint16 bit patterns; fp8 arrays hold raw uint8 OCP
+    e4m3fn codes with a companion fp32 scale array of shape
+    [..., rows/128, cols/128].
+    """
+    wl: Workload
+    x: np.ndarray                       # [N, H]  f32 or uint16(bf16)
+    router_w: np.ndarray                # [E, H]  f32
+    router_b: Optional[np.ndarray]      # [E]     f32 or None
+    w13: np.ndarray                     # [E, 2I, H]
+    w13_scale: Optional[np.ndarray]     # [E, 2I/128, H/128] f32 (fp8 only)
+    w2: np.ndarray                      # [E, H, I]
+    w2_scale: Optional[np.ndarray]      # [E, H/128, I/128] f32 (fp8 only)
+    shared_w13: Optional[np.ndarray]    # [2Is, H]
+    shared_w13_scale: Optional[np.ndarray]
+    shared_w2: Optional[np.ndarray]     # [H, Is]
+    shared_w2_scale: Optional[np.ndarray]
+
+
+# ----------------------------------------------------------------------------
+# storage casts (input preparation only)
+# ----------------------------------------------------------------------------
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (round-to-nearest-even), returned as uint16 bits."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(a)
+    if nan.any():
+        out[nan] = 0x7FC0
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to fp32 (exact)."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def quantize_fp8_blocks(w: np.ndarray):
+    """Quantise a [..., rows, cols] fp32 array to OCP e4m3fn codes with one fp32
+    scale per 128x128 block: s = max|W_blk| / 448, q = RNE(W / s) (saturating).
+
+    Returns (codes uint8 [..., rows, cols], scales f32 [..., rows/128, cols/128]).
+    """
+    import torch
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    *lead, rows, cols = w.shape
+    assert rows % FP8_BLOCK == 0 and cols % FP8_BLOCK == 0
+    rb, cb = rows // FP8_BLOCK, cols // FP8_BLOCK
+    blk = w.reshape(*lead, rb, FP8_BLOCK, cb, FP8_BLOCK)
+    amax = np.abs(blk).max(axis=(-3, -1))                       # [..., rb, cb]
+    scale = (np.maximum(amax, np.float32(1e-30)) / np.float32(FP8_MAX)).astype(np.float32)
+    q = blk / scale[..., :, None, :, None]
+    q = np.clip(q, -FP8_MAX, FP8_MAX).astype(np.float32)
+    codes = torch.from_numpy(np.ascontiguousarray(q)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes.reshape(*lead, rows, cols).copy(), scale
+
+
+def _store_weight(w32: np.ndarray, dtype: str):
+    if dtype == F32:
+        return np.ascontiguousarray(w32, dtype=np.float32), None
+    if dtype == BF16:
+        return f32_to_bf16_bits(w32), None
+    if dtype == FP8:
+        return quantize_fp8_blocks(w32)
+    raise ValueError(dtype)
+
+
+# ----------------------------------------------------------------------------
+# generation
+# ----------------------------------------------------------------------------
+
+def generate(wl: Workload) -> MoEInputs:
+    """Draw every input of ``wl`` from its seed (see the module docstring)."""
+    rng = np.random.default_rng(wl.seed)
+    N, H, E, I, Is = wl.rows, wl.hidden, wl.num_experts, wl.inter, wl.shared_inter
+
+    def draw(shape, sigma):
+        return rng.standard_normal(shape, dtype=np.float32) * np.float32(sigma)
+
+    x32 = draw((N, H), wl.sigma)
+    x = f32_to_bf16_bits(x32) if wl.act_dtype == BF16 else x32
+    rw = draw((E, H), wl.sigma)
+    if wl.act_dtype == BF16:
+        rw = bf16_bits_to_f32(f32_to_bf16_bits(rw))
+    rb = draw((E,), wl.bias_sigma) if wl.bias_sigma is not None else None
+
+    w13_parts, w13_sc, w2_parts, w2_sc = [], [], [], []
+    for _ in range(E):
+        q, s = _store_weight(draw((2 * I, H), wl.sigma), wl.weight_dtype)
+        w13_parts.append(q)
+        w13_sc.append(s)
+    for _ in range(E):
+        q, s = _store_weight(draw((H, I), wl.sigma), wl.weight_dtype)
+        w2_parts.append(q)
+        w2_sc.append(s)
+    w13 = np.stack(w13_parts)
+    w2 = np.stack(w2_parts)
+    fp8 = wl.weight_dtype == FP8
+    w13_scale = np.stack(w13_sc) if fp8 else None
+    w2_scale = np.stack(w2_sc) if fp8 else None
+    if Is > 0:
+        sw13, sw13_s = _store_weight(draw((2 * Is, H), wl.sigma), wl.weight_dtype)
+        sw2, sw2_s = _store_weight(draw((H, Is), wl.sigma), wl.weight_dtype)
+    else:
+        sw13 = sw13_s = sw2 = sw2_s = None
+    return MoEInputs(wl, x, rw, rb, w13, w13_scale, w2, w2_scale, sw13, sw13_s, sw2, sw2_s)
+
+
+def with_arrays(inp: MoEInputs, **kw) -> MoEInputs:
+    """Copy of ``inp`` with some arrays replaced (used to build special cases)."""
+    return dataclasses.replace(inp, **kw)
+
+
+def row_sample(num_rows: int, count: int, seed: int) -> np.ndarray:
+    """Sorted sample of row indices used for sampled full-size parity checks.
+    Always includes the first and last row."""
+    rng = np.random.default_rng(seed + 7919)
+    count = min(count, num_rows)
+    picks = set(rng.choice(num_rows, size=count, replace=False).tolist())
+    picks.update({0, num_rows - 1})
+    return np.array(sorted(picks), dtype=np.int64)
