@@ -1,0 +1,263 @@
+"""Benchmark of the block-restricted sparse-MoE FFN on one MI355X.
+
+One step = one call of the whole hot path (router, per-block routing,
+permutation, gate/up GEMM + SwiGLU, down GEMM, combine with the shared
+expert) over one batch of synthetic blocks, with every input already resident
+in HBM.  The default workload is one 32-row bf16 block at the model's routing
+shape (H 2048, 256 experts, top-8, I 512, shared expert I 512, mass threshold
+0.9) -- the weight-streaming bound case.
+
+Successive steps cycle through `--layers` copies of the weights placed at
+different addresses (the experts of copy j are rotated by j*E/L, router
+included, so every copy routes to the same number of experts): like the
+consecutive MoE layers of a denoising pass, no step finds its weights in the
+256 MB MALL left by the previous one.
+
+Prints ONE JSON line (see the keys below).  Per-stage device times come from
+HIP events the library records on its own stream between its kernels
+(clover_moe_block_forward_staged), over the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "fp8_e4m3": 2500.0}  # fp8 weights run on bf16 MFMA
+
+
+def hip():
+    L = ctypes.CDLL("libamdhip64.so")
+    L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return L
+
+
+def layer_copies(dp, n_layers, E):
+    """Weight copies at new addresses with experts rotated by j*E/n_layers."""
+    import torch
+    import sparse_moe_ffn_softmax_amd as cm
+    layers = [dp.weights]
+    keep = []
+    t = dp.tensors
+    for j in range(1, n_layers):
+        sh = (j * E) // n_layers
+
+        def rot(a):
+            return None if a is None else torch.roll(a, shifts=sh, dims=0).contiguous()
+
+        def cp(a):
+            return None if a is None else a.clone()
+
+        c = dict(router_w=rot(t["router_w"]), router_b=rot(t["router_b"]), w13=rot(t["w13"]),
+                 w13_scale=rot(t["w13_scale"]), w2=rot(t["w2"]), w2_scale=rot(t["w2_scale"]),
+                 shared_w13=cp(t["shared_w13"]), shared_w13_scale=cp(t["shared_w13_scale"]),
+                 shared_w2=cp(t["shared_w2"]), shared_w2_scale=cp(t["shared_w2_scale"]))
+        keep.append(c)
+        layers.append(cm.make_weights(**c))
+    return layers, keep
+
+
+def source_digest(name: str) -> str:
+    p = os.path.join(ROOT, "sparse_moe_ffn_softmax_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str, src: str):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was
+    taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except ValueError:
+        return None
+    if d.get("source_sha256_16") != source_digest(src):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="block32_bf16")
+    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="rough budget of the oracle CPU-baseline leg (0 disables it)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU sharding is described in DESIGN.md but not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import sparse_moe_ffn_softmax_amd as cm
+    import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    K, tau = wl.top_k, wl.mass_threshold
+    N, H, E, I, Is, B = wl.rows, wl.hidden, wl.num_experts, wl.inter, wl.shared_inter, wl.num_blocks
+    t0 = time.time()
+    inp = W.generate(wl)
+    print(f"[bench] generated {wl.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    dp = cm.upload(inp)
+    layers, _keep = layer_copies(dp, args.layers, E)
+    ws = cm.alloc_workspace(dp.problem, K)
+    odt = torch.bfloat16 if wl.act_dtype == W.BF16 else torch.float32
+    out = torch.empty((N, H), dtype=odt, device="cuda")
+    total = args.warmup + args.steps
+    counts = torch.zeros((total, E), dtype=torch.int32, device="cuda")
+    routings = [cm.make_routing(expert_counts=counts[i]) for i in range(total)]
+
+    H_ = hip()
+    n_ev = cm.NUM_STAGES + 1
+    events = []
+    for _ in range(args.steps):
+        row = []
+        for _ in range(n_ev):
+            e = ctypes.c_void_p()
+            assert H_.hipEventCreate(ctypes.byref(e)) == 0
+            row.append(e.value)
+        events.append(row)
+
+    stream = torch.cuda.current_stream()
+    x = dp.tensors["x"]
+    for i in range(args.warmup):
+        cm.clover_moe_block_forward(dp.problem, layers[i % len(layers)], x, tau, K, out,
+                                    routings[i], ws, stream=stream)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    # timed region
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        i = args.warmup + s
+        cm.clover_moe_block_forward_staged(dp.problem, layers[i % len(layers)], x, tau, K, out,
+                                           routings[i], ws, events[s], stream=stream)
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    print(f"[bench] timed {args.steps} steps", file=sys.stderr, flush=True)
+
+    ms_per_step = (t_end - t_start) * 1e3 / args.steps
+    stage_ms = np.zeros((args.steps, cm.NUM_STAGES))
+    f = ctypes.c_float()
+    for s in range(args.steps):
+        for k in range(cm.NUM_STAGES):
+            assert H_.hipEventElapsedTime(ctypes.byref(f), events[s][k], events[s][k + 1]) == 0
+            stage_ms[s, k] = f.value
+    for row in events:
+        for e in row:
+            H_.hipEventDestroy(e)
+
+    cnt = counts[args.warmup:].cpu().numpy().astype(np.int64)  # [steps, E]
+    touched = (cnt > 0).sum(1)
+    pairs = cnt.sum(1)
+    wsz = {W.F32: 4, W.BF16: 2, W.FP8: 1}[wl.weight_dtype]
+    asz = {W.F32: 4, W.BF16: 2}[wl.act_dtype]
+    hsz = 4 if wl.act_dtype == W.F32 else 2
+    fp8 = wl.weight_dtype == W.FP8
+    sc_up = (2 * I // 128) * (H // 128) * 4 if fp8 else 0
+    sc_dn = (H // 128) * (I // 128) * 4 if fp8 else 0
+    sc_up_s = (2 * Is // 128) * (H // 128) * 4 if fp8 and Is else 0
+    sc_dn_s = (H // 128) * (Is // 128) * 4 if fp8 and Is else 0
+    n_sh = N if Is else 0
+    # algorithmic bytes per launch of the gate/up kernel: weights of the touched
+    # experts (+ shared), x once, h written once
+    up_bytes = (touched * (2 * I * H * wsz + sc_up) + (2 * Is * H * wsz + sc_up_s) + N * H * asz
+                + (pairs * I + n_sh * Is) * hsz)
+    dn_bytes = (touched * (H * I * wsz + sc_dn) + (H * Is * wsz + sc_dn_s) + (pairs * I + n_sh * Is) * hsz
+                + (pairs + n_sh) * H * 4)
+    # whole call (weights, router, x in, out)
+    call_bytes = (touched * (3 * H * I * wsz + sc_up + sc_dn) + (3 * H * Is * wsz + sc_up_s + sc_dn_s)
+                  + 4 * E * H + N * H * 2 * asz)
+    mfma_flops = 6.0 * H * I * pairs + 6.0 * H * Is * N
+    router_flops = 2.0 * N * H * E
+
+    mean_stage = stage_ms.mean(0)
+    dom = int(np.argmax(mean_stage))
+    dom_name = cm.STAGE_NAMES[dom]
+    dom_bytes = {3: up_bytes, 4: dn_bytes}.get(dom)
+    device_ms = stage_ms.sum(1)
+    if dom_bytes is not None:
+        achieved = float(dom_bytes.sum() / (stage_ms[:, dom].sum() * 1e-3) / 1e9)
+        traffic = measured_traffic(dom_name, wl.name, "expert_gemm.hip")
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                    "traffic": traffic, "kernel": f"expert_{'up' if dom == 3 else 'down'}_kernel",
+                    "algorithmic_bytes_per_launch": int(dom_bytes.mean()),
+                    "avg_launch_us": round(float(stage_ms[:, dom].mean() * 1e3), 2)}
+    else:
+        roofline = {"bound": "alu", "achieved": None, "peak": None, "unit": None, "frac": None,
+                    "traffic": None, "kernel": dom_name}
+
+    value = B / (ms_per_step * 1e-3)
+    res = {
+        "metric": "MoE block-passes/s + achieved HBM GB/s & MFMA util vs peak, 32-row block",
+        "value": round(value, 2),
+        "unit": "block-passes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {W.BF16: "bf16", W.F32: "f32", W.FP8: "fp8_e4m3 weights, bf16 activations"}[wl.weight_dtype],
+        "data": "synthetic (seeded normal inputs and random-init weights of the stated shapes)",
+        "config": {"workload": wl.name, "num_blocks": B, "block_rows": wl.block_rows, "hidden": H,
+                   "experts": E, "top_k": K, "inter": I, "shared_inter": Is,
+                   "mass_threshold": tau, "weight_copies_rotated": args.layers},
+        "roofline": roofline,
+        "call": {
+            "device_us": round(float(device_ms.mean() * 1e3), 2),
+            "algorithmic_bytes": int(call_bytes.mean()),
+            "hbm_gbps": round(float(call_bytes.mean() / (ms_per_step * 1e-3) / 1e9), 1),
+            "hbm_frac": round(float(call_bytes.mean() / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS), 4),
+            "mfma_tflops": round(float(mfma_flops.mean() / (ms_per_step * 1e-3) / 1e12), 3),
+            "mfma_util": round(float(mfma_flops.mean() / (ms_per_step * 1e-3) / 1e12
+                                     / MFMA_PEAK_TFLOPS[wl.weight_dtype]), 5),
+            "router_gflop": round(router_flops / 1e9, 3),
+            "experts_touched": float(touched.mean()),
+            "routed_pairs": float(pairs.mean()),
+        },
+        "stages_us": {n: round(float(v * 1e3), 2) for n, v in zip(cm.STAGE_NAMES, mean_stage)},
+        "cpu_baseline": None,
+    }
+
+    if args.cpu_seconds > 0:
+        import oracle
+        threads = int(os.environ.get("OMP_NUM_THREADS") or min(16, len(os.sched_getaffinity(0))))
+        t1 = time.perf_counter()
+        oracle.forward(inp, threads=threads)
+        one = time.perf_counter() - t1
+        reps = max(1, min(20, int(args.cpu_seconds / max(one, 1e-3))))
+        t1 = time.perf_counter()
+        for _ in range(reps):
+            oracle.forward(inp, threads=threads)
+        el = time.perf_counter() - t1
+        res["cpu_baseline"] = {
+            "value": round(reps * B / el, 4), "unit": "block-passes/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{reps} full calls of the {wl.name} workload (routing and fp64 FFN for all "
+                      f"{N} rows), {el:.1f} s wall, OpenMP over rows, after one untimed call",
+        }
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,182 @@
+/*
+ * clover_moe.h -- C ABI of the block-restricted sparse mixture-of-experts FFN
+ * for MI355X (gfx950).
+ *
+ * The operation (one MoE layer evaluated on a denoising pass of a
+ * block-diffusion language model):
+ *
+ *   Clover-35B-A3B-Preview CMF model card, introduction: every token is
+ *   routed to the top 8 of 256 experts, and a shared expert is always
+ *   applied; answers are written in 32-token blocks that are re-run pass
+ *   after pass until no mask token remains.
+ *   Same card, "Usage": during those passes the block's experts are
+ *   restricted to the set that carries 90% of the block's routing; the block
+ *   size can be 8, 16 or 32.
+ *   InfiniLM PR #604 (Clover on Hygon), "Summary", "Motivation" and "Notes for
+ *   Reviewers": block coreset routing in the preview pass, top-4 preview
+ *   routing, and a full-route replay after the approximate preview
+ *   (mass_threshold = 1.0 here).
+ *   InfiniLM PR #584 (Qwen MTP with FP8 block weights), "Benchmark" and
+ *   "Notes": E4M3 weights in 128x128 blocks with BF16 activations, aligned
+ *   block loading.
+ *
+ * For a call with B blocks of R rows (N = B*R rows), H hidden, E routed
+ * experts, top-k, expert intermediate I and shared intermediate Is:
+ *
+ *   1. logits l[r,e] = x[r,:] . Wr[e,:] (+ b[e])                     fp32
+ *   2. p[r,:] = softmax(l[r,:]) over all E experts                   fp64
+ *   3. mass[b,e] = sum of p[r,e] over the rows of block b             fp64
+ *   4. coreset C_b = smallest prefix of experts ordered by (mass desc,
+ *      id asc) whose cumulative mass reaches mass_threshold * total;
+ *      mass_threshold = 1 selects all experts
+ *   5. per row: the min(k, |C_b|) experts of C_b with the largest logits
+ *      (ties: lower id), gates renormalised over the chosen slots
+ *   6. out[r] = SwiGLU_shared(x[r]) + sum_j gate[r,j] * SwiGLU_{e_j}(x[r]),
+ *      SwiGLU_e(x) = W2_e (silu(W13_e[0:I] x) * (W13_e[I:2I] x))
+ *
+ * Steps 1-5 follow a fixed arithmetic contract (summation orders, fp32 fma
+ * for the logits, fp64 softmax with a Cody-Waite exp) so that expert sets,
+ * indices, gates and counts are reproducible bit for bit by any conforming
+ * implementation.  Step 6 accumulates in fp32 on MFMA; it matches an exact
+ * evaluation within a tolerance (bf16: max |err| <= 2e-2 max|ref| and
+ * sum|err| <= 5e-3 sum|ref|; fp8 weights: max |err| <= 6e-2 max|ref|).
+ *
+ * Conventions
+ *  - Every pointer argument of clover_moe_block_forward, and every pointer in
+ *    the structs, is a DEVICE pointer unless stated otherwise; the struct
+ *    objects themselves live in host memory.  Arrays are row-major and
+ *    contiguous.  Device pointers must be 16-byte aligned.
+ *  - Ownership: the caller allocates and frees everything, including the
+ *    workspace.  The library allocates no memory, keeps no pointer after the
+ *    call returns, never synchronises the host and never changes the current
+ *    device.  Buffers must stay valid until the work queued on `stream`
+ *    completes.
+ *  - Inputs are never written.  `out` and the workspace must not overlap any
+ *    input.
+ *  - Errors: every argument is checked before any work is queued and before
+ *    any byte is written; an invalid call returns a nonzero status and leaves
+ *    every buffer untouched.  clover_moe_last_error() then holds a
+ *    thread-local description.  Faults inside kernels surface at the caller's
+ *    next synchronisation.
+ *  - Non-finite inputs are not checked; their results are undefined.
+ *  - Thread safety: calls are independent; the library has no global
+ *    mutable state apart from the thread-local error text.
+ */
+#ifndef CLOVER_MOE_H
+#define CLOVER_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CMOE_OK = 0,
+    CMOE_ERR_NULL = 1,        /* a required pointer is NULL */
+    CMOE_ERR_VALUE = 2,       /* a value is out of its domain (threshold, top_k, sizes) */
+    CMOE_ERR_UNSUPPORTED = 3, /* a valid but unsupported shape or dtype combination */
+    CMOE_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned */
+    CMOE_ERR_ALIAS = 5,       /* out / workspace / routing outputs overlap an input or each other */
+    CMOE_ERR_WORKSPACE = 6,   /* workspace is NULL or smaller than clover_moe_workspace_size() */
+    CMOE_ERR_HIP = 7          /* the HIP runtime refused a launch */
+} cmoe_status;
+
+typedef enum {
+    CMOE_F32 = 0,
+    CMOE_BF16 = 1,
+    CMOE_FP8_E4M3 = 2 /* OCP E4M3 ("e4m3fn", max 448), with fp32 128x128 block scales */
+} cmoe_dtype;
+
+/* Shapes and dtypes (host struct). */
+typedef struct {
+    int32_t hidden;       /* H: multiple of 128, 128..16384 */
+    int32_t num_experts;  /* E: 1..256 */
+    int32_t inter;        /* I: multiple of 128, 128..8192 */
+    int32_t shared_inter; /* Is: 0 (no shared expert) or a multiple of 128, <= 8192 */
+    int32_t block_rows;   /* R: 8, 16 or 32 (CMF model card, "Usage": block size knob) */
+    int32_t num_blocks;   /* B: 1..1024; N = B*R rows, block b is rows [b*R, (b+1)*R) */
+    int32_t act_dtype;    /* cmoe_dtype of x and out: CMOE_F32 or CMOE_BF16 */
+    int32_t weight_dtype; /* cmoe_dtype of the expert weights.  Supported pairs
+                             (act, weight): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3) */
+} cmoe_problem;
+
+/* Weights (host struct of device pointers). */
+typedef struct {
+    const float* router_w;         /* [E,H] fp32, required */
+    const float* router_b;         /* [E] fp32 per-expert logit bias, or NULL */
+    const void* w13;               /* [E,2I,H] weight_dtype: rows 0..I-1 gate, I..2I-1 up */
+    const float* w13_scale;        /* fp8 only: [E,2I/128,H/128] fp32; else ignored */
+    const void* w2;                /* [E,H,I] weight_dtype (down projection) */
+    const float* w2_scale;         /* fp8 only: [E,H/128,I/128] fp32 */
+    const void* shared_w13;        /* [2Is,H] weight_dtype; required when Is > 0 */
+    const float* shared_w13_scale; /* fp8 only: [2Is/128,H/128] */
+    const void* shared_w2;         /* [H,Is] weight_dtype; required when Is > 0 */
+    const float* shared_w2_scale;  /* fp8 only: [H/128,Is/128] */
+} cmoe_weights;
+
+/* Optional routing outputs (host struct of device pointers; each may be NULL). */
+typedef struct {
+    int32_t* topk_idx;       /* [N,k] chosen experts per slot, -1 for unused slots */
+    float* gates;            /* [N,k] renormalised gates, 0 for unused slots */
+    int32_t* coreset_ids;    /* [B,E] coreset of each block, by (mass desc, id asc), -1 padded */
+    int32_t* coreset_size;   /* [B] |C_b| */
+    int32_t* expert_counts;  /* [E] number of (row, slot) pairs routed to each expert */
+    int32_t* expert_offsets; /* [E+1] exclusive prefix sum of expert_counts */
+    int32_t* perm;           /* [N*k] row*k+slot of each routed pair in expert-major order
+                                (experts ascending, then row ascending), -1 padded */
+    float* logits;           /* [N,E] router logits */
+    double* block_mass;      /* [B,E] routing mass of each expert in each block */
+} cmoe_routing;
+
+/* Bytes of device workspace clover_moe_block_forward needs for this problem
+ * and top_k.  Host-only; queues no work.  Writes *bytes on success. */
+cmoe_status clover_moe_workspace_size(const cmoe_problem* problem, int32_t top_k, size_t* bytes);
+
+/* One MoE layer over B blocks (steps 1-6 above), queued on `stream`.
+ *
+ *  problem, weights, routing: host pointers to the structs above (routing may be NULL)
+ *  x:               [N,H] act_dtype, device
+ *  mass_threshold:  share of the block's routing mass the coreset must carry,
+ *                   in (0, 1]; 1.0 = unrestricted top-k ("full route")
+ *  top_k:           1..min(8, E); 4 = "preview" routing, 8 = the model's routing
+ *  out:             [N,H] act_dtype, device; written, rounded once from fp32
+ *  workspace:       device scratch of at least clover_moe_workspace_size() bytes;
+ *                   its contents on entry do not matter
+ *  stream:          hipStream_t to queue the work on (NULL = the default stream)
+ */
+cmoe_status clover_moe_block_forward(const cmoe_problem* problem, const cmoe_weights* weights,
+                                     const void* x, float mass_threshold, int32_t top_k,
+                                     void* out, const cmoe_routing* routing,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Number of kernel stages clover_moe_block_forward queues, in order:
+ * 0 router logits, 1 per-block routing (softmax, mass, coreset, top-k, gates),
+ * 2 row permutation and work list, 3 gate/up GEMM + SwiGLU, 4 down GEMM,
+ * 5 gate-weighted combine with the shared expert. */
+#define CLOVER_MOE_NUM_STAGES 6
+
+/* Same operation as clover_moe_block_forward, for profiling: records
+ * stage_events[i] (i = 0..CLOVER_MOE_NUM_STAGES-1) on `stream` right before
+ * stage i is queued and stage_events[CLOVER_MOE_NUM_STAGES] after the last
+ * one.  stage_events points to n_events = CLOVER_MOE_NUM_STAGES + 1 host
+ * hipEvent_t handles created by the caller (hipEventCreate); the library only
+ * records them.  The elapsed time between events i and i+1 is the device time
+ * of stage i. */
+cmoe_status clover_moe_block_forward_staged(const cmoe_problem* problem, const cmoe_weights* weights,
+                                            const void* x, float mass_threshold, int32_t top_k,
+                                            void* out, const cmoe_routing* routing,
+                                            void* workspace, size_t workspace_bytes, void* stream,
+                                            void* const* stage_events, int32_t n_events);
+
+/* Static text of a status code. */
+const char* clover_moe_status_string(cmoe_status status);
+
+/* Thread-local text describing the last non-OK status returned on this thread. */
+const char* clover_moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CLOVER_MOE_H */

@@ -1,0 +1,310 @@
+// api.cpp -- the C entry points of include/clover_moe.h: argument checks,
+// workspace layout and the launch sequence.
+//
+// Every check runs on the host before any HIP call, so an invalid call
+// returns without queueing work or writing a byte (InfiniLM PR #604,
+// "Notes for Reviewers": unsupported options are rejected explicitly, and
+// conversions are rejected before writing; its checklist asks for mask,
+// state and workspace bounds and lifetime contracts).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/clover_moe.h"
+#include "cmoe_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+cmoe_status fail(cmoe_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+cmoe_status fail(cmoe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+size_t dtype_size(int d) { return d == CMOE_F32 ? 4 : d == CMOE_BF16 ? 2 : 1; }
+
+struct Range {
+  const char* name;
+  uintptr_t lo;
+  size_t bytes;
+  bool writable;
+};
+
+bool overlap(const Range& a, const Range& b) {
+  if (!a.lo || !b.lo || !a.bytes || !b.bytes) return false;
+  return a.lo < b.lo + b.bytes && b.lo < a.lo + a.bytes;
+}
+
+cmoe_status check_problem(const cmoe_problem* p, int32_t top_k) {
+  if (!p) return fail(CMOE_ERR_NULL, "problem is NULL");
+  if (p->hidden < 128 || p->hidden > 16384 || p->hidden % 128)
+    return fail(p->hidden <= 0 ? CMOE_ERR_VALUE : CMOE_ERR_UNSUPPORTED,
+                "hidden=%d: must be a multiple of 128 in [128, 16384]", p->hidden);
+  if (p->num_experts < 1) return fail(CMOE_ERR_VALUE, "num_experts=%d must be >= 1", p->num_experts);
+  if (p->num_experts > 256)
+    return fail(CMOE_ERR_UNSUPPORTED, "num_experts=%d: at most 256 experts", p->num_experts);
+  if (p->inter < 128 || p->inter > 8192 || p->inter % 128)
+    return fail(p->inter <= 0 ? CMOE_ERR_VALUE : CMOE_ERR_UNSUPPORTED,
+                "inter=%d: must be a multiple of 128 in [128, 8192]", p->inter);
+  if (p->shared_inter < 0) return fail(CMOE_ERR_VALUE, "shared_inter=%d < 0", p->shared_inter);
+  if (p->shared_inter > 8192 || p->shared_inter % 128)
+    return fail(CMOE_ERR_UNSUPPORTED, "shared_inter=%d: must be 0 or a multiple of 128 up to 8192",
+                p->shared_inter);
+  if (p->block_rows != 8 && p->block_rows != 16 && p->block_rows != 32)
+    return fail(p->block_rows <= 0 ? CMOE_ERR_VALUE : CMOE_ERR_UNSUPPORTED,
+                "block_rows=%d: must be 8, 16 or 32", p->block_rows);
+  if (p->num_blocks < 1) return fail(CMOE_ERR_VALUE, "num_blocks=%d must be >= 1", p->num_blocks);
+  if (p->num_blocks > 1024)
+    return fail(CMOE_ERR_UNSUPPORTED, "num_blocks=%d: at most 1024 blocks per call", p->num_blocks);
+  const bool ok_pair = (p->act_dtype == CMOE_F32 && p->weight_dtype == CMOE_F32) ||
+                       (p->act_dtype == CMOE_BF16 && p->weight_dtype == CMOE_BF16) ||
+                       (p->act_dtype == CMOE_BF16 && p->weight_dtype == CMOE_FP8_E4M3);
+  if (!ok_pair)
+    return fail(CMOE_ERR_UNSUPPORTED,
+                "dtype pair (act=%d, weight=%d) unsupported: use (F32,F32), (BF16,BF16) or (BF16,FP8_E4M3)",
+                p->act_dtype, p->weight_dtype);
+  if (top_k < 1 || top_k > p->num_experts)
+    return fail(CMOE_ERR_VALUE, "top_k=%d must be in [1, num_experts=%d]", top_k, p->num_experts);
+  if (top_k > 8) return fail(CMOE_ERR_UNSUPPORTED, "top_k=%d: at most 8", top_k);
+  return CMOE_OK;
+}
+
+struct Layout {
+  size_t logits, topk, gates, counts, offsets, pair_row, pair_pos, prefix, rowmask, tiles,
+      tile_count, h, y, total;
+  int max_tiles, mask_words;
+};
+
+Layout layout(const cmoe_problem& p, int K) {
+  const size_t N = (size_t)p.block_rows * p.num_blocks, E = p.num_experts, H = p.hidden;
+  const size_t NK = N * K;
+  Layout L;
+  L.mask_words = (int)((N + 31) / 32);
+  L.max_tiles = (int)(NK / cmoe::kTileRows + (E < NK ? E : NK) + (N + cmoe::kTileRows - 1) / cmoe::kTileRows + 1);
+  const size_t hsz = p.act_dtype == CMOE_F32 ? 4 : 2;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  L.logits = take(N * E * 4);
+  L.topk = take(NK * 4);
+  L.gates = take(NK * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.pair_row = take(NK * 4);
+  L.pair_pos = take(NK * 4);
+  L.prefix = take(E * L.mask_words * 4);
+  L.rowmask = take(E * L.mask_words * 4);
+  L.tiles = take((size_t)L.max_tiles * sizeof(cmoe::Tile));
+  L.tile_count = take(4);
+  L.h = take((NK * p.inter + N * p.shared_inter) * hsz);
+  L.y = take((NK + N) * H * 4);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+namespace cmoe {
+
+size_t workspace_bytes(const cmoe_problem& pr, int top_k) { return layout(pr, top_k).total; }
+
+void carve(Plan& p, const cmoe_problem& pr, int K, void* ws, const cmoe_routing* rt) {
+  const Layout L = layout(pr, K);
+  char* base = static_cast<char*>(ws);
+  p.N = pr.block_rows * pr.num_blocks;
+  p.H = pr.hidden;
+  p.E = pr.num_experts;
+  p.I = pr.inter;
+  p.Is = pr.shared_inter;
+  p.R = pr.block_rows;
+  p.B = pr.num_blocks;
+  p.K = K;
+  p.act = pr.act_dtype;
+  p.wt = pr.weight_dtype;
+  p.max_tiles = L.max_tiles;
+  p.mask_words = L.mask_words;
+  p.logits = (rt && rt->logits) ? rt->logits : reinterpret_cast<float*>(base + L.logits);
+  p.topk = (rt && rt->topk_idx) ? rt->topk_idx : reinterpret_cast<int32_t*>(base + L.topk);
+  p.gates = (rt && rt->gates) ? rt->gates : reinterpret_cast<float*>(base + L.gates);
+  p.counts = reinterpret_cast<int32_t*>(base + L.counts);
+  p.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  p.pair_row = reinterpret_cast<int32_t*>(base + L.pair_row);
+  p.pair_pos = reinterpret_cast<int32_t*>(base + L.pair_pos);
+  p.prefix = reinterpret_cast<int32_t*>(base + L.prefix);
+  p.rowmask = reinterpret_cast<uint32_t*>(base + L.rowmask);
+  p.tiles = reinterpret_cast<Tile*>(base + L.tiles);
+  p.tile_count = reinterpret_cast<int32_t*>(base + L.tile_count);
+  p.h = base + L.h;
+  p.y = reinterpret_cast<float*>(base + L.y);
+  p.coreset_ids = rt ? rt->coreset_ids : nullptr;
+  p.coreset_size = rt ? rt->coreset_size : nullptr;
+  p.block_mass = rt ? rt->block_mass : nullptr;
+  p.out_counts = rt ? rt->expert_counts : nullptr;
+  p.out_offsets = rt ? rt->expert_offsets : nullptr;
+  p.out_perm = rt ? rt->perm : nullptr;
+}
+
+}  // namespace cmoe
+
+extern "C" {
+
+cmoe_status clover_moe_workspace_size(const cmoe_problem* problem, int32_t top_k, size_t* bytes) {
+  if (!bytes) return fail(CMOE_ERR_NULL, "bytes is NULL");
+  const cmoe_status s = check_problem(problem, top_k);
+  if (s != CMOE_OK) return s;
+  *bytes = cmoe::workspace_bytes(*problem, top_k);
+  return CMOE_OK;
+}
+
+static cmoe_status forward_impl(const cmoe_problem* problem, const cmoe_weights* w,
+                                const void* x, float mass_threshold, int32_t top_k, void* out,
+                                const cmoe_routing* routing, void* workspace,
+                                size_t workspace_bytes, void* stream, void* const* events,
+                                int32_t n_events) {
+  cmoe_status s = check_problem(problem, top_k);
+  if (s != CMOE_OK) return s;
+  const cmoe_problem& p = *problem;
+  if (!w) return fail(CMOE_ERR_NULL, "weights is NULL");
+  if (!x) return fail(CMOE_ERR_NULL, "x is NULL");
+  if (!out) return fail(CMOE_ERR_NULL, "out is NULL");
+  if (!w->router_w) return fail(CMOE_ERR_NULL, "weights->router_w is NULL");
+  if (!w->w13) return fail(CMOE_ERR_NULL, "weights->w13 is NULL");
+  if (!w->w2) return fail(CMOE_ERR_NULL, "weights->w2 is NULL");
+  if (p.shared_inter > 0 && (!w->shared_w13 || !w->shared_w2))
+    return fail(CMOE_ERR_NULL, "shared_inter > 0 but the shared expert weights are NULL");
+  const bool fp8 = p.weight_dtype == CMOE_FP8_E4M3;
+  if (fp8 && (!w->w13_scale || !w->w2_scale ||
+              (p.shared_inter > 0 && (!w->shared_w13_scale || !w->shared_w2_scale))))
+    return fail(CMOE_ERR_NULL, "fp8 weights need every 128x128 block-scale array");
+  if (!(mass_threshold > 0.0f && mass_threshold <= 1.0f))
+    return fail(CMOE_ERR_VALUE, "mass_threshold=%g must be in (0, 1]", (double)mass_threshold);
+
+  const size_t need = cmoe::workspace_bytes(p, top_k);
+  if (!workspace || workspace_bytes < need)
+    return fail(CMOE_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed",
+                workspace_bytes, workspace, need);
+
+  // every device range the call touches
+  const size_t N = (size_t)p.block_rows * p.num_blocks, E = p.num_experts, H = p.hidden,
+               I = p.inter, Is = p.shared_inter, B = p.num_blocks, K = top_k;
+  const size_t asz = dtype_size(p.act_dtype), wsz = dtype_size(p.weight_dtype);
+  std::vector<Range> rs = {
+      {"x", (uintptr_t)x, N * H * asz, false},
+      {"router_w", (uintptr_t)w->router_w, E * H * 4, false},
+      {"router_b", (uintptr_t)w->router_b, E * 4, false},
+      {"w13", (uintptr_t)w->w13, E * 2 * I * H * wsz, false},
+      {"w2", (uintptr_t)w->w2, E * H * I * wsz, false},
+      {"shared_w13", Is ? (uintptr_t)w->shared_w13 : 0, 2 * Is * H * wsz, false},
+      {"shared_w2", Is ? (uintptr_t)w->shared_w2 : 0, H * Is * wsz, false},
+      {"out", (uintptr_t)out, N * H * asz, true},
+      {"workspace", (uintptr_t)workspace, need, true},
+  };
+  if (fp8) {
+    rs.push_back({"w13_scale", (uintptr_t)w->w13_scale, E * (2 * I / 128) * (H / 128) * 4, false});
+    rs.push_back({"w2_scale", (uintptr_t)w->w2_scale, E * (H / 128) * (I / 128) * 4, false});
+    if (Is) {
+      rs.push_back({"shared_w13_scale", (uintptr_t)w->shared_w13_scale, (2 * Is / 128) * (H / 128) * 4, false});
+      rs.push_back({"shared_w2_scale", (uintptr_t)w->shared_w2_scale, (H / 128) * (Is / 128) * 4, false});
+    }
+  }
+  if (routing) {
+    rs.push_back({"routing.topk_idx", (uintptr_t)routing->topk_idx, N * K * 4, true});
+    rs.push_back({"routing.gates", (uintptr_t)routing->gates, N * K * 4, true});
+    rs.push_back({"routing.coreset_ids", (uintptr_t)routing->coreset_ids, B * E * 4, true});
+    rs.push_back({"routing.coreset_size", (uintptr_t)routing->coreset_size, B * 4, true});
+    rs.push_back({"routing.expert_counts", (uintptr_t)routing->expert_counts, E * 4, true});
+    rs.push_back({"routing.expert_offsets", (uintptr_t)routing->expert_offsets, (E + 1) * 4, true});
+    rs.push_back({"routing.perm", (uintptr_t)routing->perm, N * K * 4, true});
+    rs.push_back({"routing.logits", (uintptr_t)routing->logits, N * E * 4, true});
+    rs.push_back({"routing.block_mass", (uintptr_t)routing->block_mass, B * E * 8, true});
+  }
+  for (const Range& r : rs)
+    if (r.lo % 16)
+      return fail(CMOE_ERR_ALIGN, "%s at %p is not 16-byte aligned", r.name, (void*)r.lo);
+  for (size_t i = 0; i < rs.size(); ++i)
+    for (size_t j = i + 1; j < rs.size(); ++j)
+      if ((rs[i].writable || rs[j].writable) && overlap(rs[i], rs[j]))
+        return fail(CMOE_ERR_ALIAS, "%s overlaps %s", rs[i].name, rs[j].name);
+
+  if (events) {
+    if (n_events != CLOVER_MOE_NUM_STAGES + 1)
+      return fail(CMOE_ERR_VALUE, "n_events=%d, expected %d", n_events, CLOVER_MOE_NUM_STAGES + 1);
+    for (int i = 0; i < n_events; ++i)
+      if (!events[i]) return fail(CMOE_ERR_NULL, "stage_events[%d] is NULL", i);
+  }
+
+  cmoe::Plan plan;
+  cmoe::carve(plan, p, top_k, workspace, routing);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  for (int stage = 0; stage <= CLOVER_MOE_NUM_STAGES && e == hipSuccess; ++stage) {
+    if (events) {
+      e = hipEventRecord(static_cast<hipEvent_t>(events[stage]), st);
+      if (e != hipSuccess) break;
+    }
+    switch (stage) {
+      case 0: e = cmoe::launch_router(plan, x, w->router_w, w->router_b, st); break;
+      case 1: e = cmoe::launch_route_blocks(plan, mass_threshold, st); break;
+      case 2: e = cmoe::launch_permute(plan, st); break;
+      case 3: e = cmoe::launch_expert_up(plan, *w, x, st); break;
+      case 4: e = cmoe::launch_expert_down(plan, *w, st); break;
+      case 5: e = cmoe::launch_combine(plan, out, st); break;
+      default: break;
+    }
+  }
+  if (e != hipSuccess) return fail(CMOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return CMOE_OK;
+}
+
+cmoe_status clover_moe_block_forward(const cmoe_problem* problem, const cmoe_weights* w,
+                                     const void* x, float mass_threshold, int32_t top_k, void* out,
+                                     const cmoe_routing* routing, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  return forward_impl(problem, w, x, mass_threshold, top_k, out, routing, workspace,
+                      workspace_bytes, stream, nullptr, 0);
+}
+
+cmoe_status clover_moe_block_forward_staged(const cmoe_problem* problem, const cmoe_weights* w,
+                                            const void* x, float mass_threshold, int32_t top_k,
+                                            void* out, const cmoe_routing* routing,
+                                            void* workspace, size_t workspace_bytes, void* stream,
+                                            void* const* stage_events, int32_t n_events) {
+  if (!stage_events) return fail(CMOE_ERR_NULL, "stage_events is NULL");
+  return forward_impl(problem, w, x, mass_threshold, top_k, out, routing, workspace,
+                      workspace_bytes, stream, stage_events, n_events);
+}
+
+const char* clover_moe_status_string(cmoe_status s) {
+  switch (s) {
+    case CMOE_OK: return "ok";
+    case CMOE_ERR_NULL: return "a required pointer is NULL";
+    case CMOE_ERR_VALUE: return "an argument is out of its domain";
+    case CMOE_ERR_UNSUPPORTED: return "unsupported shape or dtype combination";
+    case CMOE_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case CMOE_ERR_ALIAS: return "an output overlaps an input or another output";
+    case CMOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case CMOE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* clover_moe_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

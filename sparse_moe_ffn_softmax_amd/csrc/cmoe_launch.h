@@ -1,0 +1,72 @@
+// cmoe_launch.h -- internal interface between the host entry points (api.cpp)
+// and the HIP kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/clover_moe.h"
+
+namespace cmoe {
+
+// Rows handled by one grouped-GEMM work tile (4 MFMA tiles of 16 rows).
+constexpr int kTileRows = 64;
+// h columns produced by one expert_up workgroup (4 waves x 8 gate/up pairs).
+constexpr int kUpCols = 32;
+// output columns produced by one expert_down workgroup (4 waves x 16).
+constexpr int kDownCols = 64;
+
+// One unit of grouped-GEMM work: `rows` consecutive pairs of one expert,
+// starting at pair position `start` (expert == E means the shared expert,
+// whose pairs are the N rows in order).
+struct Tile {
+  int32_t expert;
+  int32_t start;
+  int32_t rows;
+  int32_t pad;
+};
+
+// Everything a launch needs: sizes plus device pointers carved out of the
+// caller's workspace (or the caller's optional routing buffers).
+struct Plan {
+  int N, H, E, I, Is, R, B, K;
+  int act, wt;           // cmoe_dtype codes
+  int max_tiles;         // grid bound for the grouped GEMMs
+  int mask_words;        // ceil(N / 32)
+  float* logits;         // [N,E]
+  int32_t* topk;         // [N,K]
+  float* gates;          // [N,K]
+  int32_t* counts;       // [E]
+  int32_t* offsets;      // [E+1]
+  int32_t* pair_row;     // [N*K]  source row of each routed pair, expert-major
+  int32_t* pair_pos;     // [N*K]  pair position of (row, slot), -1 if unused
+  int32_t* prefix;       // [E, mask_words] exclusive popcount prefix of rowmask
+  uint32_t* rowmask;     // [E, mask_words] bit r set if row r routes to expert e
+  Tile* tiles;           // [max_tiles]
+  int32_t* tile_count;   // [1]
+  void* h;               // routed [N*K, I] then shared [N, Is]; act_dtype elements
+  float* y;              // routed [N*K, H] then shared [N, H]; fp32
+  // optional caller outputs
+  int32_t* coreset_ids;
+  int32_t* coreset_size;
+  double* block_mass;
+  int32_t* out_counts;
+  int32_t* out_offsets;
+  int32_t* out_perm;
+};
+
+size_t workspace_bytes(const cmoe_problem& pr, int top_k);
+// Carves the workspace; routing buffers given by the caller replace the
+// workspace copies where the layout is the same.
+void carve(Plan& p, const cmoe_problem& pr, int top_k, void* ws, const cmoe_routing* rt);
+
+hipError_t launch_router(const Plan& p, const void* x, const float* router_w,
+                         const float* router_b, hipStream_t s);
+hipError_t launch_route_blocks(const Plan& p, float tau, hipStream_t s);
+hipError_t launch_permute(const Plan& p, hipStream_t s);
+hipError_t launch_expert_up(const Plan& p, const cmoe_weights& w, const void* x, hipStream_t s);
+hipError_t launch_expert_down(const Plan& p, const cmoe_weights& w, hipStream_t s);
+hipError_t launch_combine(const Plan& p, void* out, hipStream_t s);
+
+}  // namespace cmoe

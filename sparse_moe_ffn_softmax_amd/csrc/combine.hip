@@ -1,0 +1,63 @@
+// combine.hip -- gate-weighted combine of the routed expert outputs plus the
+// shared expert (Clover-35B-A3B-Preview CMF model card, introduction: top-8
+// routed experts plus a shared expert):
+//
+//   out[r] = y_shared[r] + sum_j gate[r,j] * y[pos(r,j)]     (slots ascending)
+//
+// accumulated in fp32 with one rounding to the activation dtype at the end.
+// The order is fixed, so results are bitwise identical from run to run (no
+// floating-point atomics anywhere on the path).
+#include "cmoe_device.h"
+#include "cmoe_launch.h"
+
+namespace cmoe {
+
+template <typename OT>
+__device__ __forceinline__ void store4(OT* p, f32x4 v);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, f32x4 v) {
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+template <>
+__device__ __forceinline__ void store4<uint16_t>(uint16_t* p, f32x4 v) {
+  u32x2 o;
+  o[0] = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+  o[1] = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+  *reinterpret_cast<u32x2*>(p) = o;
+}
+
+template <typename OT>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
+                                                      const int32_t* __restrict__ pair_pos,
+                                                      const float* __restrict__ gates,
+                                                      OT* __restrict__ out, int N, int H, int K,
+                                                      int has_shared) {
+  const int r = blockIdx.y;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (c >= H) return;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (has_shared) acc = *reinterpret_cast<const f32x4*>(y + ((size_t)N * K + r) * H + c);
+  for (int j = 0; j < K; ++j) {
+    const int pos = pair_pos[(size_t)r * K + j];
+    if (pos < 0) continue;
+    const float g = gates[(size_t)r * K + j];
+    const f32x4 v = *reinterpret_cast<const f32x4*>(y + (size_t)pos * H + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(g, v[i], acc[i]);
+  }
+  store4<OT>(out + (size_t)r * H + c, acc);
+}
+
+hipError_t launch_combine(const Plan& p, void* out, hipStream_t s) {
+  dim3 grid((p.H / 4 + 255) / 256, p.N);
+  if (p.act == CMOE_BF16)
+    combine_kernel<uint16_t><<<grid, 256, 0, s>>>(p.y, p.pair_pos, p.gates,
+                                                  static_cast<uint16_t*>(out), p.N, p.H, p.K,
+                                                  p.Is > 0);
+  else
+    combine_kernel<float><<<grid, 256, 0, s>>>(p.y, p.pair_pos, p.gates, static_cast<float*>(out),
+                                               p.N, p.H, p.K, p.Is > 0);
+  return hipGetLastError();
+}
+
+}  // namespace cmoe

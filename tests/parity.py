@@ -1,0 +1,94 @@
+"""Helpers shared by the GPU parity tests: run one call through the C ABI,
+run the oracle on the same bytes, compare.
+
+Bars (the operation's accuracy contract):
+  routing (logits, block mass, coreset, top-k indices, gates, counts,
+  offsets, permutation): bit-exact;
+  FFN output, bf16 weights: max|d| <= 2e-2 max|ref| and sum|d| <= 5e-3 sum|ref|;
+  FFN output, fp8 weights:  max|d| <= 6e-2 max|ref|;
+  FFN output, fp32 (no bf16 rounding anywhere): max|d| <= 1e-4 max|ref|.  The
+  only error sources are fp32 accumulation over at most max(H, I) terms and
+  fp32 SiLU, both below 2^-24 * 2048 ~ 1.2e-4 relative in the worst case and
+  ~1e-6 in practice.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import sparse_moe_ffn_softmax_amd as cm
+import workloads as W
+
+ROUTING_KEYS = ("logits", "block_mass", "coreset_ids", "coreset_size", "topk_idx", "gates",
+                "expert_counts", "expert_offsets", "perm")
+
+TOL = {
+    W.BF16: dict(max_rel=2e-2, mean_rel=5e-3),
+    W.FP8: dict(max_rel=6e-2, mean_rel=None),
+    W.F32: dict(max_rel=1e-4, mean_rel=5e-3),
+}
+
+
+def run_gpu(inp, tau: float, top_k: int, dp=None, workspace=None):
+    """One call through the C ABI; returns (out as fp64 numpy, routing dict)."""
+    import torch
+    wl = inp.wl
+    dp = dp or cm.upload(inp)
+    ws = workspace if workspace is not None else cm.alloc_workspace(dp.problem, top_k)
+    rt_t, rt = cm.alloc_routing(dp.problem, top_k)
+    odt = torch.bfloat16 if wl.act_dtype == W.BF16 else torch.float32
+    out = torch.empty((wl.rows, wl.hidden), dtype=odt, device="cuda")
+    cm.clover_moe_block_forward(dp.problem, dp.weights, dp.tensors["x"], tau, top_k, out, rt, ws)
+    torch.cuda.synchronize()
+    res = {k: v.cpu().numpy() for k, v in rt_t.items()}
+    return out.double().cpu().numpy(), res
+
+
+def bits(a: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float32:
+        return a.view(np.uint32)
+    if a.dtype == np.float64:
+        return a.view(np.uint64)
+    return a
+
+
+def assert_routing_equal(gpu: dict, ref: dict):
+    for k in ROUTING_KEYS:
+        g, r = bits(gpu[k]), bits(ref[k])
+        assert g.shape == r.shape, (k, g.shape, r.shape)
+        if not np.array_equal(g, r):
+            bad = np.argwhere(g != r)
+            raise AssertionError(f"routing output {k} differs at {len(bad)} places, first {bad[:5].tolist()}")
+
+
+def ffn_errors(out: np.ndarray, ref: np.ndarray, rows=None):
+    if rows is not None:
+        out, ref = out[rows], ref[rows]
+    d = np.abs(out - ref)
+    return float(d.max() / np.abs(ref).max()), float(d.sum() / np.abs(ref).sum())
+
+
+def assert_ffn_close(out, ref, weight_dtype, rows=None):
+    assert np.all(np.isfinite(out if rows is None else out[rows]))
+    mx, mean = ffn_errors(out, ref, rows)
+    tol = TOL[weight_dtype]
+    assert mx <= tol["max_rel"], f"max|d|/max|ref| = {mx:.3e} > {tol['max_rel']}"
+    if tol["mean_rel"] is not None:
+        assert mean <= tol["mean_rel"], f"sum|d|/sum|ref| = {mean:.3e} > {tol['mean_rel']}"
+    return mx, mean
+
+
+def check(inp, tau=None, top_k=None, rows=None, threads=0, dp=None):
+    """Full parity check of one call; returns (max_rel, mean_rel, oracle result)."""
+    wl = inp.wl
+    tau = wl.mass_threshold if tau is None else tau
+    top_k = wl.top_k if top_k is None else top_k
+    print(f"[parity] {wl.name} B={wl.num_blocks} R={wl.block_rows} H={wl.hidden} E={wl.num_experts} "
+          f"I={wl.inter} Is={wl.shared_inter} {wl.act_dtype}/{wl.weight_dtype} tau={tau} k={top_k}",
+          flush=True)
+    out, gpu = run_gpu(inp, tau, top_k, dp=dp)
+    ref = oracle.forward(inp, tau=tau, top_k=top_k, rows=rows, threads=threads)
+    assert_routing_equal(gpu, ref)
+    mx, mean = assert_ffn_close(out, ref["out"], wl.weight_dtype, rows)
+    return mx, mean, ref

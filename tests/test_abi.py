@@ -1,0 +1,160 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/clover_moe.h declares, and rejects every invalid call before any HIP
+call (fake, never-dereferenced device addresses are enough for that)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_moe_ffn_softmax_amd as cm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            names += re.findall(r"^\S.*?\b(clover_moe_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    lib = cm.load_library()
+    declared = header_functions()
+    assert set(declared) == set(cm.EXPORTED)
+    for n in declared:
+        assert hasattr(lib, n), n
+    syms = subprocess.run(["nm", "-D", "--defined-only", cm.LIB_PATH], capture_output=True,
+                          text=True, check=True).stdout
+    for n in declared:
+        assert re.search(rf"\bT {n}$", syms, flags=re.M), n
+
+
+def test_status_strings():
+    for s in range(8):
+        assert cm.clover_moe_status_string(s)
+    assert cm.clover_moe_status_string(0) == "ok"
+
+
+# fake device addresses, 16-byte aligned and far apart
+BASE = 0x7F0000000000
+STEP = 1 << 36
+
+
+def fake(i, misalign=0):
+    return BASE + i * STEP + misalign
+
+
+def problem(**kw):
+    d = dict(hidden=2048, num_experts=256, inter=512, shared_inter=512, block_rows=32,
+             num_blocks=1, act_dtype="bf16", weight_dtype="bf16")
+    d.update(kw)
+    return cm.make_problem(**d)
+
+
+def weights(fp8=False, **override):
+    d = dict(router_w=fake(1), w13=fake(2), w2=fake(3), shared_w13=fake(4), shared_w2=fake(5))
+    if fp8:
+        d.update(w13_scale=fake(6), w2_scale=fake(7), shared_w13_scale=fake(8), shared_w2_scale=fake(9))
+    d.update(override)
+    return cm.make_weights(**d)
+
+
+def call(prob=None, w=None, x=fake(10), tau=0.9, k=8, out=fake(11), routing=None, ws=fake(12),
+         ws_bytes=None):
+    prob = prob or problem()
+    w = w or weights()
+    if ws_bytes is None:
+        try:
+            ws_bytes = cm.clover_moe_workspace_size(prob, k)
+        except cm.ClovermoeError:
+            ws_bytes = 1 << 30
+    lib = cm.load_library()
+    rt = ctypes.byref(routing) if routing is not None else None
+    return lib.clover_moe_block_forward(ctypes.byref(prob), ctypes.byref(w), x, ctypes.c_float(tau), k,
+                                        out, rt, ws, ws_bytes, None)
+
+
+def test_workspace_size_grows_with_rows_and_is_host_only():
+    a = cm.clover_moe_workspace_size(problem(), 8)
+    b = cm.clover_moe_workspace_size(problem(num_blocks=16), 8)
+    c = cm.clover_moe_workspace_size(problem(num_blocks=16), 4)
+    assert 0 < a < b and c < b
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(tau=0.0), cm.CMOE_ERR_VALUE),
+    (dict(tau=-0.1), cm.CMOE_ERR_VALUE),
+    (dict(tau=1.0001), cm.CMOE_ERR_VALUE),
+    (dict(tau=float("nan")), cm.CMOE_ERR_VALUE),
+    (dict(k=0), cm.CMOE_ERR_VALUE),
+    (dict(k=9), cm.CMOE_ERR_UNSUPPORTED),
+    (dict(x=None), cm.CMOE_ERR_NULL),
+    (dict(out=None), cm.CMOE_ERR_NULL),
+    (dict(ws=None), cm.CMOE_ERR_WORKSPACE),
+    (dict(ws_bytes=1024), cm.CMOE_ERR_WORKSPACE),
+    (dict(x=fake(10, 8)), cm.CMOE_ERR_ALIGN),
+    (dict(out=fake(11, 4)), cm.CMOE_ERR_ALIGN),
+    (dict(out=fake(10)), cm.CMOE_ERR_ALIAS),              # out == x
+    (dict(out=fake(2) + 4096), cm.CMOE_ERR_ALIAS),        # out inside w13
+    (dict(ws=fake(11)), cm.CMOE_ERR_ALIAS),               # workspace == out
+])
+def test_invalid_calls_rejected(kw, expect):
+    assert call(**kw) == expect
+    assert cm.clover_moe_last_error()
+
+
+@pytest.mark.parametrize("pkw,k,expect", [
+    (dict(hidden=2000), 8, cm.CMOE_ERR_UNSUPPORTED),
+    (dict(hidden=0), 8, cm.CMOE_ERR_VALUE),
+    (dict(num_experts=0), 1, cm.CMOE_ERR_VALUE),
+    (dict(num_experts=300), 8, cm.CMOE_ERR_UNSUPPORTED),
+    (dict(num_experts=4), 8, cm.CMOE_ERR_VALUE),          # k > E
+    (dict(inter=500), 8, cm.CMOE_ERR_UNSUPPORTED),
+    (dict(shared_inter=-128), 8, cm.CMOE_ERR_VALUE),
+    (dict(shared_inter=100), 8, cm.CMOE_ERR_UNSUPPORTED),
+    (dict(block_rows=24), 8, cm.CMOE_ERR_UNSUPPORTED),
+    (dict(block_rows=0), 8, cm.CMOE_ERR_VALUE),
+    (dict(num_blocks=0), 8, cm.CMOE_ERR_VALUE),
+    (dict(num_blocks=2048), 8, cm.CMOE_ERR_UNSUPPORTED),
+    (dict(act_dtype="f32", weight_dtype="bf16"), 8, cm.CMOE_ERR_UNSUPPORTED),
+    (dict(act_dtype="f32", weight_dtype="fp8_e4m3"), 8, cm.CMOE_ERR_UNSUPPORTED),
+    (dict(act_dtype="fp8_e4m3", weight_dtype="fp8_e4m3"), 8, cm.CMOE_ERR_UNSUPPORTED),
+])
+def test_invalid_problems_rejected(pkw, k, expect):
+    assert call(prob=problem(**pkw), k=k) == expect
+    n = ctypes.c_size_t(123)
+    assert cm.load_library().clover_moe_workspace_size(ctypes.byref(problem(**pkw)), k, ctypes.byref(n)) == expect
+    assert n.value == 123  # untouched on failure
+
+
+def test_missing_weights_rejected():
+    assert call(w=weights(router_w=None)) == cm.CMOE_ERR_NULL
+    assert call(w=weights(w13=None)) == cm.CMOE_ERR_NULL
+    assert call(w=weights(shared_w2=None)) == cm.CMOE_ERR_NULL
+    # no shared expert: its weights may be NULL -> passes validation, would launch;
+    # check only the fp8 scale requirement here
+    fp8 = problem(weight_dtype="fp8_e4m3")
+    assert call(prob=fp8, w=weights(fp8=True, w2_scale=None)) == cm.CMOE_ERR_NULL
+    assert call(prob=fp8, w=weights(fp8=True, shared_w13_scale=None)) == cm.CMOE_ERR_NULL
+    assert call(w=weights(router_b=fake(13, 4))) == cm.CMOE_ERR_ALIGN
+
+
+def test_routing_outputs_checked_for_alias_and_alignment():
+    r = cm.make_routing(topk_idx=fake(20), gates=fake(21), logits=fake(1))   # logits on router_w
+    assert call(routing=r) == cm.CMOE_ERR_ALIAS
+    r = cm.make_routing(topk_idx=fake(20), gates=fake(20) + 64)              # overlap each other
+    assert call(routing=r) == cm.CMOE_ERR_ALIAS
+    r = cm.make_routing(block_mass=fake(22, 8))
+    assert call(routing=r) == cm.CMOE_ERR_ALIGN
+
+
+def test_binding_raises_with_message():
+    with pytest.raises(cm.ClovermoeError) as ei:
+        cm.clover_moe_workspace_size(problem(block_rows=12), 8)
+    assert ei.value.status == cm.CMOE_ERR_UNSUPPORTED
+    assert "block_rows" in str(ei.value)

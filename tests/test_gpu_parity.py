@@ -1,0 +1,175 @@
+"""GPU parity: the HIP library through its C ABI against the CPU oracle on the
+same seeded bytes.  Routing bit-exact, FFN within the stated tolerance (see
+tests/parity.py)."""
+import hashlib
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from parity import assert_ffn_close, assert_routing_equal, check, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu(require_gpu):
+    pass
+
+
+MID = W.Workload("mid_bf16", 4, 16, 256, 32, 8, 256, 128, W.BF16, W.BF16, 0.9, seed=21)
+
+
+# ---------------------------------------------------------------------------
+# small and mid-size cases: full FFN comparison, several tiles, ragged tails
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [0, 100])
+def test_tiny_fp32(seed):
+    check(W.generate(W.WORKLOADS["tiny_fp32"].with_(seed=seed)))
+
+
+@pytest.mark.parametrize("wl", [
+    MID,
+    MID.with_(name="mid_fp8", weight_dtype=W.FP8, seed=22),
+    MID.with_(name="mid_f32", act_dtype=W.F32, weight_dtype=W.F32, seed=23),
+    MID.with_(name="mid_noshared", shared_inter=0, seed=24),
+    MID.with_(name="mid_E20_k3", num_experts=20, top_k=3, seed=25),
+    MID.with_(name="mid_rows8", block_rows=8, num_blocks=5, seed=26),
+    MID.with_(name="mid_rows32", block_rows=32, num_blocks=3, seed=27),
+    MID.with_(name="mid_Is_ne_I", inter=128, shared_inter=384, seed=28),
+    MID.with_(name="mid_E256", num_experts=256, seed=29),
+], ids=lambda w: w.name)
+def test_mid(wl):
+    check(W.generate(wl))
+
+
+@pytest.mark.parametrize("tau,k", [(1.0, 8), (0.95, 8), (0.5, 8), (0.9, 4), (0.3, 1)])
+def test_mid_threshold_and_topk(tau, k):
+    check(W.generate(MID.with_(bias_sigma=0.5, seed=31)), tau=tau, top_k=k)
+
+
+def test_coreset_smaller_than_k_pads_slots():
+    inp = W.generate(MID.with_(bias_sigma=6.0, seed=32))
+    _, _, ref = check(inp, tau=0.5, top_k=8)
+    assert ref["coreset_size"].min() < 8
+
+
+def test_expert_with_more_rows_than_a_tile():
+    """All 256 rows route to the same few experts: several 64-row tiles per expert."""
+    wl = W.Workload("hot_experts", 8, 32, 256, 16, 4, 128, 128, W.BF16, W.BF16, 0.9, seed=33,
+                    bias_sigma=4.0)
+    inp = W.generate(wl)
+    _, _, ref = check(inp, tau=0.9, top_k=4)
+    assert ref["expert_counts"].max() > 128
+
+
+def test_uniform_router_closed_form_on_gpu():
+    inp = W.generate(MID.with_(num_experts=64, seed=34))
+    inp = W.with_arrays(inp, router_w=np.zeros_like(inp.router_w))
+    _, _, ref = check(inp)
+    assert np.all(ref["coreset_size"] == 58)          # ceil(fl32(0.9) * 64)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def block32():
+    return W.generate(W.WORKLOADS["block32_bf16"])
+
+
+def test_block32_bf16_full(block32):
+    mx, mean, ref = check(block32, threads=16)
+    print(f"[parity] block32_bf16 max_rel={mx:.3e} mean_rel={mean:.3e} coreset={ref['coreset_size']}")
+
+
+def test_block32_bf16_second_seed():
+    check(W.generate(W.WORKLOADS["block32_bf16"].with_(seed=101)), threads=16)
+
+
+@pytest.fixture(scope="module")
+def skewed():
+    return W.generate(W.WORKLOADS["block32_skewed"])
+
+
+@pytest.mark.parametrize("tau,k", W.SKEWED_SWEEP)
+def test_block32_skewed_sweep(skewed, tau, k):
+    rows = W.row_sample(32, 8, seed=2)
+    check(skewed, tau=tau, top_k=k, rows=rows, threads=16)
+
+
+def test_blocks16_bf16_sampled():
+    inp = W.generate(W.WORKLOADS["blocks16_bf16"])
+    check(inp, rows=W.row_sample(inp.wl.rows, 24, seed=3), threads=16)
+
+
+def test_blocks64_fp8_sampled():
+    inp = W.generate(W.WORKLOADS["blocks64_fp8"])
+    check(inp, rows=W.row_sample(inp.wl.rows, 16, seed=4), threads=16)
+
+
+# ---------------------------------------------------------------------------
+# hygiene: determinism, inputs untouched, no writes outside the outputs
+# ---------------------------------------------------------------------------
+
+def _digest(tensors):
+    h = hashlib.sha256()
+    for k in sorted(tensors):
+        t = tensors[k]
+        if t is not None:
+            h.update(t.view(-1).view(__import__("torch").uint8).cpu().numpy().tobytes())
+    return h.hexdigest()
+
+
+def test_deterministic_and_inputs_unchanged():
+    import sparse_moe_ffn_softmax_amd as cm
+    inp = W.generate(MID.with_(seed=41))
+    dp = cm.upload(inp)
+    before = _digest(dp.tensors)
+    outs = [run_gpu(inp, 0.9, 8, dp=dp) for _ in range(3)]
+    assert _digest(dp.tensors) == before
+    for o, r in outs[1:]:
+        assert np.array_equal(o, outs[0][0])
+        assert_routing_equal(r, outs[0][1])
+
+
+def test_no_writes_outside_out_and_workspace():
+    import torch
+    import sparse_moe_ffn_softmax_amd as cm
+    inp = W.generate(MID.with_(seed=42))
+    wl = inp.wl
+    dp = cm.upload(inp)
+    K = wl.top_k
+    need = cm.clover_moe_workspace_size(dp.problem, K)
+    pad = 4096
+    ws_big = torch.full((need + 2 * pad,), 0xA5, dtype=torch.uint8, device="cuda")
+    n_out = wl.rows * wl.hidden
+    out_big = torch.full((n_out + 2 * pad,), 12345.0, dtype=torch.bfloat16, device="cuda")
+    out = out_big[pad:pad + n_out].view(wl.rows, wl.hidden)
+    ws = ws_big[pad:pad + need]
+    cm.clover_moe_block_forward(dp.problem, dp.weights, dp.tensors["x"], 0.9, K, out, None, ws)
+    torch.cuda.synchronize()
+    assert torch.all(ws_big[:pad] == 0xA5) and torch.all(ws_big[pad + need:] == 0xA5)
+    assert torch.all(out_big[:pad] == 12345.0) and torch.all(out_big[pad + n_out:] == 12345.0)
+    ref = oracle.forward(inp)
+    assert_ffn_close(out.double().cpu().numpy(), ref["out"], wl.weight_dtype)
+
+
+def test_blocks_independent_on_gpu():
+    """A 4-block call gives the same routing and the same output as four
+    one-block calls."""
+    inp = W.generate(MID.with_(seed=43))
+    wl = inp.wl
+    out_all, r_all = run_gpu(inp, 0.9, wl.top_k)
+    R = wl.block_rows
+    for b in range(wl.num_blocks):
+        sl = slice(b * R, (b + 1) * R)
+        one = W.with_arrays(inp, wl=wl.with_(num_blocks=1), x=np.ascontiguousarray(inp.x[sl]))
+        o1, r1 = run_gpu(one, 0.9, wl.top_k)
+        np.testing.assert_array_equal(r_all["topk_idx"][sl], r1["topk_idx"])
+        np.testing.assert_array_equal(r_all["gates"][sl].view(np.uint32), r1["gates"].view(np.uint32))
+        np.testing.assert_array_equal(r_all["coreset_ids"][b], r1["coreset_ids"][0])
+        np.testing.assert_array_equal(out_all[sl], o1)
