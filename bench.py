@@ -191,14 +191,14 @@ def main():
     mean_stage = stage_ms.mean(0)
     dom = int(np.argmax(mean_stage))
     dom_name = cm.STAGE_NAMES[dom]
-    dom_bytes = {3: up_bytes, 4: dn_bytes}.get(dom)
+    dom_bytes = {2: up_bytes, 3: dn_bytes}.get(dom)
     device_ms = stage_ms.sum(1)
     if dom_bytes is not None:
         achieved = float(dom_bytes.sum() / (stage_ms[:, dom].sum() * 1e-3) / 1e9)
         traffic = measured_traffic(dom_name, wl.name, "expert_gemm.hip")
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                    "traffic": traffic, "kernel": f"expert_{'up' if dom == 3 else 'down'}_kernel",
+                    "traffic": traffic, "kernel": f"expert_{'up' if dom == 2 else 'down'}_kernel",
                     "algorithmic_bytes_per_launch": int(dom_bytes.mean()),
                     "avg_launch_us": round(float(stage_ms[:, dom].mean() * 1e3), 2)}
     else:

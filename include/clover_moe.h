@@ -152,10 +152,11 @@ cmoe_status clover_moe_block_forward(const cmoe_problem* problem, const cmoe_wei
                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Number of kernel stages clover_moe_block_forward queues, in order:
- * 0 router logits, 1 per-block routing (softmax, mass, coreset, top-k, gates),
- * 2 row permutation and work list, 3 gate/up GEMM + SwiGLU, 4 down GEMM,
- * 5 gate-weighted combine with the shared expert. */
-#define CLOVER_MOE_NUM_STAGES 6
+ * 0 router logits, 1 per-block routing (softmax, mass, coreset, top-k, gates;
+ * the last block also builds the row permutation and the GEMM work list),
+ * 2 gate/up GEMM + SwiGLU, 3 down GEMM, 4 gate-weighted combine with the
+ * shared expert. */
+#define CLOVER_MOE_NUM_STAGES 5
 
 /* Same operation as clover_moe_block_forward, for profiling: records
  * stage_events[i] (i = 0..CLOVER_MOE_NUM_STAGES-1) on `stream` right before

@@ -23,8 +23,8 @@ DTYPE_CODES = {"f32": CMOE_F32, "bf16": CMOE_BF16, "fp8_e4m3": CMOE_FP8_E4M3}
 
 EXPORTED = ("clover_moe_workspace_size", "clover_moe_block_forward",
             "clover_moe_block_forward_staged", "clover_moe_status_string", "clover_moe_last_error")
-NUM_STAGES = 6
-STAGE_NAMES = ("router", "route_blocks", "permute", "expert_up", "expert_down", "combine")
+NUM_STAGES = 5
+STAGE_NAMES = ("router", "route_blocks", "expert_up", "expert_down", "combine")
 
 
 class cmoe_problem(ctypes.Structure):

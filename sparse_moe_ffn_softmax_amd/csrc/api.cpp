@@ -85,8 +85,8 @@ cmoe_status check_problem(const cmoe_problem* p, int32_t top_k) {
 
 struct Layout {
   size_t logits, topk, gates, counts, offsets, pair_row, pair_pos, prefix, rowmask, tiles,
-      tile_count, h, y, total;
-  int max_tiles, mask_words;
+      tile_count, sync, h, y, total;
+  int max_tiles, mask_words, mt_max;
 };
 
 Layout layout(const cmoe_problem& p, int K) {
@@ -94,7 +94,14 @@ Layout layout(const cmoe_problem& p, int K) {
   const size_t NK = N * K;
   Layout L;
   L.mask_words = (int)((N + 31) / 32);
-  L.max_tiles = (int)(NK / cmoe::kTileRows + (E < NK ? E : NK) + (N + cmoe::kTileRows - 1) / cmoe::kTileRows + 1);
+  // work-tile height: about 1.5x the mean rows per expert, in 16-row MFMA
+  // tiles (1..4); experts with more rows get several tiles
+  const size_t want = (NK * 3 / 2 + E - 1) / E;
+  L.mt_max = (int)((want + 15) / 16);
+  if (L.mt_max < 1) L.mt_max = 1;
+  if (L.mt_max > 4) L.mt_max = 4;
+  const size_t T = 16 * (size_t)L.mt_max;
+  L.max_tiles = (int)(NK / T + (E < NK ? E : NK) + (N + T - 1) / T + 1);
   const size_t hsz = p.act_dtype == CMOE_F32 ? 4 : 2;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -113,6 +120,7 @@ Layout layout(const cmoe_problem& p, int K) {
   L.rowmask = take(E * L.mask_words * 4);
   L.tiles = take((size_t)L.max_tiles * sizeof(cmoe::Tile));
   L.tile_count = take(4);
+  L.sync = take(16 * 4);
   L.h = take((NK * p.inter + N * p.shared_inter) * hsz);
   L.y = take((NK + N) * H * 4);
   L.total = off;
@@ -139,6 +147,8 @@ void carve(Plan& p, const cmoe_problem& pr, int K, void* ws, const cmoe_routing*
   p.act = pr.act_dtype;
   p.wt = pr.weight_dtype;
   p.max_tiles = L.max_tiles;
+  p.mt_max = L.mt_max;
+  p.tile_rows = 16 * L.mt_max;
   p.mask_words = L.mask_words;
   p.logits = (rt && rt->logits) ? rt->logits : reinterpret_cast<float*>(base + L.logits);
   p.topk = (rt && rt->topk_idx) ? rt->topk_idx : reinterpret_cast<int32_t*>(base + L.topk);
@@ -151,6 +161,7 @@ void carve(Plan& p, const cmoe_problem& pr, int K, void* ws, const cmoe_routing*
   p.rowmask = reinterpret_cast<uint32_t*>(base + L.rowmask);
   p.tiles = reinterpret_cast<Tile*>(base + L.tiles);
   p.tile_count = reinterpret_cast<int32_t*>(base + L.tile_count);
+  p.sync = reinterpret_cast<int32_t*>(base + L.sync);
   p.h = base + L.h;
   p.y = reinterpret_cast<float*>(base + L.y);
   p.coreset_ids = rt ? rt->coreset_ids : nullptr;
@@ -262,10 +273,9 @@ static cmoe_status forward_impl(const cmoe_problem* problem, const cmoe_weights*
     switch (stage) {
       case 0: e = cmoe::launch_router(plan, x, w->router_w, w->router_b, st); break;
       case 1: e = cmoe::launch_route_blocks(plan, mass_threshold, st); break;
-      case 2: e = cmoe::launch_permute(plan, st); break;
-      case 3: e = cmoe::launch_expert_up(plan, *w, x, st); break;
-      case 4: e = cmoe::launch_expert_down(plan, *w, st); break;
-      case 5: e = cmoe::launch_combine(plan, out, st); break;
+      case 2: e = cmoe::launch_expert_up(plan, *w, x, st); break;
+      case 3: e = cmoe::launch_expert_down(plan, *w, st); break;
+      case 4: e = cmoe::launch_combine(plan, out, st); break;
       default: break;
     }
   }

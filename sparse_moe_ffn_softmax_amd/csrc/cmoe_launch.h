@@ -10,10 +10,12 @@
 
 namespace cmoe {
 
-// Rows handled by one grouped-GEMM work tile (4 MFMA tiles of 16 rows).
-constexpr int kTileRows = 64;
-// h columns produced by one expert_up workgroup (4 waves x 8 gate/up pairs).
-constexpr int kUpCols = 32;
+// Rows of one grouped-GEMM work tile: 16 * mt_max, mt_max in 1..4 MFMA row
+// tiles, chosen per call from the expected rows per expert (see carve()).
+constexpr int kMaxTileRows = 64;
+// h columns produced by one expert_up workgroup (one 16-column MFMA tile of 8
+// gate + 8 up columns; the 4 waves split the hidden dimension).
+constexpr int kUpCols = 8;
 // output columns produced by one expert_down workgroup (4 waves x 16).
 constexpr int kDownCols = 64;
 
@@ -33,6 +35,8 @@ struct Plan {
   int N, H, E, I, Is, R, B, K;
   int act, wt;           // cmoe_dtype codes
   int max_tiles;         // grid bound for the grouped GEMMs
+  int mt_max;            // MFMA row tiles per work tile (1..4)
+  int tile_rows;         // 16 * mt_max
   int mask_words;        // ceil(N / 32)
   float* logits;         // [N,E]
   int32_t* topk;         // [N,K]
@@ -45,8 +49,9 @@ struct Plan {
   uint32_t* rowmask;     // [E, mask_words] bit r set if row r routes to expert e
   Tile* tiles;           // [max_tiles]
   int32_t* tile_count;   // [1]
+  int32_t* sync;         // [16] call-local counters, zeroed by the router kernel
   void* h;               // routed [N*K, I] then shared [N, Is]; act_dtype elements
-  float* y;              // routed [N*K, H] then shared [N, H]; fp32
+  float* y;              // [N*K + N][H] fp32: routed pairs, then shared rows
   // optional caller outputs
   int32_t* coreset_ids;
   int32_t* coreset_size;
@@ -63,8 +68,8 @@ void carve(Plan& p, const cmoe_problem& pr, int top_k, void* ws, const cmoe_rout
 
 hipError_t launch_router(const Plan& p, const void* x, const float* router_w,
                          const float* router_b, hipStream_t s);
+// per-block routing; the last block also builds the permutation and work list
 hipError_t launch_route_blocks(const Plan& p, float tau, hipStream_t s);
-hipError_t launch_permute(const Plan& p, hipStream_t s);
 hipError_t launch_expert_up(const Plan& p, const cmoe_weights& w, const void* x, hipStream_t s);
 hipError_t launch_expert_down(const Plan& p, const cmoe_weights& w, hipStream_t s);
 hipError_t launch_combine(const Plan& p, void* out, hipStream_t s);

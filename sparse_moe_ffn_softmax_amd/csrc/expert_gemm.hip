@@ -11,11 +11,15 @@
 // only need to keep up.
 //
 // Work decomposition.  The permutation kernel leaves a list of tiles
-// (expert, first pair, up to 64 pairs).  A workgroup of 4 waves takes one
-// tile and one slice of output columns:
-//   expert_up   : 32 h columns; wave w computes 8 gate and the matching 8 up
-//                 columns as one 16-column MFMA tile, so SwiGLU pairs lanes
-//                 l and l+8 of the accumulator;
+// (expert, first pair, up to 16 * MTMAX pairs; MTMAX in 1..4 is picked per call
+// from the mean rows per expert, so a one-block call runs a lean single-tile
+// kernel and many-block calls share each weight byte among up to 64 rows).
+// A workgroup of 4 waves takes one tile and one slice of output columns,
+// 64 KiB of bf16 weights either way:
+//   expert_up   : 8 h columns = one 16-column MFMA tile of 8 gate and the
+//                 matching 8 up columns (SwiGLU pairs lanes l and l+8 of the
+//                 accumulator); the 4 waves split the hidden dimension and
+//                 their partial sums meet in LDS, added in wave order;
 //   expert_down : 64 y columns, 16 per wave.
 // Each wave streams its 16 weight rows straight from HBM into MFMA operand
 // registers (no LDS: every weight byte is used by exactly one wave), and the
@@ -35,132 +39,80 @@
 // and added into the result times its block scale.
 #include "cmoe_device.h"
 #include "cmoe_launch.h"
+#include "expert_frag.h"
 
 namespace cmoe {
-
-enum class WFmt { BF16, F32, FP8 };
-
-// ---------------------------------------------------------------------------
-// fragments: what one lane loads for one k step
-// ---------------------------------------------------------------------------
-template <WFmt F>
-struct Frag;
-
-template <>
-struct Frag<WFmt::BF16> {
-  static constexpr int kStep = 32;  // k per MFMA step
-  static constexpr int kLane = 8;   // elements per lane per step
-  using A = u32x4;                  // 8 bf16
-  using B = u32x4;
-  using AT = uint16_t;
-  using WT = uint16_t;
-  static __device__ __forceinline__ A load_a(const AT* p) { return *reinterpret_cast<const u32x4*>(p); }
-  static __device__ __forceinline__ B load_b(const WT* p) { return *reinterpret_cast<const u32x4*>(p); }
-  static __device__ __forceinline__ A zero_a() { return u32x4{0u, 0u, 0u, 0u}; }
-  static __device__ __forceinline__ f32x4 mma(A a, B b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  }
-};
-
-template <>
-struct Frag<WFmt::F32> {
-  static constexpr int kStep = 16;
-  static constexpr int kLane = 4;
-  using A = f32x4;
-  using B = f32x4;
-  using AT = float;
-  using WT = float;
-  static __device__ __forceinline__ A load_a(const AT* p) { return *reinterpret_cast<const f32x4*>(p); }
-  static __device__ __forceinline__ B load_b(const WT* p) { return *reinterpret_cast<const f32x4*>(p); }
-  static __device__ __forceinline__ A zero_a() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-  static __device__ __forceinline__ f32x4 mma(A a, B b, f32x4 c) {
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
-    return c;
-  }
-};
-
-template <>
-struct Frag<WFmt::FP8> {
-  static constexpr int kStep = 32;
-  static constexpr int kLane = 8;
-  using A = u32x4;  // 8 bf16
-  using B = u32x2;  // 8 e4m3 codes
-  using AT = uint16_t;
-  using WT = uint8_t;
-  static __device__ __forceinline__ A load_a(const AT* p) { return *reinterpret_cast<const u32x4*>(p); }
-  static __device__ __forceinline__ B load_b(const WT* p) { return *reinterpret_cast<const u32x2*>(p); }
-  static __device__ __forceinline__ A zero_a() { return u32x4{0u, 0u, 0u, 0u}; }
-  static __device__ __forceinline__ u32x4 widen(B b) {
-    // exact e4m3 -> bf16 (scale 1.0), two codes per instruction
-    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b[0], 1.0f, false);
-    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b[0], 1.0f, true);
-    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b[1], 1.0f, false);
-    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b[1], 1.0f, true);
-    return u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-                 __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
-  }
-  static __device__ __forceinline__ f32x4 mma(A a, B b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, widen(b)), c, 0, 0,
-                                                   0);
-  }
-};
 
 // ---------------------------------------------------------------------------
 // one wave: acc[mt] (16 rows x 16 cols) = sum_k A_mt[:, k] * W[col, k] over
 // k in [0, K).  wrow: pointer to this lane's weight row at its k offset;
 // arow[mt]: this lane's activation row at its k offset, or nullptr (zeros).
 // For fp8, wscale points at this lane's row of 128x128 block scales.
+//
+// K is consumed in stages of 128; the loads of stage s+1 are issued before
+// the MFMAs of stage s, so each wave always has a stage of weights in flight
+// (two register buffers, alternating).
 // ---------------------------------------------------------------------------
+template <WFmt F, int MT>
+struct Stage {
+  static constexpr int U = 128 / Frag<F>::kStep;  // MFMA steps per stage
+  typename Frag<F>::B b[U];
+  typename Frag<F>::A a[MT][U];
+};
+
+template <WFmt F, int MT>
+__device__ __forceinline__ void load_stage(Stage<F, MT>& st, const typename Frag<F>::WT* __restrict__ wrow,
+                                           const typename Frag<F>::AT* const (&arow)[MT], int k0) {
+  using Fr = Frag<F>;
+#pragma unroll
+  for (int u = 0; u < Stage<F, MT>::U; ++u) st.b[u] = Fr::load_b(wrow + k0 + u * Fr::kStep);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int u = 0; u < Stage<F, MT>::U; ++u)
+      st.a[mt][u] = arow[mt] ? Fr::load_a(arow[mt] + k0 + u * Fr::kStep) : Fr::zero_a();
+}
+
+template <WFmt F, int MT>
+__device__ __forceinline__ void mma_stage(const Stage<F, MT>& st, const float* __restrict__ wscale,
+                                          int k0, f32x4 (&acc)[MT]) {
+  using Fr = Frag<F>;
+  constexpr int U = Stage<F, MT>::U;
+  if constexpr (F == WFmt::FP8) {
+    const float s = wscale[k0 / 128];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < U; ++u) t = Fr::mma(st.a[mt][u], st.b[u], t);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[mt][v] = __builtin_fmaf(s, t[v], acc[mt][v]);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = Fr::mma(st.a[mt][u], st.b[u], acc[mt]);
+  }
+}
+
 template <WFmt F, int MT>
 __device__ __forceinline__ void wave_gemm(const typename Frag<F>::WT* __restrict__ wrow,
                                           const typename Frag<F>::AT* const (&arow)[MT], int K,
                                           const float* __restrict__ wscale, f32x4 (&acc)[MT]) {
-  using Fr = Frag<F>;
-  constexpr int U = 128 / Fr::kStep;  // steps per 128-deep k block
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int k0 = 0; k0 < K; k0 += 128) {
-    typename Fr::B b[U];
-    typename Fr::A a[MT][U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) b[u] = Fr::load_b(wrow + k0 + u * Fr::kStep);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        a[mt][u] = arow[mt] ? Fr::load_a(arow[mt] + k0 + u * Fr::kStep) : Fr::zero_a();
-    if constexpr (F == WFmt::FP8) {
-      const float s = wscale[k0 / 128];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int u = 0; u < U; ++u) t = Fr::mma(a[mt][u], b[u], t);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[mt][v] = __builtin_fmaf(s, t[v], acc[mt][v]);
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = Fr::mma(a[mt][u], b[u], acc[mt]);
-    }
+  Stage<F, MT> s0, s1;
+  load_stage<F, MT>(s0, wrow, arow, 0);
+  for (int k0 = 0; k0 < K; k0 += 256) {
+    const bool two = k0 + 128 < K;
+    if (two) load_stage<F, MT>(s1, wrow, arow, k0 + 128);
+    mma_stage<F, MT>(s0, wscale, k0, acc);
+    if (!two) break;
+    if (k0 + 256 < K) load_stage<F, MT>(s0, wrow, arow, k0 + 256);
+    mma_stage<F, MT>(s1, wscale, k0 + 128, acc);
   }
 }
-
-template <typename T>
-__device__ __forceinline__ void store_act(T* p, float v);
-template <>
-__device__ __forceinline__ void store_act<uint16_t>(uint16_t* p, float v) { *p = f32_to_bf16(v); }
-template <>
-__device__ __forceinline__ void store_act<float>(float* p, float v) { *p = v; }
 
 struct UpArgs {
   const void* x;
@@ -180,56 +132,73 @@ __device__ __forceinline__ void up_tile(const UpArgs& a, const Tile& t, int slic
   using Fr = Frag<F>;
   using AT = typename Fr::AT;
   using WT = typename Fr::WT;
+  __shared__ f32x4 red[4][MT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kg = lane >> 4;
   const bool shared = t.expert == a.E;
   const int inter = shared ? a.Is : a.I;
-  const int i0 = slice * kUpCols + wave * 8;
+  const int i0 = slice * kUpCols;
   const int wr = col < 8 ? i0 + col : inter + i0 + col - 8;  // gate row / up row
+  // the waves split the hidden dimension into ks equal parts (multiples of 128)
+  const int ks = (a.H % 512 == 0) ? 4 : (a.H % 256 == 0) ? 2 : 1;
+  const int klen = a.H / ks, kbeg = wave * klen;
   const WT* W = shared ? static_cast<const WT*>(a.sw13)
                        : static_cast<const WT*>(a.w13) + (size_t)t.expert * 2 * a.I * a.H;
-  const WT* wrow = W + (size_t)wr * a.H + kg * Fr::kLane;
+  const WT* wrow = W + (size_t)wr * a.H + kbeg + kg * Fr::kLane;
   const float* wscale = nullptr;
   if constexpr (F == WFmt::FP8) {
     const float* S = shared ? a.sw13_scale : a.w13_scale + (size_t)t.expert * (2 * a.I / 128) * (a.H / 128);
-    wscale = S + (size_t)(wr / 128) * (a.H / 128);
+    wscale = S + (size_t)(wr / 128) * (a.H / 128) + kbeg / 128;
   }
   const AT* arow[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = mt * 16 + col;
     const int src = m < t.rows ? (shared ? t.start + m : a.pair_row[t.start + m]) : -1;
-    arow[mt] = src >= 0 ? static_cast<const AT*>(a.x) + (size_t)src * a.H + kg * Fr::kLane : nullptr;
+    arow[mt] = src >= 0 ? static_cast<const AT*>(a.x) + (size_t)src * a.H + kbeg + kg * Fr::kLane : nullptr;
   }
   f32x4 acc[MT];
-  wave_gemm<F, MT>(wrow, arow, a.H, wscale, acc);
-
+  if (wave < ks) {
+    wave_gemm<F, MT>(wrow, arow, klen, wscale, acc);
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) red[wave][mt][lane] = acc[mt];
+  __syncthreads();
+  // wave w finishes M-tile w: sum the k parts in wave order, then SwiGLU
+  if (wave >= MT) return;
+  const int mt = wave;
+  f32x4 z = red[0][mt][lane];
+  for (int w = 1; w < ks; ++w) {
+    const f32x4 o = red[w][mt][lane];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) z[v] = z[v] + o[v];
+  }
   AT* h = static_cast<AT*>(a.h) +
           (shared ? (size_t)a.N * a.K * a.I + (size_t)t.start * a.Is : (size_t)t.start * a.I);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float g = acc[mt][v];
-      const float up = shfl_xor_f(g, 8);
-      const int m = mt * 16 + kg * 4 + v;
-      if (col < 8 && m < t.rows) store_act<AT>(h + (size_t)m * inter + i0 + col, silu(g) * up);
-    }
+  for (int v = 0; v < 4; ++v) {
+    const float g = z[v];
+    const float up = shfl_xor_f(g, 8);
+    const int m = mt * 16 + kg * 4 + v;
+    if (col < 8 && m < t.rows) store_act<AT>(h + (size_t)m * inter + i0 + col, silu(g) * up);
+  }
 }
 
-template <WFmt F>
+template <WFmt F, int MTMAX>
 __global__ __launch_bounds__(256) void expert_up_kernel(UpArgs a) {
   const int slot = blockIdx.x / a.n_slices, slice = blockIdx.x % a.n_slices;
   if (slot >= *a.tile_count) return;
   const Tile t = a.tiles[slot];
   const int inter = t.expert == a.E ? a.Is : a.I;
   if (slice * kUpCols >= inter) return;
-  switch ((t.rows + 15) >> 4) {
-    case 1: up_tile<F, 1>(a, t, slice); break;
-    case 2: up_tile<F, 2>(a, t, slice); break;
-    case 3: up_tile<F, 3>(a, t, slice); break;
-    default: up_tile<F, 4>(a, t, slice); break;
-  }
+  const int mt = (t.rows + 15) >> 4;  // 1..MTMAX
+  if constexpr (MTMAX >= 4) if (mt == 4) { up_tile<F, 4>(a, t, slice); return; }
+  if constexpr (MTMAX >= 3) if (mt == 3) { up_tile<F, 3>(a, t, slice); return; }
+  if constexpr (MTMAX >= 2) if (mt == 2) { up_tile<F, 2>(a, t, slice); return; }
+  up_tile<F, 1>(a, t, slice);
 }
 
 struct DownArgs {
@@ -283,16 +252,46 @@ __device__ __forceinline__ void down_tile(const DownArgs& a, const Tile& t, int 
     }
 }
 
-template <WFmt F>
+template <WFmt F, int MTMAX>
 __global__ __launch_bounds__(256) void expert_down_kernel(DownArgs a) {
   const int slot = blockIdx.x / a.n_slices, slice = blockIdx.x % a.n_slices;
   if (slot >= *a.tile_count) return;
   const Tile t = a.tiles[slot];
-  switch ((t.rows + 15) >> 4) {
-    case 1: down_tile<F, 1>(a, t, slice); break;
-    case 2: down_tile<F, 2>(a, t, slice); break;
-    case 3: down_tile<F, 3>(a, t, slice); break;
-    default: down_tile<F, 4>(a, t, slice); break;
+  const int mt = (t.rows + 15) >> 4;  // 1..MTMAX
+  if constexpr (MTMAX >= 4) if (mt == 4) { down_tile<F, 4>(a, t, slice); return; }
+  if constexpr (MTMAX >= 3) if (mt == 3) { down_tile<F, 3>(a, t, slice); return; }
+  if constexpr (MTMAX >= 2) if (mt == 2) { down_tile<F, 2>(a, t, slice); return; }
+  down_tile<F, 1>(a, t, slice);
+}
+
+struct UpKernel {
+  template <WFmt F, int M>
+  static void launch(unsigned grid, hipStream_t s, const UpArgs& a) {
+    expert_up_kernel<F, M><<<grid, 256, 0, s>>>(a);
+  }
+};
+struct DownKernel {
+  template <WFmt F, int M>
+  static void launch(unsigned grid, hipStream_t s, const DownArgs& a) {
+    expert_down_kernel<F, M><<<grid, 256, 0, s>>>(a);
+  }
+};
+
+template <WFmt F, typename Kern, typename Args>
+static void dispatch_mt(int mt_max, unsigned grid, hipStream_t s, const Args& a) {
+  switch (mt_max) {
+    case 1: Kern::template launch<F, 1>(grid, s, a); break;
+    case 2: Kern::template launch<F, 2>(grid, s, a); break;
+    default: Kern::template launch<F, 4>(grid, s, a); break;  // 3 runs on the 4-tile kernel
+  }
+}
+
+template <typename Kern, typename Args>
+static void dispatch(WFmt f, int mt_max, unsigned grid, hipStream_t s, const Args& a) {
+  switch (f) {
+    case WFmt::BF16: dispatch_mt<WFmt::BF16, Kern>(mt_max, grid, s, a); break;
+    case WFmt::F32: dispatch_mt<WFmt::F32, Kern>(mt_max, grid, s, a); break;
+    case WFmt::FP8: dispatch_mt<WFmt::FP8, Kern>(mt_max, grid, s, a); break;
   }
 }
 
@@ -321,11 +320,7 @@ hipError_t launch_expert_up(const Plan& p, const cmoe_weights& w, const void* x,
   a.K = p.K;
   a.n_slices = (p.I > p.Is ? p.I : p.Is) / kUpCols;
   const unsigned grid = (unsigned)p.max_tiles * (unsigned)a.n_slices;
-  switch (fmt_of(p)) {
-    case WFmt::BF16: expert_up_kernel<WFmt::BF16><<<grid, 256, 0, s>>>(a); break;
-    case WFmt::F32: expert_up_kernel<WFmt::F32><<<grid, 256, 0, s>>>(a); break;
-    case WFmt::FP8: expert_up_kernel<WFmt::FP8><<<grid, 256, 0, s>>>(a); break;
-  }
+  dispatch<UpKernel>(fmt_of(p), p.mt_max, grid, s, a);
   return hipGetLastError();
 }
 
@@ -347,11 +342,7 @@ hipError_t launch_expert_down(const Plan& p, const cmoe_weights& w, hipStream_t 
   a.K = p.K;
   a.n_slices = p.H / kDownCols;
   const unsigned grid = (unsigned)p.max_tiles * (unsigned)a.n_slices;
-  switch (fmt_of(p)) {
-    case WFmt::BF16: expert_down_kernel<WFmt::BF16><<<grid, 256, 0, s>>>(a); break;
-    case WFmt::F32: expert_down_kernel<WFmt::F32><<<grid, 256, 0, s>>>(a); break;
-    case WFmt::FP8: expert_down_kernel<WFmt::FP8><<<grid, 256, 0, s>>>(a); break;
-  }
+  dispatch<DownKernel>(fmt_of(p), p.mt_max, grid, s, a);
   return hipGetLastError();
 }
 

@@ -1,4 +1,6 @@
-// permute.hip -- row -> expert permutation and the grouped-GEMM work list.
+// permute.h -- row -> expert permutation and the grouped-GEMM work list
+// (device code; run by the last routing workgroup of a call, see
+// route_block.hip).
 //
 // Every routed (row, slot) pair gets a position in an expert-major order:
 // experts ascending, and inside an expert rows ascending (the key
@@ -12,16 +14,14 @@
 // mask bits below its row.  Counts, positions and tiles are all exact
 // integer results, independent of thread timing.
 //
-// One workgroup of 1024 threads does the whole call; the masks live in the
-// workspace and are touched only with device-scope atomics.
+// One workgroup of 1024 threads does the whole call; the masks live in LDS
+// when they fit (N <= 1024 rows at E = 256), else in the workspace, where they
+// are touched only with device-scope atomics.
+#pragma once
 #include "cmoe_device.h"
 #include "cmoe_launch.h"
 
 namespace cmoe {
-
-__device__ __forceinline__ uint32_t mask_load(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // exclusive scan of v over the 1024 threads of the workgroup; returns the
 // thread's exclusive prefix and writes the total to *total.
@@ -46,16 +46,38 @@ __device__ int block_exclusive_scan(int v, int* scratch /*[16]*/, int* total) {
   return wave_base + incl - v;
 }
 
-__global__ __launch_bounds__(1024) void permute_kernel(Plan p) {
-  __shared__ int cnt_s[256];
-  __shared__ int off_s[257];
-  __shared__ int scan_scratch[16];
+// Row masks of E x W words: in LDS when they fit, else in the workspace.
+constexpr int kLdsMaskWords = 8192;
+
+struct PermuteLds {
+  int cnt[256];
+  int off[257];
+  int scan[16];
+};
+
+// The whole permutation, run by one workgroup of 1024 threads.  lds: scratch
+// of 2 * kLdsMaskWords words (masks, then their popcount prefix), used only
+// when kLdsMask.
+template <bool kLdsMask>
+__device__ void permute_block(const Plan& p, PermuteLds& L, uint32_t* lds) {
+  uint32_t* mask_s = lds;
+  int32_t* prefix = kLdsMask ? reinterpret_cast<int32_t*>(lds + kLdsMaskWords) : p.prefix;
+  int* cnt_s = L.cnt;
+  int* off_s = L.off;
+  int* scan_scratch = L.scan;
   const int tid = threadIdx.x;
   const int N = p.N, K = p.K, E = p.E, W = p.mask_words;
   const int NK = N * K;
+  uint32_t* masks = kLdsMask ? mask_s : p.rowmask;
+  auto mask_load = [&](size_t i) -> uint32_t {
+    if constexpr (kLdsMask) return mask_s[i];
+    else return __hip_atomic_load(p.rowmask + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
 
-  for (int i = tid; i < E * W; i += 1024)
-    __hip_atomic_store(p.rowmask + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = tid; i < E * W; i += 1024) {
+    if constexpr (kLdsMask) mask_s[i] = 0u;
+    else __hip_atomic_store(p.rowmask + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   if (tid < 256) cnt_s[tid] = 0;
   __syncthreads();
 
@@ -64,7 +86,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(Plan p) {
     const int e = p.topk[i];
     if (e >= 0) {
       const int r = i / K;
-      atomicOr(p.rowmask + (size_t)e * W + (r >> 5), 1u << (r & 31));
+      atomicOr(masks + (size_t)e * W + (r >> 5), 1u << (r & 31));
       atomicAdd(&cnt_s[e], 1);
     }
   }
@@ -93,8 +115,8 @@ __global__ __launch_bounds__(1024) void permute_kernel(Plan p) {
   for (int e = tid; e < E; e += 1024) {
     int run = 0;
     for (int w = 0; w < W; ++w) {
-      p.prefix[(size_t)e * W + w] = run;
-      run += __popc(mask_load(p.rowmask + (size_t)e * W + w));
+      prefix[(size_t)e * W + w] = run;
+      run += __popc(mask_load((size_t)e * W + w));
     }
   }
   __syncthreads();
@@ -105,9 +127,9 @@ __global__ __launch_bounds__(1024) void permute_kernel(Plan p) {
     int pos = -1;
     if (e >= 0) {
       const int r = i / K;
-      const uint32_t word = mask_load(p.rowmask + (size_t)e * W + (r >> 5));
+      const uint32_t word = mask_load((size_t)e * W + (r >> 5));
       const uint32_t below = word & ((1u << (r & 31)) - 1u);
-      pos = off_s[e] + p.prefix[(size_t)e * W + (r >> 5)] + __popc(below);
+      pos = off_s[e] + prefix[(size_t)e * W + (r >> 5)] + __popc(below);
       p.pair_row[pos] = r;
       if (p.out_perm) p.out_perm[pos] = i;
     }
@@ -122,7 +144,8 @@ __global__ __launch_bounds__(1024) void permute_kernel(Plan p) {
     int n = 0;
     if (tid < E) n = cnt_s[tid];
     else if (tid == E && has_shared) n = N;
-    const int nt = (n + kTileRows - 1) / kTileRows;
+    const int T = p.tile_rows;
+    const int nt = (n + T - 1) / T;
     int ntiles;
     const int base = block_exclusive_scan(tid <= E ? nt : 0, scan_scratch, &ntiles);
     if (tid <= E) {
@@ -130,19 +153,14 @@ __global__ __launch_bounds__(1024) void permute_kernel(Plan p) {
       for (int t = 0; t < nt; ++t) {
         Tile tile;
         tile.expert = tid;
-        tile.start = start0 + t * kTileRows;
-        tile.rows = min(kTileRows, n - t * kTileRows);
+        tile.start = start0 + t * T;
+        tile.rows = min(T, n - t * T);
         tile.pad = 0;
         p.tiles[base + t] = tile;
       }
     }
     if (tid == 0) *p.tile_count = ntiles;
   }
-}
-
-hipError_t launch_permute(const Plan& p, hipStream_t s) {
-  permute_kernel<<<1, 1024, 0, s>>>(p);
-  return hipGetLastError();
 }
 
 }  // namespace cmoe

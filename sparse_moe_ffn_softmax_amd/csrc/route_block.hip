@@ -1,5 +1,6 @@
 // route_block.hip -- per-block routing: softmax, block mass, coreset and
-// restricted top-k with renormalised gates.  One workgroup per block.
+// restricted top-k with renormalised gates.  One workgroup (16 waves) per
+// block.
 //
 // What is computed (Clover-35B-A3B-Preview CMF model card: introduction for
 // "256 experts top-8 plus a shared expert", "Usage" for "the block's experts
@@ -10,7 +11,8 @@
 //   u[r,e]   = exp(l[r,e] - max_e l[r,:])                         fp64
 //   Z[r]     = sum_e u[r,e]   (8 contiguous chunks of e, ascending inside a
 //                              chunk, pairwise combine j+=j+4, j+=j+2, j+=j+1)
-//   mass[e]  = sum over the block's rows, ascending, of u[r,e] / Z[r]
+//   p[r,e]   = u[r,e] / Z[r]
+//   mass[e]  = sum over the block's rows, ascending, of p[r,e]
 //   order    = experts by (mass desc, id asc)
 //   cum[i]   = sequential fp64 prefix sum of mass in that order
 //   coreset  = order[0 : m], m the smallest with cum[m-1] >= tau * cum[E-1];
@@ -23,8 +25,22 @@
 // degree-13 Taylor polynomial of exp(r), Horner with fma, then scaled by
 // 2^n; every operation is an IEEE fp64 primitive, so results are bitwise
 // reproducible on any IEEE machine that follows the same sequence.
+//
+// Parallel layout.  Everything that is order-free (row maxima, the
+// exponentials, the divisions, ranks, the top-k selection) is spread over
+// the 1024 threads; only the summations whose order is fixed above run as
+// short serial chains.  Top-k candidates are 64-bit keys (order-preserving
+// logit bits, complemented id): each half-wave owns a row, keeps 8 sorted
+// candidates per lane and takes the best head per slot with DPP exchanges
+// inside 16-lane rows and one swizzle across them.
+//
+// The workgroup that finishes last (device-scope counter, zeroed by the
+// router kernel earlier on the stream) goes on to build the row -> expert
+// permutation and the GEMM work list for the whole call (permute.h), so the
+// call needs no separate launch for it.
 #include "cmoe_device.h"
 #include "cmoe_launch.h"
+#include "permute.h"
 
 #pragma clang fp contract(off)
 
@@ -32,6 +48,9 @@ namespace cmoe {
 
 constexpr int kMaxRows = 32;
 constexpr int kMaxExperts = 256;
+constexpr int kThreads = 1024;
+constexpr int kPStride = kMaxExperts + kMaxExperts / 32;
+__device__ __forceinline__ int pidx(int r, int e) { return r * kPStride + e + (e >> 5); }
 
 // 1/ln 2 (correctly rounded); ln 2 split into a 42-bit head (so that n*head is
 // exact for |n| < 2^11) and its correctly rounded tail; 1/i! for i = 0..13.
@@ -55,56 +74,140 @@ __device__ __forceinline__ double exp_reduced(double d) {
   return __builtin_ldexp(poly, static_cast<int>(n));
 }
 
-// (logit desc, id asc) ordering of top-k candidates; id >= E marks "none".
-__device__ __forceinline__ bool better(float la, int ea, float lb, int eb, int E) {
-  const bool va = ea < E, vb = eb < E;
-  if (va != vb) return va;
-  if (!va) return false;
-  if (la != lb) return la > lb;
-  return ea < eb;
+// DPP lane-exchange controls (within each row of 16 lanes)
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i inside 8
+constexpr int kDppMirror = 0x140;      // lane i <-> 15-i inside 16
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
 }
 
-__global__ __launch_bounds__(256) void route_block_kernel(
-    const float* __restrict__ logits, int R, int E, int K, float tau, int32_t* __restrict__ topk,
-    float* __restrict__ gates, int32_t* __restrict__ coreset_ids,
-    int32_t* __restrict__ coreset_size, double* __restrict__ block_mass) {
+// Candidate keys: (order-preserving logit bits) << 32 | ~id, so the larger
+// key is the larger logit and, on equal logits, the lower id; 0 = none.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  const uint32_t lo = dpp<CTRL>(static_cast<uint32_t>(v));
+  const uint32_t hi = dpp<CTRL>(static_cast<uint32_t>(v >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// exchange with lane ^ 16 inside each 32-lane half (ds_swizzle bitmask mode)
+__device__ __forceinline__ uint64_t swz_xor16(uint64_t v) {
+  constexpr int kPattern = 0x1F | (0x10 << 10);  // and 0x1F, or 0, xor 0x10
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), kPattern));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v >> 32), kPattern));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t max64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, __uint_as_float(dpp<kDppXor1>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp<kDppXor2>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp<kDppHalfMirror>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp<kDppMirror>(__float_as_uint(v))));
+  float m = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 0));
+#pragma unroll
+  for (int row = 1; row < 4; ++row)
+    m = fmaxf(m, __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), row * 16)));
+  return m;
+}
+
+// sort 8 keys descending in registers (Batcher odd-even merge network)
+__device__ __forceinline__ void cswap(uint64_t (&k)[8], int i, int j) {
+  const uint64_t a = k[i], b = k[j];
+  k[i] = a > b ? a : b;
+  k[j] = a > b ? b : a;
+}
+
+__device__ __forceinline__ void sort8_desc(uint64_t (&k)[8]) {
+  cswap(k, 0, 1); cswap(k, 2, 3); cswap(k, 4, 5); cswap(k, 6, 7);
+  cswap(k, 0, 2); cswap(k, 1, 3); cswap(k, 4, 6); cswap(k, 5, 7);
+  cswap(k, 1, 2); cswap(k, 5, 6);
+  cswap(k, 0, 4); cswap(k, 1, 5); cswap(k, 2, 6); cswap(k, 3, 7);
+  cswap(k, 2, 4); cswap(k, 3, 5);
+  cswap(k, 1, 2); cswap(k, 3, 4); cswap(k, 5, 6);
+}
+
+__device__ __forceinline__ uint32_t logit_key(float l) {
+  const uint32_t b = __float_as_uint(l + 0.0f);  // -0 becomes +0: equal logits tie
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float tau) {
+  const int R = plan.R, E = plan.E, K = plan.K;
+  int32_t* __restrict__ topk = plan.topk;
+  float* __restrict__ gates = plan.gates;
+  int32_t* __restrict__ coreset_ids = plan.coreset_ids;
+  int32_t* __restrict__ coreset_size = plan.coreset_size;
+  double* __restrict__ block_mass = plan.block_mass;
   __shared__ float l_s[kMaxRows][kMaxExperts];
-  __shared__ double u_s[kMaxRows][kMaxExperts];
+  // u, then p in place; one pad slot per 32 experts keeps the per-chunk
+  // serial sums of different (row, chunk) threads on different banks
+  __shared__ double p_s[kMaxRows * kPStride];
   __shared__ double zpart[kMaxRows][8];
   __shared__ double z_s[kMaxRows];
+  __shared__ float m_s[kMaxRows];
   __shared__ double mass_s[kMaxExperts];
+  __shared__ double smass_s[kMaxExperts];  // masses in (mass desc, id asc) order
   __shared__ double cum_s[kMaxExperts];
   __shared__ int order_s[kMaxExperts];
   __shared__ int rank_s[kMaxExperts];
-  __shared__ int m_s;
+  __shared__ int rcnt[4][kMaxExperts];
+  __shared__ int m_sh;
+  __shared__ int last_sh;
+  __shared__ PermuteLds perm_lds;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int b = blockIdx.x;
-  const float* lb = logits + (size_t)b * R * E;
+  const float* lb = plan.logits + (size_t)b * R * E;
 
-  for (int i = tid; i < R * E; i += 256) l_s[i / E][i % E] = lb[i];
-  __syncthreads();
+  if (tid == 0) m_sh = E;
 
-  // u = exp(l - row max); the max is exact and order-free.
-  for (int r = wave; r < R; r += 4) {
-    float m = -INFINITY;
-    for (int e = lane; e < E; e += 64) m = fmaxf(m, l_s[r][e]);
+  // rows w and w+16 on wave w: logits to LDS, row maxima (exact, order-free),
+  // and u = exp(l - max) as 8 independent chains per lane
+  {
+    float lv[2][4], mx[2];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, shfl_xor_f(m, off));
-    const double md = static_cast<double>(m);
-    for (int e = lane; e < E; e += 64) u_s[r][e] = exp_reduced(static_cast<double>(l_s[r][e]) - md);
+    for (int h = 0; h < 2; ++h) {
+      const int r = wave + 16 * h;
+      float mm = -INFINITY;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int e = lane + 64 * s;
+        const bool ok = r < R && e < E;
+        const float v = ok ? lb[r * E + e] : -INFINITY;
+        if (ok) l_s[r][e] = v;
+        lv[h][s] = v;
+        mm = fmaxf(mm, v);
+      }
+      mx[h] = wave_max_f32(mm);
+      if (lane == 0 && r < R) m_s[r] = mx[h];
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int r = wave + 16 * h, e = lane + 64 * s;
+        if (r < R && e < E)
+          p_s[pidx(r, e)] = exp_reduced(static_cast<double>(lv[h][s]) - static_cast<double>(mx[h]));
+      }
   }
   __syncthreads();
 
-  // Z: chunk partial sums, one thread per (row, chunk).
-  {
+  // Z: chunk partial sums, one thread per (row, chunk), then the fixed tree
+  if (tid < kMaxRows * 8) {
     const int r = tid >> 3, j = tid & 7;
     if (r < R) {
       const int lo = (j * E) / 8, hi = ((j + 1) * E) / 8;
       double acc = 0.0;
-      for (int e = lo; e < hi; ++e) acc = acc + u_s[r][e];
+#pragma unroll 8
+      for (int e = lo; e < hi; ++e) acc = acc + p_s[pidx(r, e)];
       zpart[r][j] = acc;
     }
   }
@@ -123,103 +226,151 @@ __global__ __launch_bounds__(256) void route_block_kernel(
   }
   __syncthreads();
 
+  // p = u / Z, all elements in parallel (8 per thread)
+#pragma unroll
+  for (int t = 0; t < kMaxRows * kMaxExperts / kThreads; ++t) {
+    const int i = tid + t * kThreads;
+    const int r = i >> 8, e = i & 255;
+    if (r < R && e < E) p_s[pidx(r, e)] = p_s[pidx(r, e)] / z_s[r];
+  }
+  __syncthreads();
+
   // block mass, one thread per expert, rows ascending
   if (tid < E) {
     double acc = 0.0;
-    for (int r = 0; r < R; ++r) acc = acc + u_s[r][tid] / z_s[r];
+#pragma unroll 8
+    for (int r = 0; r < R; ++r) acc = acc + p_s[pidx(r, tid)];
     mass_s[tid] = acc;
   }
   __syncthreads();
 
-  // rank of each expert under (mass desc, id asc)
-  if (tid < E) {
-    const double me = mass_s[tid];
-    int rank = 0;
-    for (int e = 0; e < E; ++e) {
-      const double mo = mass_s[e];
-      rank += (mo > me) || (mo == me && e < tid);
+  // rank under (mass desc, id asc): four threads per expert count a quarter each
+  {
+    const int e = tid & 255, part = tid >> 8;
+    if (e < E) {
+      const double me = mass_s[e];
+      int cnt = 0;
+      const int lo = part * 64, hi = min(E, lo + 64);
+      const int mid = max(lo, min(hi, e));
+      // experts below e win ties, experts above e must be strictly larger
+#pragma unroll 8
+      for (int o = lo; o < mid; ++o) cnt += mass_s[o] >= me;
+#pragma unroll 8
+      for (int o = max(mid, e + 1); o < hi; ++o) cnt += mass_s[o] > me;
+      rcnt[part][e] = cnt;
     }
+  }
+  __syncthreads();
+  if (tid < E) {
+    const int rank = rcnt[0][tid] + rcnt[1][tid] + rcnt[2][tid] + rcnt[3][tid];
     rank_s[tid] = rank;
     order_s[rank] = tid;
+    smass_s[rank] = mass_s[tid];
   }
   __syncthreads();
 
-  // sequential prefix sum in mass order (one lane; this order is the contract)
+  // sequential prefix sum in mass order (the contract's order), one lane
   if (tid == 0) {
+    // batches of 16: loads and stores unconditional (the arrays hold 256
+    // entries; values past E are never read back), adds strictly in order
     double c = 0.0;
-    for (int i = 0; i < E; ++i) {
-      c = c + mass_s[order_s[i]];
-      cum_s[i] = c;
+    for (int i0 = 0; i0 < E; i0 += 16) {
+      double v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = smass_s[i0 + i];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        c = c + v[i];
+        v[i] = c;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) cum_s[i0 + i] = v[i];
     }
-    m_s = E;
   }
   __syncthreads();
   if (tau < 1.0f && tid < E) {
     const double thr = static_cast<double>(tau) * cum_s[E - 1];
     // cum is non-decreasing, so exactly one index is the first to reach thr
-    if (cum_s[tid] >= thr && (tid == 0 || cum_s[tid - 1] < thr)) m_s = tid + 1;
+    if (cum_s[tid] >= thr && (tid == 0 || cum_s[tid - 1] < thr)) m_sh = tid + 1;
   }
   __syncthreads();
-  const int m = m_s;
+  const int m = m_sh;
 
   if (coreset_ids && tid < E) coreset_ids[(size_t)b * E + tid] = tid < m ? order_s[tid] : -1;
   if (coreset_size && tid == 0) coreset_size[b] = m;
   if (block_mass && tid < E) block_mass[(size_t)b * E + tid] = mass_s[tid];
 
-  // restricted top-k: one wave per row; lane holds experts lane + 64*s
-  for (int r = wave; r < R; r += 4) {
-    const int row = b * R + r;
-    float cl[4];
-    int ce[4];
+  // restricted top-k: half a wave per row (rows 2w and 2w+1 on wave w); each
+  // lane keeps its 8 candidates (experts (lane&31) + 32*s) sorted by key,
+  // and every slot takes the best head of the half-wave
+  {
+    const int half = lane >> 5, hl = lane & 31;
+    const int r = 2 * wave + half;
+    const bool row_ok = r < R;
+    uint64_t key[8];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int e = lane + 64 * s;
-      const bool ok = e < E && rank_s[e] < m;
-      ce[s] = ok ? e : E;
-      cl[s] = ok ? l_s[r][e] : 0.0f;
+    for (int s = 0; s < 8; ++s) {
+      const int e = hl + 32 * s;
+      const bool ok = row_ok && e < E && rank_s[e] < m;
+      key[s] = ok ? (static_cast<uint64_t>(logit_key(l_s[r][e])) << 32) | static_cast<uint32_t>(~e) : 0ull;
     }
-    int chosen[8];
+    sort8_desc(key);
+    int my_e = -1;  // lane hl keeps the expert of slot hl
     int k_eff = 0;
     for (int j = 0; j < K; ++j) {
-      float bl = 0.0f;
-      int be = E;
+      uint64_t best = key[0];
+      best = max64(best, dpp64<kDppXor1>(best));
+      best = max64(best, dpp64<kDppXor2>(best));
+      best = max64(best, dpp64<kDppHalfMirror>(best));
+      best = max64(best, dpp64<kDppMirror>(best));
+      best = max64(best, swz_xor16(best));  // now the half-wave's best
+      if (best != 0ull) {
+        if (hl == j) my_e = static_cast<int>(~static_cast<uint32_t>(best));
+        if (key[0] == best) {  // this lane's head was taken: pop it
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        if (better(cl[s], ce[s], bl, be, E)) {
-          bl = cl[s];
-          be = ce[s];
+          for (int s = 0; s < 7; ++s) key[s] = key[s + 1];
+          key[7] = 0ull;
         }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ol = shfl_xor_f(bl, off);
-        const int oe = shfl_xor_i(be, off);
-        if (better(ol, oe, bl, be, E)) {
-          bl = ol;
-          be = oe;
-        }
+        k_eff = j + 1;
       }
-      if (be >= E) break;  // coreset exhausted
-      chosen[j] = be;
-      k_eff = j + 1;
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        if (ce[s] == be) ce[s] = E;  // taken
+      if (__ballot(best != 0ull) == 0ull) break;  // both rows exhausted
     }
-    if (lane == 0) {
-      double U = 0.0;
-      for (int j = 0; j < k_eff; ++j) U = U + u_s[r][chosen[j]];
-      for (int j = 0; j < K; ++j) {
-        const bool ok = j < k_eff;
-        topk[(size_t)row * K + j] = ok ? chosen[j] : -1;
-        gates[(size_t)row * K + j] = ok ? static_cast<float>(u_s[r][chosen[j]] / U) : 0.0f;
-      }
+    // gates: u of the chosen experts (recomputed: same operations, same bits),
+    // summed in slot order, then divided in parallel
+    const double u = my_e >= 0 ? exp_reduced(static_cast<double>(l_s[r][my_e]) - static_cast<double>(m_s[r])) : 0.0;
+    double U = 0.0;
+    for (int j = 0; j < k_eff; ++j) U = U + __shfl(u, j, 32);
+    if (row_ok && hl < K) {
+      const int row = b * R + r;
+      const bool ok = hl < k_eff;
+      topk[(size_t)row * K + hl] = ok ? my_e : -1;
+      gates[(size_t)row * K + hl] = ok ? static_cast<float>(u / U) : 0.0f;
     }
   }
+
+  // the last block to finish builds the permutation for the whole call (a
+  // single-block call goes straight on: its own writes are all it reads)
+  if (plan.B > 1) {
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) last_sh = atomicAdd(plan.sync, 1) == plan.B - 1;
+    __syncthreads();
+    if (!last_sh) return;
+    __threadfence();
+  } else {
+    __syncthreads();
+  }
+  if (plan.E * plan.mask_words <= kLdsMaskWords)
+    permute_block<true>(plan, perm_lds, reinterpret_cast<uint32_t*>(p_s));
+  else
+    permute_block<false>(plan, perm_lds, nullptr);
 }
 
+static_assert(sizeof(double) * kMaxRows * kPStride >= 2 * sizeof(uint32_t) * kLdsMaskWords,
+              "the permutation's LDS masks and prefix reuse the probability buffer");
+
 hipError_t launch_route_blocks(const Plan& p, float tau, hipStream_t s) {
-  route_block_kernel<<<p.B, 256, 0, s>>>(p.logits, p.R, p.E, p.K, tau, p.topk, p.gates,
-                                         p.coreset_ids, p.coreset_size, p.block_mass);
+  route_block_kernel<<<p.B, kThreads, 0, s>>>(p, tau);
   return hipGetLastError();
 }
 

@@ -12,8 +12,10 @@
 // Parallel layout: a workgroup of 256 threads owns a tile of RT rows x ET
 // experts; thread group c (32 threads) runs chunk c for every output of the
 // tile, each thread keeping TR x TE independent accumulators.  Operands are
-// staged through LDS in slices of KB positions per chunk.  The register tile
-// only changes which thread runs a chain, never the order inside a chain.
+// staged through LDS in slices of KB positions per chunk, double-buffered:
+// the global loads of slice s+1 are in flight while slice s is consumed.  The
+// register tile only changes which thread runs a chain, never the order
+// inside a chain.
 #include "cmoe_device.h"
 #include "cmoe_launch.h"
 
@@ -22,33 +24,105 @@
 namespace cmoe {
 
 template <typename XT>
-__device__ __forceinline__ float load_act(const XT* p);
+struct XVec;
 template <>
-__device__ __forceinline__ float load_act<float>(const float* p) { return *p; }
+struct XVec<uint16_t> {  // 8 bf16 per 16-byte load
+  static constexpr int kN = 8;
+  static __device__ __forceinline__ void widen(const u32x4& v, float* o) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = __uint_as_float(v[i] << 16);
+      o[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+    }
+  }
+};
 template <>
-__device__ __forceinline__ float load_act<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+struct XVec<float> {  // 4 fp32 per 16-byte load
+  static constexpr int kN = 4;
+  static __device__ __forceinline__ void widen(const u32x4& v, float* o) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = __uint_as_float(v[i]);
+  }
+};
 
-template <int TR, int TE, typename XT>
+template <int TR, int TE, int KB, typename XT>
 __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict__ x,
                                                             const float* __restrict__ w,
                                                             const float* __restrict__ bias,
                                                             float* __restrict__ logits, int N,
-                                                            int H, int E) {
-  constexpr int RT = 8 * TR;  // rows per workgroup
-  constexpr int ET = 4 * TE;  // experts per workgroup
-  constexpr int KB = 16;      // positions per chunk staged at a time
-  __shared__ float xs[8][KB][RT + 1];
-  __shared__ float ws[8][KB][ET + 1];
+                                                            int H, int E, int32_t* __restrict__ sync) {
+  constexpr int RT = 8 * TR;                 // rows per workgroup
+  constexpr int ET = 4 * TE;                 // experts per workgroup
+  constexpr int KP = KB + 4;                 // padded LDS row (breaks bank aliasing)
+  constexpr int XN = XVec<XT>::kN;
+  constexpr int XV = RT * 8 * KB / XN;       // x vectors per slice
+  constexpr int WV = ET * 8 * KB / 4;        // w vectors per slice
+  constexpr int XPT = (XV + 255) / 256;      // per thread
+  constexpr int WPT = (WV + 255) / 256;
+  __shared__ float xs[2][8][RT][KP];
+  __shared__ float ws[2][8][ET][KP];
   __shared__ float part[8][RT][ET + 1];
 
   const int tid = threadIdx.x;
+  // zero the call-local counters used by the kernels queued after this one
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid < 16) sync[tid] = 0;
   const int c = tid >> 5;  // chunk run by this thread
   const int q = tid & 31;
   const int rq = q & 7;    // row group
   const int eq = q >> 3;   // expert group
   const int row0 = blockIdx.x * RT;
   const int e0 = blockIdx.y * ET;
-  const int L = H / 8;     // chunk length (H is a multiple of 128)
+  const int L = H / 8;     // chunk length, a multiple of KB
+  const int S = L / KB;    // slices
+
+  u32x4 xr[XPT], wr[WPT];
+  auto fetch = [&](int s) {
+    const int kb = s * KB;
+#pragma unroll
+    for (int t = 0; t < XPT; ++t) {
+      const int v = tid + t * 256;
+      u32x4 val = u32x4{0u, 0u, 0u, 0u};
+      if (v < XV) {
+        const int kk = (v % (KB / XN)) * XN, rest = v / (KB / XN), r = rest % RT, cc = rest / RT;
+        const int row = row0 + r;
+        if (row < N) val = *reinterpret_cast<const u32x4*>(x + (size_t)row * H + cc * L + kb + kk);
+      }
+      xr[t] = val;
+    }
+#pragma unroll
+    for (int t = 0; t < WPT; ++t) {
+      const int v = tid + t * 256;
+      u32x4 val = u32x4{0u, 0u, 0u, 0u};
+      if (v < WV) {
+        const int kk = (v % (KB / 4)) * 4, rest = v / (KB / 4), e = rest % ET, cc = rest / ET;
+        const int ex = e0 + e;
+        if (ex < E) val = *reinterpret_cast<const u32x4*>(w + (size_t)ex * H + cc * L + kb + kk);
+      }
+      wr[t] = val;
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int t = 0; t < XPT; ++t) {
+      const int v = tid + t * 256;
+      if (v < XV) {
+        const int kk = (v % (KB / XN)) * XN, rest = v / (KB / XN), r = rest % RT, cc = rest / RT;
+        float f[XN];
+        XVec<XT>::widen(xr[t], f);
+#pragma unroll
+        for (int i = 0; i < XN; ++i) xs[buf][cc][r][kk + i] = f[i];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < WPT; ++t) {
+      const int v = tid + t * 256;
+      if (v < WV) {
+        const int kk = (v % (KB / 4)) * 4, rest = v / (KB / 4), e = rest % ET, cc = rest / ET;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ws[buf][cc][e][kk + i] = __uint_as_float(wr[t][i]);
+      }
+    }
+  };
 
   float acc[TR][TE];
 #pragma unroll
@@ -56,30 +130,27 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
 #pragma unroll
     for (int j = 0; j < TE; ++j) acc[i][j] = 0.0f;
 
-  for (int kb = 0; kb < L; kb += KB) {
-    for (int i = tid; i < 8 * KB * RT; i += 256) {
-      const int k = i % KB, r = (i / KB) % RT, cc = i / (KB * RT);
-      const int row = row0 + r;
-      xs[cc][k][r] = row < N ? load_act<XT>(x + (size_t)row * H + cc * L + kb + k) : 0.0f;
-    }
-    for (int i = tid; i < 8 * KB * ET; i += 256) {
-      const int k = i % KB, e = (i / KB) % ET, cc = i / (KB * ET);
-      const int ex = e0 + e;
-      ws[cc][k][e] = ex < E ? w[(size_t)ex * H + cc * L + kb + k] : 0.0f;
-    }
-    __syncthreads();
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int s = 0; s < S; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < S) fetch(s + 1);
 #pragma unroll 4
-    for (int k = 0; k < KB; ++k) {
-      float xv[TR], wv[TE];
+    for (int k = 0; k < KB; k += 4) {
+      f32x4 xv[TR], wv[TE];
 #pragma unroll
-      for (int i = 0; i < TR; ++i) xv[i] = xs[c][k][rq * TR + i];
+      for (int i = 0; i < TR; ++i) xv[i] = *reinterpret_cast<const f32x4*>(&xs[buf][c][rq * TR + i][k]);
 #pragma unroll
-      for (int j = 0; j < TE; ++j) wv[j] = ws[c][k][eq * TE + j];
+      for (int j = 0; j < TE; ++j) wv[j] = *reinterpret_cast<const f32x4*>(&ws[buf][c][eq * TE + j][k]);
 #pragma unroll
-      for (int i = 0; i < TR; ++i)
+      for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int j = 0; j < TE; ++j) acc[i][j] = __builtin_fmaf(xv[i], wv[j], acc[i][j]);
+        for (int i = 0; i < TR; ++i)
+#pragma unroll
+          for (int j = 0; j < TE; ++j) acc[i][j] = __builtin_fmaf(xv[i][kk], wv[j][kk], acc[i][j]);
     }
+    if (s + 1 < S) stash(buf ^ 1);
     __syncthreads();
   }
 
@@ -109,26 +180,32 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
   }
 }
 
+template <int TR, int TE, int KB>
+static void launch_shape(const Plan& p, const void* x, const float* w, const float* b,
+                         hipStream_t s) {
+  dim3 grid((p.N + 8 * TR - 1) / (8 * TR), (p.E + 4 * TE - 1) / (4 * TE));
+  if (p.act == CMOE_BF16)
+    router_logits_kernel<TR, TE, KB, uint16_t><<<grid, 256, 0, s>>>(
+        static_cast<const uint16_t*>(x), w, b, p.logits, p.N, p.H, p.E, p.sync);
+  else
+    router_logits_kernel<TR, TE, KB, float><<<grid, 256, 0, s>>>(
+        static_cast<const float*>(x), w, b, p.logits, p.N, p.H, p.E, p.sync);
+}
+
 hipError_t launch_router(const Plan& p, const void* x, const float* router_w,
                          const float* router_b, hipStream_t s) {
-  // Few rows (a single block per call): one accumulator per thread keeps
-  // enough workgroups in flight.  Many rows: 4x4 register tiles.
+  // chunk length H/8 is a multiple of 16 (H is a multiple of 128)
+  const int L = p.H / 8;
   if (p.N <= 256) {
-    dim3 grid((p.N + 7) / 8, (p.E + 3) / 4);
-    if (p.act == CMOE_BF16)
-      router_logits_kernel<1, 1, uint16_t><<<grid, 256, 0, s>>>(
-          static_cast<const uint16_t*>(x), router_w, router_b, p.logits, p.N, p.H, p.E);
-    else
-      router_logits_kernel<1, 1, float><<<grid, 256, 0, s>>>(
-          static_cast<const float*>(x), router_w, router_b, p.logits, p.N, p.H, p.E);
+    // few rows (one block per call): one accumulator per thread keeps
+    // enough workgroups in flight
+    if (L % 64 == 0) launch_shape<1, 1, 64>(p, x, router_w, router_b, s);
+    else if (L % 32 == 0) launch_shape<1, 1, 32>(p, x, router_w, router_b, s);
+    else launch_shape<1, 1, 16>(p, x, router_w, router_b, s);
   } else {
-    dim3 grid((p.N + 31) / 32, (p.E + 15) / 16);
-    if (p.act == CMOE_BF16)
-      router_logits_kernel<4, 4, uint16_t><<<grid, 256, 0, s>>>(
-          static_cast<const uint16_t*>(x), router_w, router_b, p.logits, p.N, p.H, p.E);
-    else
-      router_logits_kernel<4, 4, float><<<grid, 256, 0, s>>>(
-          static_cast<const float*>(x), router_w, router_b, p.logits, p.N, p.H, p.E);
+    // many rows: 4x4 register tiles
+    if (L % 32 == 0) launch_shape<4, 4, 32>(p, x, router_w, router_b, s);
+    else launch_shape<4, 4, 16>(p, x, router_w, router_b, s);
   }
   return hipGetLastError();
 }

@@ -82,8 +82,9 @@ def call(prob=None, w=None, x=fake(10), tau=0.9, k=8, out=fake(11), routing=None
 def test_workspace_size_grows_with_rows_and_is_host_only():
     a = cm.clover_moe_workspace_size(problem(), 8)
     b = cm.clover_moe_workspace_size(problem(num_blocks=16), 8)
-    c = cm.clover_moe_workspace_size(problem(num_blocks=16), 4)
-    assert 0 < a < b and c < b
+    c = cm.clover_moe_workspace_size(problem(num_blocks=64), 8)
+    d = cm.clover_moe_workspace_size(problem(num_blocks=16), 4)
+    assert 0 < a < b < c and d > 0
 
 
 @pytest.mark.parametrize("kw,expect", [
