@@ -96,6 +96,9 @@ def main():
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="rough budget of the oracle CPU-baseline leg (0 disables it)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="copy a device buffer of this many bytes once before the workload: "
+                         "a plain copy kernel of known size for calibrating HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -107,6 +110,14 @@ def main():
     import torch
     import sparse_moe_ffn_softmax_amd as cm
     import workloads as W
+
+    if args.copy_bytes:
+        src = torch.ones(args.copy_bytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     wl = W.WORKLOADS[args.workload]
     K, tau = wl.top_k, wl.mass_threshold
@@ -195,7 +206,7 @@ def main():
     device_ms = stage_ms.sum(1)
     if dom_bytes is not None:
         achieved = float(dom_bytes.sum() / (stage_ms[:, dom].sum() * 1e-3) / 1e9)
-        traffic = measured_traffic(dom_name, wl.name, "expert_gemm.hip")
+        traffic = measured_traffic(f"{dom_name}_kernel", wl.name, "expert_gemm.hip")
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                     "traffic": traffic, "kernel": f"expert_{'up' if dom == 2 else 'down'}_kernel",
