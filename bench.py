@@ -53,7 +53,11 @@ def layer_copies(dp, n_layers, E):
         sh = (j * E) // n_layers
 
         def rot(a):
-            return None if a is None else torch.roll(a, shifts=sh, dims=0).contiguous()
+            if a is None:
+                return None
+            if a.dtype == torch.float8_e4m3fn:  # roll the raw bytes
+                return torch.roll(a.view(torch.uint8), shifts=sh, dims=0).contiguous().view(a.dtype)
+            return torch.roll(a, shifts=sh, dims=0).contiguous()
 
         def cp(a):
             return None if a is None else a.clone()
