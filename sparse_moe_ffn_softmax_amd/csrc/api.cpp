@@ -95,11 +95,10 @@ Layout layout(const cmoe_problem& p, int K) {
   Layout L;
   L.mask_words = (int)((N + 31) / 32);
   // work-tile height: about 1.5x the mean rows per expert, in 16-row MFMA
-  // tiles (1..4); experts with more rows get several tiles
+  // tiles (1, 2, 4 or 8); experts with more rows get several tiles
   const size_t want = (NK * 3 / 2 + E - 1) / E;
-  L.mt_max = (int)((want + 15) / 16);
-  if (L.mt_max < 1) L.mt_max = 1;
-  if (L.mt_max > 4) L.mt_max = 4;
+  L.mt_max = 1;
+  while (L.mt_max < 8 && (size_t)16 * L.mt_max < want) L.mt_max *= 2;
   const size_t T = 16 * (size_t)L.mt_max;
   L.max_tiles = (int)(NK / T + (E < NK ? E : NK) + (N + T - 1) / T + 1);
   const size_t hsz = p.act_dtype == CMOE_F32 ? 4 : 2;
@@ -273,8 +272,14 @@ static cmoe_status forward_impl(const cmoe_problem* problem, const cmoe_weights*
     switch (stage) {
       case 0: e = cmoe::launch_router(plan, x, w->router_w, w->router_b, st); break;
       case 1: e = cmoe::launch_route_blocks(plan, mass_threshold, st); break;
-      case 2: e = cmoe::launch_expert_up(plan, *w, x, st); break;
-      case 3: e = cmoe::launch_expert_down(plan, *w, st); break;
+      case 2:
+        e = plan.mt_max == 1 ? cmoe::launch_expert_up(plan, *w, x, st)
+                             : cmoe::launch_expert_tiled(plan, *w, x, true, st);
+        break;
+      case 3:
+        e = plan.mt_max == 1 ? cmoe::launch_expert_down(plan, *w, st)
+                             : cmoe::launch_expert_tiled(plan, *w, x, false, st);
+        break;
       case 4: e = cmoe::launch_combine(plan, out, st); break;
       default: break;
     }

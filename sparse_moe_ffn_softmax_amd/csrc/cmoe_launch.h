@@ -10,9 +10,9 @@
 
 namespace cmoe {
 
-// Rows of one grouped-GEMM work tile: 16 * mt_max, mt_max in 1..4 MFMA row
-// tiles, chosen per call from the expected rows per expert (see carve()).
-constexpr int kMaxTileRows = 64;
+// Rows of one grouped-GEMM work tile: 16 * mt_max, mt_max in {1, 2, 4, 8} MFMA
+// row tiles, chosen per call from the expected rows per expert (see carve()).
+constexpr int kMaxTileRows = 128;
 // h columns produced by one expert_up workgroup (one 16-column MFMA tile of 8
 // gate + 8 up columns; the 4 waves split the hidden dimension).
 constexpr int kUpCols = 8;
@@ -35,7 +35,7 @@ struct Plan {
   int N, H, E, I, Is, R, B, K;
   int act, wt;           // cmoe_dtype codes
   int max_tiles;         // grid bound for the grouped GEMMs
-  int mt_max;            // MFMA row tiles per work tile (1..4)
+  int mt_max;            // MFMA row tiles per work tile: 1, 2, 4 or 8
   int tile_rows;         // 16 * mt_max
   int mask_words;        // ceil(N / 32)
   float* logits;         // [N,E]
@@ -70,8 +70,12 @@ hipError_t launch_router(const Plan& p, const void* x, const float* router_w,
                          const float* router_b, hipStream_t s);
 // per-block routing; the last block also builds the permutation and work list
 hipError_t launch_route_blocks(const Plan& p, float tau, hipStream_t s);
+// mt_max == 1: register-operand kernels (expert_gemm.hip)
 hipError_t launch_expert_up(const Plan& p, const cmoe_weights& w, const void* x, hipStream_t s);
 hipError_t launch_expert_down(const Plan& p, const cmoe_weights& w, hipStream_t s);
+// mt_max > 1: LDS-staged activation tiles (expert_tiled.hip); up = gate/up + SwiGLU, else down
+hipError_t launch_expert_tiled(const Plan& p, const cmoe_weights& w, const void* x, bool up,
+                               hipStream_t s);
 hipError_t launch_combine(const Plan& p, void* out, hipStream_t s);
 
 }  // namespace cmoe

@@ -278,12 +278,9 @@ struct DownKernel {
 };
 
 template <WFmt F, typename Kern, typename Args>
-static void dispatch_mt(int mt_max, unsigned grid, hipStream_t s, const Args& a) {
-  switch (mt_max) {
-    case 1: Kern::template launch<F, 1>(grid, s, a); break;
-    case 2: Kern::template launch<F, 2>(grid, s, a); break;
-    default: Kern::template launch<F, 4>(grid, s, a); break;  // 3 runs on the 4-tile kernel
-  }
+static void dispatch_mt(int, unsigned grid, hipStream_t s, const Args& a) {
+  // these kernels serve single-row-tile calls; many-row tiles run in expert_tiled.hip
+  Kern::template launch<F, 1>(grid, s, a);
 }
 
 template <typename Kern, typename Args>

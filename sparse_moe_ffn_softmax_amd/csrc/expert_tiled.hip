@@ -1,0 +1,296 @@
+// expert_tiled.hip -- grouped expert GEMMs for calls that route many rows to
+// each expert (many blocks per call: 16-128 rows per expert tile).
+//
+//   expert_up_tiled   : h = silu(X_e W_gate^T) * (X_e W_up^T)
+//   expert_down_tiled : y = h W2_e^T
+//
+// SwiGLU experts plus a shared expert (Clover-35B-A3B-Preview CMF model card,
+// introduction); fp8 weights are E4M3 with one fp32 scale per 128x128 block
+// and bf16 activations (InfiniLM PR #584, "Benchmark").
+//
+// With tens of rows per expert every weight byte feeds tens of MFMA rows, so
+// the activation tile must not be fetched once per wave.  A workgroup
+// (8 waves) owns one tile of up to T = 16*MT rows and a slice of output
+// columns (up: 64 h columns = 128 weight columns; down: 128 y columns).  The
+// hidden (or intermediate) dimension is consumed in stages of 256 bytes per
+// row: the gathered activation rows of the next stage are loaded into
+// registers and parked in the other half of a double-buffered LDS tile while
+// the current stage feeds the MFMAs; every wave reads the whole activation
+// tile from LDS and streams its own 16 weight columns from HBM straight into
+// MFMA operand registers (also double-buffered).  fp8 codes are widened to
+// bf16 exactly in registers; each 128-deep stage is accumulated separately and
+// added times its block scale.
+#include "cmoe_device.h"
+#include "cmoe_launch.h"
+#include "expert_frag.h"
+
+namespace cmoe {
+
+constexpr int kTiledWaves = 8;                  // waves per workgroup, 16 MFMA columns each
+constexpr int kTiledThreads = 64 * kTiledWaves;
+constexpr int kTiledUpCols = 8 * kTiledWaves;     // h columns per workgroup (gate + up pairs)
+constexpr int kTiledDownCols = 16 * kTiledWaves;  // y columns per workgroup
+
+struct TiledArgs {
+  const void* x;     // up: activations [N,H]
+  const void* w;     // up: W13 [E,2I,H]; down: W2 [E,H,I]
+  const float* ws;   // fp8 scales of w
+  const void* sw;    // shared expert's matrix
+  const float* sws;  // its fp8 scales
+  const Tile* tiles;
+  const int32_t* tile_count;
+  const int32_t* pair_row;
+  void* h;           // [N*K*I + N*Is] activation dtype
+  float* y;          // [N*K + N, H]
+  int N, H, E, I, Is, K, n_slices;
+};
+
+// One workgroup's GEMM: acc[mt] (16 x 16 each) for this wave's 16 columns,
+// over k in [0, Kdim).  asrc[i]: source row pointer (stage 0) of the i-th
+// activation vector this thread stages, or nullptr for rows past the tile;
+// brow: this lane's weight row at its k offset; bsc: its fp8 block scales.
+template <WFmt F, int MT>
+struct TiledGemm {
+  using Fr = Frag<F>;
+  using AT = typename Fr::AT;
+  using WT = typename Fr::WT;
+  static constexpr int T = 16 * MT;
+  static constexpr int KS = 256 / (int)sizeof(AT);  // k per stage (256 bytes of a row)
+  static constexpr int U = KS / Fr::kStep;          // MFMA steps per stage
+  static constexpr int VPR = 16;                    // 16-byte vectors per row per stage
+  static constexpr int RPP = kTiledThreads / VPR;   // rows staged per pass of the workgroup
+  static constexpr int AV = T / RPP;                // vectors per thread per stage
+  static constexpr int PAD = 16 / (int)sizeof(AT);
+  using Lds = AT[2][T][KS + PAD];
+
+  static __device__ __forceinline__ void run(Lds& As, const AT* const (&asrc)[AV],
+                                             const WT* brow, const float* bsc, int Kdim,
+                                             int mt_act, f32x4 (&acc)[MT]) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int col = lane & 15, kg = lane >> 4;
+    const int seg = tid % VPR, r0 = tid / VPR;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    u32x4 areg[AV];
+    typename Fr::B b0[U], b1[U];
+    auto load_a = [&](int k0) {
+#pragma unroll
+      for (int i = 0; i < AV; ++i)
+        areg[i] = asrc[i] ? *reinterpret_cast<const u32x4*>(asrc[i] + k0) : u32x4{0u, 0u, 0u, 0u};
+    };
+    auto store_a = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < AV; ++i)
+        *reinterpret_cast<u32x4*>(&As[buf][r0 + i * RPP][seg * (16 / (int)sizeof(AT))]) = areg[i];
+    };
+    auto load_b = [&](typename Fr::B (&b)[U], int k0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) b[u] = Fr::load_b(brow + k0 + u * Fr::kStep);
+    };
+    auto compute = [&](typename Fr::B (&b)[U], int buf, int k0) {
+      if constexpr (F == WFmt::FP8) {
+        f32x4 tmp[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) tmp[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            if (mt < mt_act) {
+              const typename Fr::A av = Fr::load_a(&As[buf][mt * 16 + col][u * Fr::kStep + kg * Fr::kLane]);
+              tmp[mt] = Fr::mma(av, b[u], tmp[mt]);
+            }
+        const float sc = bsc[k0 / 128];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[mt][v] = __builtin_fmaf(sc, tmp[mt][v], acc[mt][v]);
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            if (mt < mt_act) {
+              const typename Fr::A av = Fr::load_a(&As[buf][mt * 16 + col][u * Fr::kStep + kg * Fr::kLane]);
+              acc[mt] = Fr::mma(av, b[u], acc[mt]);
+            }
+          // keep the scheduler from hoisting every k step's operands at once
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+
+    const int S = Kdim / KS;
+    load_a(0);
+    load_b(b0, 0);
+    store_a(0);
+    __syncthreads();
+    for (int s = 0; s < S; s += 2) {
+      // stage s from buffer 0 / b0, prefetching stage s+1 into buffer 1 / b1
+      if (s + 1 < S) {
+        load_a((s + 1) * KS);
+        load_b(b1, (s + 1) * KS);
+      }
+      compute(b0, 0, s * KS);
+      if (s + 1 < S) store_a(1);
+      __syncthreads();
+      if (s + 1 >= S) break;
+      // stage s+1 from buffer 1 / b1, prefetching stage s+2 into buffer 0 / b0
+      if (s + 2 < S) {
+        load_a((s + 2) * KS);
+        load_b(b0, (s + 2) * KS);
+      }
+      compute(b1, 1, (s + 1) * KS);
+      if (s + 2 < S) store_a(0);
+      __syncthreads();
+    }
+  }
+};
+
+template <WFmt F, int MT>
+__global__ __launch_bounds__(kTiledThreads) void expert_up_tiled_kernel(TiledArgs a) {
+  using G = TiledGemm<F, MT>;
+  using AT = typename G::AT;
+  using WT = typename G::WT;
+  using Fr = Frag<F>;
+  __shared__ typename G::Lds As;
+  const int slot = blockIdx.x / a.n_slices, slice = blockIdx.x % a.n_slices;
+  if (slot >= *a.tile_count) return;
+  const Tile t = a.tiles[slot];
+  const bool shared = t.expert == a.E;
+  const int inter = shared ? a.Is : a.I;
+  if (slice * kTiledUpCols >= inter) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, kg = lane >> 4;
+  const int H = a.H;
+
+  const AT* asrc[G::AV];
+#pragma unroll
+  for (int i = 0; i < G::AV; ++i) {
+    const int r = tid / G::VPR + i * G::RPP;
+    const int src = r < t.rows ? (shared ? t.start + r : a.pair_row[t.start + r]) : -1;
+    asrc[i] = src >= 0 ? static_cast<const AT*>(a.x) + (size_t)src * H + (tid % G::VPR) * (16 / (int)sizeof(AT))
+                       : nullptr;
+  }
+  const WT* W = shared ? static_cast<const WT*>(a.sw) : static_cast<const WT*>(a.w) + (size_t)t.expert * 2 * a.I * H;
+  const float* S = nullptr;
+  if constexpr (F == WFmt::FP8) S = shared ? a.sws : a.ws + (size_t)t.expert * (2 * a.I / 128) * (H / 128);
+  const int i0 = slice * kTiledUpCols + wave * 8;
+  const int wr = col < 8 ? i0 + col : inter + i0 + col - 8;  // gate row / up row
+  const WT* brow = W + (size_t)wr * H + kg * Fr::kLane;
+  const float* bsc = (F == WFmt::FP8) ? S + (size_t)(wr / 128) * (H / 128) : nullptr;
+  const int mt_act = (t.rows + 15) >> 4;
+  f32x4 acc[MT];
+  G::run(As, asrc, brow, bsc, H, mt_act, acc);
+
+  AT* h = static_cast<AT*>(a.h) +
+          (shared ? (size_t)a.N * a.K * a.I + (size_t)t.start * a.Is : (size_t)t.start * a.I);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float gate = acc[mt][v];
+      const float up = shfl_xor_f(gate, 8);
+      const int m = mt * 16 + kg * 4 + v;
+      if (col < 8 && m < t.rows) store_act<AT>(h + (size_t)m * inter + i0 + col, silu(gate) * up);
+    }
+}
+
+template <WFmt F, int MT>
+__global__ __launch_bounds__(kTiledThreads) void expert_down_tiled_kernel(TiledArgs a) {
+  using G = TiledGemm<F, MT>;
+  using AT = typename G::AT;
+  using WT = typename G::WT;
+  using Fr = Frag<F>;
+  __shared__ typename G::Lds As;
+  const int slot = blockIdx.x / a.n_slices, slice = blockIdx.x % a.n_slices;
+  if (slot >= *a.tile_count) return;
+  const Tile t = a.tiles[slot];
+  const bool shared = t.expert == a.E;
+  const int inter = shared ? a.Is : a.I;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, kg = lane >> 4;
+  const int H = a.H;
+
+  const AT* hb = static_cast<const AT*>(a.h) +
+                 (shared ? (size_t)a.N * a.K * a.I + (size_t)t.start * a.Is : (size_t)t.start * a.I);
+  const AT* asrc[G::AV];
+#pragma unroll
+  for (int i = 0; i < G::AV; ++i) {
+    const int r = tid / G::VPR + i * G::RPP;
+    asrc[i] = r < t.rows ? hb + (size_t)r * inter + (tid % G::VPR) * (16 / (int)sizeof(AT)) : nullptr;
+  }
+  const WT* W = shared ? static_cast<const WT*>(a.sw) : static_cast<const WT*>(a.w) + (size_t)t.expert * H * a.I;
+  const float* S = nullptr;
+  if constexpr (F == WFmt::FP8) S = shared ? a.sws : a.ws + (size_t)t.expert * (H / 128) * (a.I / 128);
+  const int c0 = slice * kTiledDownCols + wave * 16;
+  const int orow = c0 + col;  // W2 row = output column
+  const WT* brow = W + (size_t)orow * inter + kg * Fr::kLane;
+  const float* bsc = (F == WFmt::FP8) ? S + (size_t)(orow / 128) * (inter / 128) : nullptr;
+  const int mt_act = (t.rows + 15) >> 4;
+  f32x4 acc[MT];
+  G::run(As, asrc, brow, bsc, inter, mt_act, acc);
+
+  float* y = a.y + ((shared ? (size_t)a.N * a.K : 0) + (size_t)t.start) * H;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = mt * 16 + kg * 4 + v;
+      if (m < t.rows) y[(size_t)m * H + c0 + col] = acc[mt][v];
+    }
+}
+
+template <bool kUp, WFmt F, int MT>
+static void launch_tiled(const TiledArgs& a, unsigned grid, hipStream_t s) {
+  if constexpr (kUp)
+    expert_up_tiled_kernel<F, MT><<<grid, kTiledThreads, 0, s>>>(a);
+  else
+    expert_down_tiled_kernel<F, MT><<<grid, kTiledThreads, 0, s>>>(a);
+}
+
+template <bool kUp, WFmt F>
+static void launch_tiled_mt(const TiledArgs& a, int mt_max, unsigned grid, hipStream_t s) {
+  switch (mt_max) {
+    case 2: launch_tiled<kUp, F, 2>(a, grid, s); break;
+    case 4: launch_tiled<kUp, F, 4>(a, grid, s); break;
+    default: launch_tiled<kUp, F, 8>(a, grid, s); break;
+  }
+}
+
+hipError_t launch_expert_tiled(const Plan& p, const cmoe_weights& w, const void* x, bool up,
+                               hipStream_t s) {
+  TiledArgs a;
+  a.x = x;
+  a.w = up ? w.w13 : w.w2;
+  a.ws = up ? w.w13_scale : w.w2_scale;
+  a.sw = up ? w.shared_w13 : w.shared_w2;
+  a.sws = up ? w.shared_w13_scale : w.shared_w2_scale;
+  a.tiles = p.tiles;
+  a.tile_count = p.tile_count;
+  a.pair_row = p.pair_row;
+  a.h = p.h;
+  a.y = p.y;
+  a.N = p.N;
+  a.H = p.H;
+  a.E = p.E;
+  a.I = p.I;
+  a.Is = p.Is;
+  a.K = p.K;
+  a.n_slices = up ? (p.I > p.Is ? p.I : p.Is) / kTiledUpCols : p.H / kTiledDownCols;
+  const unsigned grid = (unsigned)p.max_tiles * (unsigned)a.n_slices;
+  const WFmt f = p.wt == CMOE_FP8_E4M3 ? WFmt::FP8 : p.wt == CMOE_F32 ? WFmt::F32 : WFmt::BF16;
+  if (up) {
+    if (f == WFmt::FP8) launch_tiled_mt<true, WFmt::FP8>(a, p.mt_max, grid, s);
+    else if (f == WFmt::F32) launch_tiled_mt<true, WFmt::F32>(a, p.mt_max, grid, s);
+    else launch_tiled_mt<true, WFmt::BF16>(a, p.mt_max, grid, s);
+  } else {
+    if (f == WFmt::FP8) launch_tiled_mt<false, WFmt::FP8>(a, p.mt_max, grid, s);
+    else if (f == WFmt::F32) launch_tiled_mt<false, WFmt::F32>(a, p.mt_max, grid, s);
+    else launch_tiled_mt<false, WFmt::BF16>(a, p.mt_max, grid, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace cmoe
