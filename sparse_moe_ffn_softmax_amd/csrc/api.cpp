@@ -84,7 +84,7 @@ cmoe_status check_problem(const cmoe_problem* p, int32_t top_k) {
 }
 
 struct Layout {
-  size_t logits, topk, gates, counts, offsets, pair_row, pair_pos, prefix, rowmask, tiles,
+  size_t logits, topk, gates, counts, offsets, pair_row, pair_pos, rowmask, tiles,
       tile_count, sync, h, y, total;
   int max_tiles, mask_words, mt_max;
 };
@@ -115,7 +115,6 @@ Layout layout(const cmoe_problem& p, int K) {
   L.offsets = take((E + 1) * 4);
   L.pair_row = take(NK * 4);
   L.pair_pos = take(NK * 4);
-  L.prefix = take(E * L.mask_words * 4);
   L.rowmask = take(E * L.mask_words * 4);
   L.tiles = take((size_t)L.max_tiles * sizeof(cmoe::Tile));
   L.tile_count = take(4);
@@ -156,7 +155,6 @@ void carve(Plan& p, const cmoe_problem& pr, int K, void* ws, const cmoe_routing*
   p.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
   p.pair_row = reinterpret_cast<int32_t*>(base + L.pair_row);
   p.pair_pos = reinterpret_cast<int32_t*>(base + L.pair_pos);
-  p.prefix = reinterpret_cast<int32_t*>(base + L.prefix);
   p.rowmask = reinterpret_cast<uint32_t*>(base + L.rowmask);
   p.tiles = reinterpret_cast<Tile*>(base + L.tiles);
   p.tile_count = reinterpret_cast<int32_t*>(base + L.tile_count);

@@ -45,7 +45,6 @@ struct Plan {
   int32_t* offsets;      // [E+1]
   int32_t* pair_row;     // [N*K]  source row of each routed pair, expert-major
   int32_t* pair_pos;     // [N*K]  pair position of (row, slot), -1 if unused
-  int32_t* prefix;       // [E, mask_words] exclusive popcount prefix of rowmask
   uint32_t* rowmask;     // [E, mask_words] bit r set if row r routes to expert e
   Tile* tiles;           // [max_tiles]
   int32_t* tile_count;   // [1]

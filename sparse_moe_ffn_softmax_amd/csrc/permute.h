@@ -15,7 +15,7 @@
 // integer results, independent of thread timing.
 //
 // One workgroup of 1024 threads does the whole call; the masks live in LDS
-// when they fit (N <= 1024 rows at E = 256), else in the workspace, where they
+// when they fit (N <= 2048 rows at E = 256), else in the workspace, where they
 // are touched only with device-scope atomics.
 #pragma once
 #include "cmoe_device.h"
@@ -46,8 +46,12 @@ __device__ int block_exclusive_scan(int v, int* scratch /*[16]*/, int* total) {
   return wave_base + incl - v;
 }
 
-// Row masks of E x W words: in LDS when they fit, else in the workspace.
-constexpr int kLdsMaskWords = 8192;
+// Row masks of E x W words (W = ceil(N/32)): in LDS when they fit (N <= 2048
+// rows at E = 256), else in the workspace.  A coarse per-expert popcount
+// prefix over groups of G mask words always lives in LDS; a pair's rank adds
+// the popcounts of at most G-1 words of its group.
+constexpr int kLdsMaskWords = 16384;
+constexpr int kPrefixWords = 8192;
 
 struct PermuteLds {
   int cnt[256];
@@ -55,27 +59,24 @@ struct PermuteLds {
   int scan[16];
 };
 
-// The whole permutation, run by one workgroup of 1024 threads.  lds: scratch
-// of 2 * kLdsMaskWords words (masks, then their popcount prefix), used only
-// when kLdsMask.
+// The whole permutation, run by one workgroup of 1024 threads.
+// mask_lds: kLdsMaskWords words (used when kLdsMask); pref_lds: kPrefixWords.
 template <bool kLdsMask>
-__device__ void permute_block(const Plan& p, PermuteLds& L, uint32_t* lds) {
-  uint32_t* mask_s = lds;
-  int32_t* prefix = kLdsMask ? reinterpret_cast<int32_t*>(lds + kLdsMaskWords) : p.prefix;
+__device__ void permute_block(const Plan& p, PermuteLds& L, uint32_t* mask_lds, int32_t* pref_lds) {
   int* cnt_s = L.cnt;
   int* off_s = L.off;
   int* scan_scratch = L.scan;
   const int tid = threadIdx.x;
   const int N = p.N, K = p.K, E = p.E, W = p.mask_words;
   const int NK = N * K;
-  uint32_t* masks = kLdsMask ? mask_s : p.rowmask;
+  uint32_t* masks = kLdsMask ? mask_lds : p.rowmask;
   auto mask_load = [&](size_t i) -> uint32_t {
-    if constexpr (kLdsMask) return mask_s[i];
+    if constexpr (kLdsMask) return mask_lds[i];
     else return __hip_atomic_load(p.rowmask + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
 
   for (int i = tid; i < E * W; i += 1024) {
-    if constexpr (kLdsMask) mask_s[i] = 0u;
+    if constexpr (kLdsMask) mask_lds[i] = 0u;
     else __hip_atomic_store(p.rowmask + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (tid < 256) cnt_s[tid] = 0;
@@ -111,12 +112,23 @@ __device__ void permute_block(const Plan& p, PermuteLds& L, uint32_t* lds) {
     }
   }
 
-  // per-expert exclusive popcount prefix over mask words
+  // coarse exclusive popcount prefix per expert over groups of G words
+  int G = 1;
+  while (E * ((W + G - 1) / G) > kPrefixWords) G <<= 1;
+  const int J = (W + G - 1) / G;
+  for (int i = tid; i < E * J; i += 1024) {
+    const int e = i / J, j = i % J;
+    int c = 0;
+    for (int w = j * G; w < min(W, j * G + G); ++w) c += __popc(mask_load((size_t)e * W + w));
+    pref_lds[i] = c;
+  }
+  __syncthreads();
   for (int e = tid; e < E; e += 1024) {
     int run = 0;
-    for (int w = 0; w < W; ++w) {
-      prefix[(size_t)e * W + w] = run;
-      run += __popc(mask_load((size_t)e * W + w));
+    for (int j = 0; j < J; ++j) {
+      const int c = pref_lds[e * J + j];
+      pref_lds[e * J + j] = run;
+      run += c;
     }
   }
   __syncthreads();
@@ -126,10 +138,11 @@ __device__ void permute_block(const Plan& p, PermuteLds& L, uint32_t* lds) {
     const int e = p.topk[i];
     int pos = -1;
     if (e >= 0) {
-      const int r = i / K;
-      const uint32_t word = mask_load((size_t)e * W + (r >> 5));
-      const uint32_t below = word & ((1u << (r & 31)) - 1u);
-      pos = off_s[e] + prefix[(size_t)e * W + (r >> 5)] + __popc(below);
+      const int r = i / K, w = r >> 5, j = w / G;
+      int rank = pref_lds[e * J + j];
+      for (int w2 = j * G; w2 < w; ++w2) rank += __popc(mask_load((size_t)e * W + w2));
+      rank += __popc(mask_load((size_t)e * W + w) & ((1u << (r & 31)) - 1u));
+      pos = off_s[e] + rank;
       p.pair_row[pos] = r;
       if (p.out_perm) p.out_perm[pos] = i;
     }

@@ -360,14 +360,17 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
   } else {
     __syncthreads();
   }
+  // the probability and logit buffers are dead now: masks and prefix reuse them
   if (plan.E * plan.mask_words <= kLdsMaskWords)
-    permute_block<true>(plan, perm_lds, reinterpret_cast<uint32_t*>(p_s));
+    permute_block<true>(plan, perm_lds, reinterpret_cast<uint32_t*>(p_s), reinterpret_cast<int32_t*>(l_s));
   else
-    permute_block<false>(plan, perm_lds, nullptr);
+    permute_block<false>(plan, perm_lds, nullptr, reinterpret_cast<int32_t*>(l_s));
 }
 
-static_assert(sizeof(double) * kMaxRows * kPStride >= 2 * sizeof(uint32_t) * kLdsMaskWords,
-              "the permutation's LDS masks and prefix reuse the probability buffer");
+static_assert(sizeof(double) * kMaxRows * kPStride >= sizeof(uint32_t) * kLdsMaskWords,
+              "the permutation's LDS masks reuse the probability buffer");
+static_assert(sizeof(float) * kMaxRows * kMaxExperts >= sizeof(int32_t) * kPrefixWords,
+              "the permutation's popcount prefix reuses the logit buffer");
 
 hipError_t launch_route_blocks(const Plan& p, float tau, hipStream_t s) {
   route_block_kernel<<<p.B, kThreads, 0, s>>>(p, tau);

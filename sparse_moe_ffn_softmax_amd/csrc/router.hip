@@ -61,7 +61,9 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
   constexpr int WPT = (WV + 255) / 256;
   __shared__ float xs[2][8][RT][KP];
   __shared__ float ws[2][8][ET][KP];
-  __shared__ float part[8][RT][ET + 1];
+  // the chunk partial sums reuse the x staging buffer once the k loop is done
+  static_assert(sizeof(float) * 8 * RT * (ET + 1) <= sizeof(xs), "partials must fit in xs");
+  auto part = reinterpret_cast<float(*)[RT][ET + 1]>(&xs[0][0][0][0]);
 
   const int tid = threadIdx.x;
   // zero the call-local counters used by the kernels queued after this one
@@ -203,9 +205,9 @@ hipError_t launch_router(const Plan& p, const void* x, const float* router_w,
     else if (L % 32 == 0) launch_shape<1, 1, 32>(p, x, router_w, router_b, s);
     else launch_shape<1, 1, 16>(p, x, router_w, router_b, s);
   } else {
-    // many rows: 4x4 register tiles
-    if (L % 32 == 0) launch_shape<4, 4, 32>(p, x, router_w, router_b, s);
-    else launch_shape<4, 4, 16>(p, x, router_w, router_b, s);
+    // many rows: 4x4 register tiles, 16-position slices (about 60 KiB of
+    // LDS, so two workgroups share a CU)
+    launch_shape<4, 4, 16>(p, x, router_w, router_b, s);
   }
   return hipGetLastError();
 }
