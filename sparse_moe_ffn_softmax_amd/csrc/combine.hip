@@ -35,15 +35,27 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int r = blockIdx.y;
   const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (c >= H) return;
+  // every load is issued before the first add: positions and gates, then the
+  // shared row and the routed rows (K <= 8)
+  int pos[8];
+  float g[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    pos[j] = j < K ? pair_pos[(size_t)r * K + j] : -1;
+    g[j] = j < K ? gates[(size_t)r * K + j] : 0.0f;
+  }
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   if (has_shared) acc = *reinterpret_cast<const f32x4*>(y + ((size_t)N * K + r) * H + c);
-  for (int j = 0; j < K; ++j) {
-    const int pos = pair_pos[(size_t)r * K + j];
-    if (pos < 0) continue;
-    const float g = gates[(size_t)r * K + j];
-    const f32x4 v = *reinterpret_cast<const f32x4*>(y + (size_t)pos * H + c);
+  f32x4 v[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(g, v[i], acc[i]);
+  for (int j = 0; j < 8; ++j)
+    v[j] = pos[j] >= 0 ? *reinterpret_cast<const f32x4*>(y + (size_t)pos[j] * H + c)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (pos[j] < 0) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(g[j], v[j][i], acc[i]);
   }
   store4<OT>(out + (size_t)r * H + c, acc);
 }

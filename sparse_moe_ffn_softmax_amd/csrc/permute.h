@@ -1,6 +1,5 @@
 // permute.h -- row -> expert permutation and the grouped-GEMM work list
-// (device code; run by the last routing workgroup of a call, see
-// route_block.hip).
+// (device code, run at the end of the routing kernel, see route_block.hip).
 //
 // Every routed (row, slot) pair gets a position in an expert-major order:
 // experts ascending, and inside an expert rows ascending (the key
@@ -14,36 +13,125 @@
 // mask bits below its row.  Counts, positions and tiles are all exact
 // integer results, independent of thread timing.
 //
-// One workgroup of 1024 threads does the whole call; the masks live in LDS
-// when they fit (N <= 2048 rows at E = 256), else in the workspace, where they
-// are touched only with device-scope atomics.
+// Two variants:
+//  * permute_single: the call is one block of at most 32 rows, whose routing
+//    workgroup still holds the top-k result and one mask word per expert in
+//    LDS; two barriers and no global round trips.
+//  * permute_block: many blocks; the workgroup that finishes its routing
+//    last reads every block's top-k back and builds the masks in LDS (N <=
+//    2048 rows at E = 256) or in the workspace.
 #pragma once
 #include "cmoe_device.h"
 #include "cmoe_launch.h"
 
 namespace cmoe {
 
-// exclusive scan of v over the 1024 threads of the workgroup; returns the
-// thread's exclusive prefix and writes the total to *total.
-__device__ int block_exclusive_scan(int v, int* scratch /*[16]*/, int* total) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int incl = v;
+// inclusive prefix sum over the 64 lanes of a wave (all lanes active):
+// shifted adds inside each 16-lane row, then the totals of the rows below
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15);
+  const int r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = lane >> 4;
+  return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
+struct PermuteLds {
+  int cnt[256];
+  int off[257];
+};
+
+// Run by one whole wave (lanes 0..63): expert e = 4*lane + i has L.cnt[e]
+// pairs.  Writes the exclusive offsets (LDS and the call's buffers) and the
+// work list: ceil(count / T) tiles per expert, experts ascending, then the
+// shared expert's tiles over the N rows in order.
+__device__ __forceinline__ void offsets_and_tiles(const Plan& p, PermuteLds& L) {
+  const int lane = threadIdx.x & 63;
+  const int E = p.E, T = p.tile_rows;
+  int c[4], nt[4], csum = 0, tsum = 0;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * lane + i;
+    c[i] = e < E ? L.cnt[e] : 0;
+    nt[i] = (c[i] + T - 1) / T;
+    csum += c[i];
+    tsum += nt[i];
   }
-  if (lane == 63) scratch[wave] = incl;
-  __syncthreads();
-  int wave_base = 0, all = 0;
-  for (int w = 0; w < 16; ++w) {
-    const int t = scratch[w];
-    if (w < wave) wave_base += t;
-    all += t;
+  const int cinc = wave_incl_scan(csum), tinc = wave_incl_scan(tsum);
+  const int ctot = __builtin_amdgcn_readlane(cinc, 63), ttot = __builtin_amdgcn_readlane(tinc, 63);
+  int coff = cinc - csum, toff = tinc - tsum;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * lane + i;
+    if (e < E) {
+      L.off[e] = coff;
+      p.counts[e] = c[i];
+      p.offsets[e] = coff;
+      if (p.out_counts) p.out_counts[e] = c[i];
+      if (p.out_offsets) p.out_offsets[e] = coff;
+      for (int t = 0; t < nt[i]; ++t) {
+        Tile tile;
+        tile.expert = e;
+        tile.start = coff + t * T;
+        tile.rows = min(T, c[i] - t * T);
+        tile.pad = 0;
+        p.tiles[toff + t] = tile;
+      }
+    }
+    coff += c[i];
+    toff += nt[i];
+  }
+  if (lane == 0) {
+    L.off[E] = ctot;
+    p.offsets[E] = ctot;
+    if (p.out_offsets) p.out_offsets[E] = ctot;
+  }
+  const int ns = p.Is > 0 ? (p.N + T - 1) / T : 0;
+  for (int t = lane; t < ns; t += 64) {
+    Tile tile;
+    tile.expert = E;
+    tile.start = t * T;
+    tile.rows = min(T, p.N - t * T);
+    tile.pad = 0;
+    p.tiles[ttot + t] = tile;
+  }
+  if (lane == 0) *p.tile_count = ttot + ns;
+}
+
+// One block of N <= 32 rows: tk_s[N*K] holds the block's top-k (-1 for an
+// empty slot) and mask_s[e] bit r is set iff row r routes to expert e.
+// Called by all 1024 threads after a barrier that follows those writes.
+__device__ void permute_single(const Plan& p, PermuteLds& L, const uint32_t* mask_s,
+                               const int* tk_s) {
+  const int tid = threadIdx.x;
+  const int NK = p.N * p.K;
+  if (tid < 64) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * tid + i;
+      if (e < p.E) L.cnt[e] = __popc(mask_s[e]);
+    }
+    offsets_and_tiles(p, L);
   }
   __syncthreads();
-  *total = all;
-  return wave_base + incl - v;
+  if (tid < NK) {
+    const int e = tk_s[tid];
+    int pos = -1;
+    if (e >= 0) {
+      const int r = tid / p.K;
+      pos = L.off[e] + __popc(mask_s[e] & ((1u << r) - 1u));
+      p.pair_row[pos] = r;
+      if (p.out_perm) p.out_perm[pos] = tid;
+    }
+    p.pair_pos[tid] = pos;
+  }
+  if (p.out_perm)
+    for (int i = L.off[p.E] + tid; i < NK; i += 1024) p.out_perm[i] = -1;
 }
 
 // Row masks of E x W words (W = ceil(N/32)): in LDS when they fit (N <= 2048
@@ -53,19 +141,11 @@ __device__ int block_exclusive_scan(int v, int* scratch /*[16]*/, int* total) {
 constexpr int kLdsMaskWords = 16384;
 constexpr int kPrefixWords = 8192;
 
-struct PermuteLds {
-  int cnt[256];
-  int off[257];
-  int scan[16];
-};
-
-// The whole permutation, run by one workgroup of 1024 threads.
-// mask_lds: kLdsMaskWords words (used when kLdsMask); pref_lds: kPrefixWords.
+// The whole permutation for many blocks, run by one workgroup of 1024
+// threads.  mask_lds: kLdsMaskWords words (used when kLdsMask); pref_lds:
+// kPrefixWords words.
 template <bool kLdsMask>
 __device__ void permute_block(const Plan& p, PermuteLds& L, uint32_t* mask_lds, int32_t* pref_lds) {
-  int* cnt_s = L.cnt;
-  int* off_s = L.off;
-  int* scan_scratch = L.scan;
   const int tid = threadIdx.x;
   const int N = p.N, K = p.K, E = p.E, W = p.mask_words;
   const int NK = N * K;
@@ -79,40 +159,19 @@ __device__ void permute_block(const Plan& p, PermuteLds& L, uint32_t* mask_lds, 
     if constexpr (kLdsMask) mask_lds[i] = 0u;
     else __hip_atomic_store(p.rowmask + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (tid < 256) cnt_s[tid] = 0;
   __syncthreads();
 
-  // masks and counts
   for (int i = tid; i < NK; i += 1024) {
     const int e = p.topk[i];
     if (e >= 0) {
       const int r = i / K;
       atomicOr(masks + (size_t)e * W + (r >> 5), 1u << (r & 31));
-      atomicAdd(&cnt_s[e], 1);
     }
   }
   __syncthreads();
 
-  // offsets: exclusive scan of counts
-  int total;
-  {
-    const int v = tid < E ? cnt_s[tid] : 0;
-    const int ex = block_exclusive_scan(v, scan_scratch, &total);
-    if (tid < E) {
-      off_s[tid] = ex;
-      p.counts[tid] = v;
-      p.offsets[tid] = ex;
-      if (p.out_counts) p.out_counts[tid] = v;
-      if (p.out_offsets) p.out_offsets[tid] = ex;
-    }
-    if (tid == 0) {
-      off_s[E] = total;
-      p.offsets[E] = total;
-      if (p.out_offsets) p.out_offsets[E] = total;
-    }
-  }
-
-  // coarse exclusive popcount prefix per expert over groups of G words
+  // coarse popcount prefix per expert over groups of G words; the last
+  // running total is the expert's count
   int G = 1;
   while (E * ((W + G - 1) / G) > kPrefixWords) G <<= 1;
   const int J = (W + G - 1) / G;
@@ -130,7 +189,10 @@ __device__ void permute_block(const Plan& p, PermuteLds& L, uint32_t* mask_lds, 
       pref_lds[e * J + j] = run;
       run += c;
     }
+    L.cnt[e] = run;
   }
+  __syncthreads();
+  if (tid < 64) offsets_and_tiles(p, L);
   __syncthreads();
 
   // positions
@@ -142,38 +204,14 @@ __device__ void permute_block(const Plan& p, PermuteLds& L, uint32_t* mask_lds, 
       int rank = pref_lds[e * J + j];
       for (int w2 = j * G; w2 < w; ++w2) rank += __popc(mask_load((size_t)e * W + w2));
       rank += __popc(mask_load((size_t)e * W + w) & ((1u << (r & 31)) - 1u));
-      pos = off_s[e] + rank;
+      pos = L.off[e] + rank;
       p.pair_row[pos] = r;
       if (p.out_perm) p.out_perm[pos] = i;
     }
     p.pair_pos[i] = pos;
   }
   if (p.out_perm)
-    for (int i = total + tid; i < NK; i += 1024) p.out_perm[i] = -1;
-
-  // work tiles: experts ascending, then the shared expert (index E)
-  {
-    const bool has_shared = p.Is > 0;
-    int n = 0;
-    if (tid < E) n = cnt_s[tid];
-    else if (tid == E && has_shared) n = N;
-    const int T = p.tile_rows;
-    const int nt = (n + T - 1) / T;
-    int ntiles;
-    const int base = block_exclusive_scan(tid <= E ? nt : 0, scan_scratch, &ntiles);
-    if (tid <= E) {
-      const int start0 = tid < E ? off_s[tid] : 0;
-      for (int t = 0; t < nt; ++t) {
-        Tile tile;
-        tile.expert = tid;
-        tile.start = start0 + t * T;
-        tile.rows = min(T, n - t * T);
-        tile.pad = 0;
-        p.tiles[base + t] = tile;
-      }
-    }
-    if (tid == 0) *p.tile_count = ntiles;
-  }
+    for (int i = L.off[E] + tid; i < NK; i += 1024) p.out_perm[i] = -1;
 }
 
 }  // namespace cmoe

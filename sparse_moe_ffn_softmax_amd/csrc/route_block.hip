@@ -63,15 +63,21 @@ __constant__ double kInvFact[14] = {
     0x1.a01a01a01a01ap-16, 0x1.71de3a556c734p-19, 0x1.27e4fb7789f5cp-22, 0x1.ae64567f544e4p-26,
     0x1.1eed8eff8d898p-29, 0x1.6124613a86d09p-33};
 
+// Every step is an fp64 primitive, so the result is reproducible bit for bit;
+// below -708 (outside the normal range of the result) the value is 0.  The
+// operations run unconditionally and the cut-off is a select, so a wave can
+// interleave several independent evaluations.
 __device__ __forceinline__ double exp_reduced(double d) {
-  if (d < -708.0) return 0.0;  // below the normal range
   const double n = __builtin_rint(d * kInvLn2);
   double r = __builtin_fma(-n, kLn2Head, d);
   r = __builtin_fma(-n, kLn2Tail, r);
   double poly = kInvFact[13];
 #pragma unroll
   for (int i = 12; i >= 0; --i) poly = __builtin_fma(poly, r, kInvFact[i]);
-  return __builtin_ldexp(poly, static_cast<int>(n));
+  // the clamp only matters for the discarded lanes (d < -708 or NaN)
+  const int ni = static_cast<int>(__builtin_fmin(__builtin_fmax(n, -1100.0), 1100.0));
+  const double v = __builtin_ldexp(poly, ni);
+  return d < -708.0 ? 0.0 : v;
 }
 
 // DPP lane-exchange controls (within each row of 16 lanes)
@@ -85,24 +91,20 @@ __device__ __forceinline__ uint32_t dpp(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
 }
 
-// Candidate keys: (order-preserving logit bits) << 32 | ~id, so the larger
-// key is the larger logit and, on equal logits, the lower id; 0 = none.
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
-  const uint32_t lo = dpp<CTRL>(static_cast<uint32_t>(v));
-  const uint32_t hi = dpp<CTRL>(static_cast<uint32_t>(v >> 32));
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
 // exchange with lane ^ 16 inside each 32-lane half (ds_swizzle bitmask mode)
-__device__ __forceinline__ uint64_t swz_xor16(uint64_t v) {
+__device__ __forceinline__ uint32_t swz_xor16(uint32_t v) {
   constexpr int kPattern = 0x1F | (0x10 << 10);  // and 0x1F, or 0, xor 0x10
-  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), kPattern));
-  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v >> 32), kPattern));
-  return (static_cast<uint64_t>(hi) << 32) | lo;
+  return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), kPattern));
 }
 
-__device__ __forceinline__ uint64_t max64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+// maximum over each 32-lane half of the wave, in every lane of that half
+__device__ __forceinline__ uint32_t half_max_u32(uint32_t v) {
+  v = max(v, dpp<kDppXor1>(v));
+  v = max(v, dpp<kDppXor2>(v));
+  v = max(v, dpp<kDppHalfMirror>(v));
+  v = max(v, dpp<kDppMirror>(v));
+  return max(v, swz_xor16(v));
+}
 
 __device__ __forceinline__ float wave_max_f32(float v) {
   v = fmaxf(v, __uint_as_float(dpp<kDppXor1>(__float_as_uint(v))));
@@ -132,6 +134,8 @@ __device__ __forceinline__ void sort8_desc(uint64_t (&k)[8]) {
   cswap(k, 1, 2); cswap(k, 3, 4); cswap(k, 5, 6);
 }
 
+// Candidate keys: (order-preserving logit bits) << 32 | ~id, so the larger
+// key is the larger logit and, on equal logits, the lower id; 0 = none.
 __device__ __forceinline__ uint32_t logit_key(float l) {
   const uint32_t b = __float_as_uint(l + 0.0f);  // -0 becomes +0: equal logits tie
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
@@ -145,10 +149,11 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
   int32_t* __restrict__ coreset_size = plan.coreset_size;
   double* __restrict__ block_mass = plan.block_mass;
   __shared__ float l_s[kMaxRows][kMaxExperts];
-  // u, then p in place; one pad slot per 32 experts keeps the per-chunk
-  // serial sums of different (row, chunk) threads on different banks
+  // u; then each lane's sorted top-k candidates; then (many blocks) the
+  // permutation's row masks.  One pad slot per 32 experts keeps the
+  // per-chunk serial sums of different (row, chunk) threads on different banks.
   __shared__ double p_s[kMaxRows * kPStride];
-  __shared__ double zpart[kMaxRows][8];
+  __shared__ double zpart[kMaxRows][8];  // Z partials; later the chosen u
   __shared__ double z_s[kMaxRows];
   __shared__ float m_s[kMaxRows];
   __shared__ double mass_s[kMaxExperts];
@@ -157,6 +162,8 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
   __shared__ int order_s[kMaxExperts];
   __shared__ int rank_s[kMaxExperts];
   __shared__ int rcnt[4][kMaxExperts];
+  __shared__ uint32_t mask1_s[kMaxExperts];  // one-block calls: rows per expert
+  __shared__ int tk_s[kMaxRows * 8];          // this block's top-k
   __shared__ int m_sh;
   __shared__ int last_sh;
   __shared__ PermuteLds perm_lds;
@@ -168,9 +175,11 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
   const float* lb = plan.logits + (size_t)b * R * E;
 
   if (tid == 0) m_sh = E;
+  if (tid < kMaxExperts) mask1_s[tid] = 0u;
 
   // rows w and w+16 on wave w: logits to LDS, row maxima (exact, order-free),
-  // and u = exp(l - max) as 8 independent chains per lane
+  // and u = exp(l - max) as 8 independent chains per lane.  Rows past R and
+  // experts past E hold -inf logits and u = 0 (rows past R: NaN), never read.
   {
     float lv[2][4], mx[2];
 #pragma unroll
@@ -182,20 +191,19 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
         const int e = lane + 64 * s;
         const bool ok = r < R && e < E;
         const float v = ok ? lb[r * E + e] : -INFINITY;
-        if (ok) l_s[r][e] = v;
+        l_s[r][e] = v;
         lv[h][s] = v;
         mm = fmaxf(mm, v);
       }
       mx[h] = wave_max_f32(mm);
-      if (lane == 0 && r < R) m_s[r] = mx[h];
+      if (lane == 0) m_s[r] = mx[h];
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int r = wave + 16 * h, e = lane + 64 * s;
-        if (r < R && e < E)
-          p_s[pidx(r, e)] = exp_reduced(static_cast<double>(lv[h][s]) - static_cast<double>(mx[h]));
+        p_s[pidx(r, e)] = exp_reduced(static_cast<double>(lv[h][s]) - static_cast<double>(mx[h]));
       }
   }
   __syncthreads();
@@ -226,20 +234,18 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
   }
   __syncthreads();
 
-  // p = u / Z, all elements in parallel (8 per thread)
-#pragma unroll
-  for (int t = 0; t < kMaxRows * kMaxExperts / kThreads; ++t) {
-    const int i = tid + t * kThreads;
-    const int r = i >> 8, e = i & 255;
-    if (r < R && e < E) p_s[pidx(r, e)] = p_s[pidx(r, e)] / z_s[r];
-  }
-  __syncthreads();
-
-  // block mass, one thread per expert, rows ascending
+  // block mass, one thread per expert: p = u / Z for each row, summed over
+  // rows ascending (R is a multiple of 8; the 8 divisions of a group are
+  // independent, only the adds are chained)
   if (tid < E) {
     double acc = 0.0;
-#pragma unroll 8
-    for (int r = 0; r < R; ++r) acc = acc + p_s[pidx(r, tid)];
+    for (int r0 = 0; r0 < R; r0 += 8) {
+      double q[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = p_s[pidx(r0 + i, tid)] / z_s[r0 + i];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc = acc + q[i];
+    }
     mass_s[tid] = acc;
   }
   __syncthreads();
@@ -251,12 +257,11 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
       const double me = mass_s[e];
       int cnt = 0;
       const int lo = part * 64, hi = min(E, lo + 64);
-      const int mid = max(lo, min(hi, e));
-      // experts below e win ties, experts above e must be strictly larger
 #pragma unroll 8
-      for (int o = lo; o < mid; ++o) cnt += mass_s[o] >= me;
-#pragma unroll 8
-      for (int o = max(mid, e + 1); o < hi; ++o) cnt += mass_s[o] > me;
+      for (int o = lo; o < hi; ++o) {
+        const double mo = mass_s[o];
+        cnt += (mo > me) | ((mo == me) & (o < e));
+      }
       rcnt[part][e] = cnt;
     }
   }
@@ -269,15 +274,19 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
   }
   __syncthreads();
 
-  // sequential prefix sum in mass order (the contract's order), one lane
+  // sequential prefix sum in mass order (the contract's order), one lane;
+  // batches of 16, the next batch's loads in flight while this one adds.
+  // Loads and stores are unconditional (the arrays hold 256 entries; values
+  // past E are never read back).
   if (tid == 0) {
-    // batches of 16: loads and stores unconditional (the arrays hold 256
-    // entries; values past E are never read back), adds strictly in order
     double c = 0.0;
-    for (int i0 = 0; i0 < E; i0 += 16) {
-      double v[16];
+    double v[16], nxt[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = smass_s[i0 + i];
+    for (int i = 0; i < 16; ++i) v[i] = smass_s[i];
+    for (int i0 = 0; i0 < E; i0 += 16) {
+      const int n0 = min(i0 + 16, kMaxExperts - 16);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) nxt[i] = smass_s[n0 + i];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         c = c + v[i];
@@ -285,6 +294,8 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) cum_s[i0 + i] = v[i];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = nxt[i];
     }
   }
   __syncthreads();
@@ -301,8 +312,10 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
   if (block_mass && tid < E) block_mass[(size_t)b * E + tid] = mass_s[tid];
 
   // restricted top-k: half a wave per row (rows 2w and 2w+1 on wave w); each
-  // lane keeps its 8 candidates (experts (lane&31) + 32*s) sorted by key,
-  // and every slot takes the best head of the half-wave
+  // lane sorts its 8 candidates (experts (lane&31) + 32*s) by key into LDS,
+  // and every slot takes the best head of the half-wave: the largest high
+  // word, then the largest low word among the lanes holding it.  The lane
+  // whose head was taken moves its pointer on.
   {
     const int half = lane >> 5, hl = lane & 31;
     const int r = 2 * wave + half;
@@ -315,51 +328,63 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
       key[s] = ok ? (static_cast<uint64_t>(logit_key(l_s[r][e])) << 32) | static_cast<uint32_t>(~e) : 0ull;
     }
     sort8_desc(key);
+    uint64_t* lst = reinterpret_cast<uint64_t*>(p_s);  // [slot][thread]
+#pragma unroll
+    for (int s = 1; s < 8; ++s) lst[s * kThreads + tid] = key[s];
+    uint64_t head = key[0];
+    int ptr = 0;
     int my_e = -1;  // lane hl keeps the expert of slot hl
     int k_eff = 0;
     for (int j = 0; j < K; ++j) {
-      uint64_t best = key[0];
-      best = max64(best, dpp64<kDppXor1>(best));
-      best = max64(best, dpp64<kDppXor2>(best));
-      best = max64(best, dpp64<kDppHalfMirror>(best));
-      best = max64(best, dpp64<kDppMirror>(best));
-      best = max64(best, swz_xor16(best));  // now the half-wave's best
-      if (best != 0ull) {
-        if (hl == j) my_e = static_cast<int>(~static_cast<uint32_t>(best));
-        if (key[0] == best) {  // this lane's head was taken: pop it
-#pragma unroll
-          for (int s = 0; s < 7; ++s) key[s] = key[s + 1];
-          key[7] = 0ull;
-        }
+      const uint32_t hh = static_cast<uint32_t>(head >> 32), hlo = static_cast<uint32_t>(head);
+      const uint32_t bh = half_max_u32(hh);
+      const uint32_t bl = half_max_u32(hh == bh ? hlo : 0u);
+      const bool found = (bh | bl) != 0u;
+      if (found) {
+        if (hl == j) my_e = static_cast<int>(~bl);
         k_eff = j + 1;
       }
-      if (__ballot(best != 0ull) == 0ull) break;  // both rows exhausted
+      const bool popped = found && hh == bh && hlo == bl;
+      ptr += popped ? 1 : 0;
+      const uint64_t nxt = lst[min(ptr, 7) * kThreads + tid];
+      head = popped ? (ptr < 8 ? nxt : 0ull) : head;
+      if (__ballot(found) == 0ull) break;  // both rows exhausted
     }
-    // gates: u of the chosen experts (recomputed: same operations, same bits),
-    // summed in slot order, then divided in parallel
-    const double u = my_e >= 0 ? exp_reduced(static_cast<double>(l_s[r][my_e]) - static_cast<double>(m_s[r])) : 0.0;
+    // gates: u of the chosen experts (recomputed: same operations, same
+    // bits); each lane sums its row's slots in order (empty slots add +0)
+    const double u = my_e >= 0
+                         ? exp_reduced(static_cast<double>(l_s[r][max(my_e, 0)]) - static_cast<double>(m_s[r]))
+                         : 0.0;
+    double* u_s = &zpart[0][0];  // [row][slot]
+    if (hl < 8) u_s[r * 8 + hl] = u;
+    __builtin_amdgcn_wave_barrier();
     double U = 0.0;
-    for (int j = 0; j < k_eff; ++j) U = U + __shfl(u, j, 32);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) U = U + u_s[r * 8 + j];
     if (row_ok && hl < K) {
       const int row = b * R + r;
       const bool ok = hl < k_eff;
-      topk[(size_t)row * K + hl] = ok ? my_e : -1;
+      const int e_out = ok ? my_e : -1;
+      topk[(size_t)row * K + hl] = e_out;
       gates[(size_t)row * K + hl] = ok ? static_cast<float>(u / U) : 0.0f;
+      tk_s[r * K + hl] = e_out;
+      if (ok) atomicOr(&mask1_s[my_e], 1u << r);
     }
   }
 
-  // the last block to finish builds the permutation for the whole call (a
-  // single-block call goes straight on: its own writes are all it reads)
-  if (plan.B > 1) {
-    __threadfence();
+  if (plan.B == 1) {
+    // a one-block call: its own routing is the whole call
     __syncthreads();
-    if (tid == 0) last_sh = atomicAdd(plan.sync, 1) == plan.B - 1;
-    __syncthreads();
-    if (!last_sh) return;
-    __threadfence();
-  } else {
-    __syncthreads();
+    permute_single(plan, perm_lds, mask1_s, tk_s);
+    return;
   }
+  // the last block to finish builds the permutation for the whole call
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) last_sh = atomicAdd(plan.sync, 1) == plan.B - 1;
+  __syncthreads();
+  if (!last_sh) return;
+  __threadfence();
   // the probability and logit buffers are dead now: masks and prefix reuse them
   if (plan.E * plan.mask_words <= kLdsMaskWords)
     permute_block<true>(plan, perm_lds, reinterpret_cast<uint32_t*>(p_s), reinterpret_cast<int32_t*>(l_s));
@@ -367,6 +392,8 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
     permute_block<false>(plan, perm_lds, nullptr, reinterpret_cast<int32_t*>(l_s));
 }
 
+static_assert(sizeof(double) * kMaxRows * kPStride >= sizeof(uint64_t) * 8 * kThreads,
+              "the sorted top-k candidate lists reuse the probability buffer");
 static_assert(sizeof(double) * kMaxRows * kPStride >= sizeof(uint32_t) * kLdsMaskWords,
               "the permutation's LDS masks reuse the probability buffer");
 static_assert(sizeof(float) * kMaxRows * kMaxExperts >= sizeof(int32_t) * kPrefixWords,

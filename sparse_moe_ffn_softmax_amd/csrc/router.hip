@@ -12,8 +12,11 @@
 // Parallel layout: a workgroup of 256 threads owns a tile of RT rows x ET
 // experts; thread group c (32 threads) runs chunk c for every output of the
 // tile, each thread keeping TR x TE independent accumulators.  Operands are
-// staged through LDS in slices of KB positions per chunk, double-buffered:
-// the global loads of slice s+1 are in flight while slice s is consumed.  The
+// staged through LDS in slices of KB positions per chunk.  With NBUF = 2 the
+// slices are double-buffered (the global loads of slice s+1 are in flight
+// while slice s is consumed); with NBUF = 1 one slice covers the whole chunk,
+// so every load of the workgroup is issued at once and the kernel waits on a
+// single memory round trip (the few-row case is latency-bound).  The
 // register tile only changes which thread runs a chain, never the order
 // inside a chain.
 #include "cmoe_device.h"
@@ -45,7 +48,7 @@ struct XVec<float> {  // 4 fp32 per 16-byte load
   }
 };
 
-template <int TR, int TE, int KB, typename XT>
+template <int TR, int TE, int KB, int NBUF, typename XT>
 __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict__ x,
                                                             const float* __restrict__ w,
                                                             const float* __restrict__ bias,
@@ -59,8 +62,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
   constexpr int WV = ET * 8 * KB / 4;        // w vectors per slice
   constexpr int XPT = (XV + 255) / 256;      // per thread
   constexpr int WPT = (WV + 255) / 256;
-  __shared__ float xs[2][8][RT][KP];
-  __shared__ float ws[2][8][ET][KP];
+  __shared__ float xs[NBUF][8][RT][KP];
+  __shared__ float ws[NBUF][8][ET][KP];
   // the chunk partial sums reuse the x staging buffer once the k loop is done
   static_assert(sizeof(float) * 8 * RT * (ET + 1) <= sizeof(xs), "partials must fit in xs");
   auto part = reinterpret_cast<float(*)[RT][ET + 1]>(&xs[0][0][0][0]);
@@ -75,7 +78,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
   const int row0 = blockIdx.x * RT;
   const int e0 = blockIdx.y * ET;
   const int L = H / 8;     // chunk length, a multiple of KB
-  const int S = L / KB;    // slices
+  const int S = L / KB;    // slices (1 when NBUF == 1)
 
   u32x4 xr[XPT], wr[WPT];
   auto fetch = [&](int s) {
@@ -136,8 +139,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
   stash(0);
   __syncthreads();
   for (int s = 0; s < S; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < S) fetch(s + 1);
+    const int buf = NBUF == 1 ? 0 : (s & 1);
+    if (NBUF > 1 && s + 1 < S) fetch(s + 1);
 #pragma unroll 4
     for (int k = 0; k < KB; k += 4) {
       f32x4 xv[TR], wv[TE];
@@ -152,7 +155,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
 #pragma unroll
           for (int j = 0; j < TE; ++j) acc[i][j] = __builtin_fmaf(xv[i][kk], wv[j][kk], acc[i][j]);
     }
-    if (s + 1 < S) stash(buf ^ 1);
+    if (NBUF > 1 && s + 1 < S) stash(buf ^ 1);
     __syncthreads();
   }
 
@@ -182,15 +185,15 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
   }
 }
 
-template <int TR, int TE, int KB>
+template <int TR, int TE, int KB, int NBUF = 2>
 static void launch_shape(const Plan& p, const void* x, const float* w, const float* b,
                          hipStream_t s) {
   dim3 grid((p.N + 8 * TR - 1) / (8 * TR), (p.E + 4 * TE - 1) / (4 * TE));
   if (p.act == CMOE_BF16)
-    router_logits_kernel<TR, TE, KB, uint16_t><<<grid, 256, 0, s>>>(
+    router_logits_kernel<TR, TE, KB, NBUF, uint16_t><<<grid, 256, 0, s>>>(
         static_cast<const uint16_t*>(x), w, b, p.logits, p.N, p.H, p.E, p.sync);
   else
-    router_logits_kernel<TR, TE, KB, float><<<grid, 256, 0, s>>>(
+    router_logits_kernel<TR, TE, KB, NBUF, float><<<grid, 256, 0, s>>>(
         static_cast<const float*>(x), w, b, p.logits, p.N, p.H, p.E, p.sync);
 }
 
@@ -200,8 +203,10 @@ hipError_t launch_router(const Plan& p, const void* x, const float* router_w,
   const int L = p.H / 8;
   if (p.N <= 256) {
     // few rows (one block per call): one accumulator per thread keeps
-    // enough workgroups in flight
-    if (L % 64 == 0) launch_shape<1, 1, 64>(p, x, router_w, router_b, s);
+    // enough workgroups in flight; whole chunks in one slice where they fit
+    if (L == 256) launch_shape<1, 1, 256, 1>(p, x, router_w, router_b, s);
+    else if (L == 128) launch_shape<1, 1, 128, 1>(p, x, router_w, router_b, s);
+    else if (L % 64 == 0) launch_shape<1, 1, 64>(p, x, router_w, router_b, s);
     else if (L % 32 == 0) launch_shape<1, 1, 32>(p, x, router_w, router_b, s);
     else launch_shape<1, 1, 16>(p, x, router_w, router_b, s);
   } else {

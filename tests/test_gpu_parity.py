@@ -45,6 +45,25 @@ def test_mid(wl):
     check(W.generate(wl))
 
 
+# few rows per expert (one 16-row MFMA tile each): the register-operand
+# grouped GEMMs, across weight formats, block heights and shared widths
+FEW = MID.with_(name="few_E256", num_experts=256, seed=61)
+
+
+@pytest.mark.parametrize("wl", [
+    FEW,
+    FEW.with_(name="few_fp8", weight_dtype=W.FP8, seed=62),
+    FEW.with_(name="few_f32", act_dtype=W.F32, weight_dtype=W.F32, seed=63),
+    FEW.with_(name="few_noshared", shared_inter=0, seed=64),
+    FEW.with_(name="few_Is_eq_I", shared_inter=256, seed=65),
+    FEW.with_(name="few_rows8", block_rows=8, num_blocks=5, seed=66),
+    FEW.with_(name="few_E20_k3", num_experts=20, top_k=3, num_blocks=1, seed=67),
+    FEW.with_(name="few_one_row_block", block_rows=8, num_blocks=1, seed=68),
+], ids=lambda w: w.name)
+def test_few_rows_per_expert(wl):
+    check(W.generate(wl))
+
+
 @pytest.mark.parametrize("tau,k", [(1.0, 8), (0.95, 8), (0.5, 8), (0.9, 4), (0.3, 1)])
 def test_mid_threshold_and_topk(tau, k):
     check(W.generate(MID.with_(bias_sigma=0.5, seed=31)), tau=tau, top_k=k)
