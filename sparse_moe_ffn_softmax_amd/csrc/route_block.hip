@@ -32,7 +32,9 @@
 // short serial chains.  Top-k candidates are 64-bit keys (order-preserving
 // logit bits, complemented id): each half-wave owns a row, keeps 8 sorted
 // candidates per lane and takes the best head per slot with DPP exchanges
-// inside 16-lane rows and one swizzle across them.
+// inside 16-lane rows and one lane swap across them.  The block's experts
+// are ordered by (mass desc, id asc) with four 64-wide bitonic sorts in
+// registers and a binary-search merge of the four sorted runs.
 //
 // The workgroup that finishes last (device-scope counter, zeroed by the
 // router kernel earlier on the stream) goes on to build the row -> expert
@@ -91,19 +93,18 @@ __device__ __forceinline__ uint32_t dpp(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
 }
 
-// exchange with lane ^ 16 inside each 32-lane half (ds_swizzle bitmask mode)
-__device__ __forceinline__ uint32_t swz_xor16(uint32_t v) {
-  constexpr int kPattern = 0x1F | (0x10 << 10);  // and 0x1F, or 0, xor 0x10
-  return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), kPattern));
-}
-
-// maximum over each 32-lane half of the wave, in every lane of that half
+// maximum over each 32-lane half of the wave, in every lane of that half:
+// DPP inside each row of 16 lanes, then v_permlane16_swap, which hands each
+// lane the value of its partner in the other row of the half (checked on
+// gfx950: with both operands v, result 0 holds rows (0,0,2,2) and result 1
+// rows (1,1,3,3) of v)
 __device__ __forceinline__ uint32_t half_max_u32(uint32_t v) {
   v = max(v, dpp<kDppXor1>(v));
   v = max(v, dpp<kDppXor2>(v));
   v = max(v, dpp<kDppHalfMirror>(v));
   v = max(v, dpp<kDppMirror>(v));
-  return max(v, swz_xor16(v));
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return max(static_cast<uint32_t>(r[0]), static_cast<uint32_t>(r[1]));
 }
 
 __device__ __forceinline__ float wave_max_f32(float v) {
@@ -141,6 +142,75 @@ __device__ __forceinline__ uint32_t logit_key(float l) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// ---------------------------------------------------------------------------
+// (mass desc, id asc): the order the coreset and the mass prefix sum use.
+// Masses are sums of non-negative probabilities from +0, so their fp64 bit
+// patterns order as unsigned integers; with the complemented id below them,
+// "a comes first" is one unsigned compare of 96-bit keys.
+// ---------------------------------------------------------------------------
+struct MassKey {
+  uint64_t m;    // bits of the block mass
+  uint32_t nid;  // ~expert id
+};
+
+__device__ __forceinline__ bool beats(const MassKey& a, const MassKey& b) {
+  // b - a over the three words; the final borrow is set iff b < a
+  unsigned c0, c1, c2;
+  (void)__builtin_subc(b.nid, a.nid, 0u, &c0);
+  (void)__builtin_subc(static_cast<unsigned>(b.m), static_cast<unsigned>(a.m), c0, &c1);
+  (void)__builtin_subc(static_cast<unsigned>(b.m >> 32), static_cast<unsigned>(a.m >> 32), c1, &c2);
+  return c2 != 0u;
+}
+
+// value of lane ^ J (J a power of two below 64), all lanes active
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v, int lane) {
+  if constexpr (J == 1) {
+    return dpp<kDppXor1>(v);
+  } else if constexpr (J == 2) {
+    return dpp<kDppXor2>(v);
+  } else if constexpr (J == 4) {
+    return dpp<kDppHalfMirror>(dpp<0x1B>(v));  // (i ^ 3) then (i ^ 7) inside 8
+  } else if constexpr (J == 8) {
+    return dpp<0x128>(v);  // rotate by 8 inside 16 = i ^ 8
+  } else if constexpr (J == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane & 16) ? static_cast<uint32_t>(r[0]) : static_cast<uint32_t>(r[1]);
+  } else {
+    return static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), J, 64));
+  }
+}
+
+// one compare-exchange step of a bitonic sort over the 64 lanes: blocks of
+// K lanes, partners J apart; the final order (K = 64) is descending
+template <int K, int J>
+__device__ __forceinline__ void bitonic_step(MassKey& k, int lane) {
+  MassKey p;
+  const uint32_t plo = xor_lane<J>(static_cast<uint32_t>(k.m), lane);
+  const uint32_t phi = xor_lane<J>(static_cast<uint32_t>(k.m >> 32), lane);
+  p.m = (static_cast<uint64_t>(phi) << 32) | plo;
+  p.nid = xor_lane<J>(k.nid, lane);
+  const bool keep_greater = ((lane & J) == 0) == ((lane & K) == 0);
+  if (keep_greater == beats(p, k)) k = p;
+}
+
+template <int K, int J>
+__device__ __forceinline__ void bitonic_merge(MassKey& k, int lane) {
+  if constexpr (J > 0) {
+    bitonic_step<K, J>(k, lane);
+    bitonic_merge<K, J / 2>(k, lane);
+  }
+}
+
+// sorts the wave's 64 keys, one per lane, so that lane i holds the i-th
+template <int K = 2>
+__device__ __forceinline__ void wave_sort64(MassKey& k, int lane) {
+  if constexpr (K <= 64) {
+    bitonic_merge<K, K / 2>(k, lane);
+    wave_sort64<K * 2>(k, lane);
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float tau) {
   const int R = plan.R, E = plan.E, K = plan.K;
   int32_t* __restrict__ topk = plan.topk;
@@ -162,6 +232,8 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
   __shared__ int order_s[kMaxExperts];
   __shared__ int rank_s[kMaxExperts];
   __shared__ int rcnt[4][kMaxExperts];
+  __shared__ MassKey run_s[4][64];   // four sorted runs of 64 experts
+  __shared__ int runpos_s[kMaxExperts];  // an expert's place in its own run
   __shared__ uint32_t mask1_s[kMaxExperts];  // one-block calls: rows per expert
   __shared__ int tk_s[kMaxRows * 8];          // this block's top-k
   __shared__ int m_sh;
@@ -250,27 +322,48 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
   }
   __syncthreads();
 
-  // rank under (mass desc, id asc): four threads per expert count a quarter each
+  // rank under (mass desc, id asc).  Waves 0..3 each sort 64 experts in
+  // registers (experts past E carry mass +0 and the largest ids, so they sort
+  // after every real expert); then thread
+  // (expert e, run q) counts the experts of run q that beat e: e's place in
+  // its own run, or a binary search (the beating experts are a prefix of a
+  // sorted run).  The rank is the sum over the four runs.
+  if (wave < 4) {
+    const int e = 64 * wave + lane;
+    MassKey k;
+    k.m = e < E ? static_cast<uint64_t>(__double_as_longlong(mass_s[e])) : 0ull;
+    k.nid = ~static_cast<uint32_t>(e);
+    wave_sort64(k, lane);
+    run_s[wave][lane] = k;
+    runpos_s[~k.nid & 255] = lane;
+  }
+  __syncthreads();
   {
-    const int e = tid & 255, part = tid >> 8;
+    const int e = tid & 255, q = tid >> 8;
     if (e < E) {
-      const double me = mass_s[e];
-      int cnt = 0;
-      const int lo = part * 64, hi = min(E, lo + 64);
-#pragma unroll 8
-      for (int o = lo; o < hi; ++o) {
-        const double mo = mass_s[o];
-        cnt += (mo > me) | ((mo == me) & (o < e));
+      int cnt;
+      if (q == (e >> 6)) {
+        cnt = runpos_s[e];
+      } else {
+        MassKey me;
+        me.m = static_cast<uint64_t>(__double_as_longlong(mass_s[e]));
+        me.nid = ~static_cast<uint32_t>(e);
+        cnt = 0;
+#pragma unroll
+        for (int step = 32; step > 0; step >>= 1)
+          if (beats(run_s[q][cnt + step - 1], me)) cnt += step;
+        // the steps reach index 62 at most: all 64 beating e ends at 63
+        if (cnt == 63 && beats(run_s[q][63], me)) cnt = 64;
       }
-      rcnt[part][e] = cnt;
+      rcnt[q][e] = cnt;
     }
   }
   __syncthreads();
   if (tid < E) {
     const int rank = rcnt[0][tid] + rcnt[1][tid] + rcnt[2][tid] + rcnt[3][tid];
     rank_s[tid] = rank;
-    order_s[rank] = tid;
-    smass_s[rank] = mass_s[tid];
+    order_s[min(rank, kMaxExperts - 1)] = tid;
+    smass_s[min(rank, kMaxExperts - 1)] = mass_s[tid];
   }
   __syncthreads();
 
