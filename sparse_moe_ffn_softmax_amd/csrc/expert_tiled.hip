@@ -48,7 +48,8 @@ struct TiledArgs {
 // One workgroup's GEMM: acc[mt] (16 x 16 each) for this wave's 16 columns,
 // over k in [0, Kdim).  asrc[i]: source row pointer (stage 0) of the i-th
 // activation vector this thread stages, or nullptr for rows past the tile;
-// brow: this lane's weight row at its k offset; bsc: its fp8 block scales.
+// brow: this lane's weight row at its first k (blane); bsc: its fp8 block
+// scales.
 template <WFmt F, int MT>
 struct TiledGemm {
   using Fr = Frag<F>;
@@ -62,6 +63,17 @@ struct TiledGemm {
   static constexpr int AV = T / RPP;                // vectors per thread per stage
   static constexpr int PAD = 16 / (int)sizeof(AT);
   using Lds = AT[2][T][KS + PAD];
+  // k order inside a stage.  MFMA only needs A and B to agree on it, so fp8
+  // pairs steps: lane group kg takes k [16kg, 16kg+16) of each 64-deep step
+  // pair, and its weights arrive as one 16-byte load per two steps (8 fp8
+  // codes per step) instead of two 8-byte ones.
+  static constexpr bool kPair = (F == WFmt::FP8);
+  static_assert(!kPair || U % 2 == 0, "paired fp8 steps");
+  static __device__ __forceinline__ int koff(int u, int kg) {
+    return kPair ? 64 * (u / 2) + 16 * kg + 8 * (u % 2) : u * Fr::kStep + kg * Fr::kLane;
+  }
+  // this lane's first weight byte of a stage, relative to its weight row
+  static __device__ __forceinline__ int blane(int kg) { return kPair ? 16 * kg : kg * Fr::kLane; }
 
   static __device__ __forceinline__ void run(Lds& As, const AT* const (&asrc)[AV],
                                              const WT* brow, const float* bsc, int Kdim,
@@ -85,8 +97,17 @@ struct TiledGemm {
         *reinterpret_cast<u32x4*>(&As[buf][r0 + i * RPP][seg * (16 / (int)sizeof(AT))]) = areg[i];
     };
     auto load_b = [&](typename Fr::B (&b)[U], int k0) {
+      if constexpr (kPair) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) b[u] = Fr::load_b(brow + k0 + u * Fr::kStep);
+        for (int j = 0; j < U / 2; ++j) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(brow + k0 + 64 * j);
+          b[2 * j] = typename Fr::B{v[0], v[1]};
+          b[2 * j + 1] = typename Fr::B{v[2], v[3]};
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) b[u] = Fr::load_b(brow + k0 + u * Fr::kStep);
+      }
     };
     auto compute = [&](typename Fr::B (&b)[U], int buf, int k0) {
       if constexpr (F == WFmt::FP8) {
@@ -98,7 +119,7 @@ struct TiledGemm {
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
             if (mt < mt_act) {
-              const typename Fr::A av = Fr::load_a(&As[buf][mt * 16 + col][u * Fr::kStep + kg * Fr::kLane]);
+              const typename Fr::A av = Fr::load_a(&As[buf][mt * 16 + col][koff(u, kg)]);
               tmp[mt] = Fr::mma(av, b[u], tmp[mt]);
             }
         const float sc = bsc[k0 / 128];
@@ -112,7 +133,7 @@ struct TiledGemm {
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
             if (mt < mt_act) {
-              const typename Fr::A av = Fr::load_a(&As[buf][mt * 16 + col][u * Fr::kStep + kg * Fr::kLane]);
+              const typename Fr::A av = Fr::load_a(&As[buf][mt * 16 + col][koff(u, kg)]);
               acc[mt] = Fr::mma(av, b[u], acc[mt]);
             }
           // keep the scheduler from hoisting every k step's operands at once
@@ -178,7 +199,7 @@ __global__ __launch_bounds__(kTiledThreads) void expert_up_tiled_kernel(TiledArg
   if constexpr (F == WFmt::FP8) S = shared ? a.sws : a.ws + (size_t)t.expert * (2 * a.I / 128) * (H / 128);
   const int i0 = slice * kTiledUpCols + wave * 8;
   const int wr = col < 8 ? i0 + col : inter + i0 + col - 8;  // gate row / up row
-  const WT* brow = W + (size_t)wr * H + kg * Fr::kLane;
+  const WT* brow = W + (size_t)wr * H + G::blane(kg);
   const float* bsc = (F == WFmt::FP8) ? S + (size_t)(wr / 128) * (H / 128) : nullptr;
   const int mt_act = (t.rows + 15) >> 4;
   f32x4 acc[MT];
@@ -226,7 +247,7 @@ __global__ __launch_bounds__(kTiledThreads) void expert_down_tiled_kernel(TiledA
   if constexpr (F == WFmt::FP8) S = shared ? a.sws : a.ws + (size_t)t.expert * (H / 128) * (a.I / 128);
   const int c0 = slice * kTiledDownCols + wave * 16;
   const int orow = c0 + col;  // W2 row = output column
-  const WT* brow = W + (size_t)orow * inter + kg * Fr::kLane;
+  const WT* brow = W + (size_t)orow * inter + G::blane(kg);
   const float* bsc = (F == WFmt::FP8) ? S + (size_t)(orow / 128) * (inter / 128) : nullptr;
   const int mt_act = (t.rows + 15) >> 4;
   f32x4 acc[MT];
