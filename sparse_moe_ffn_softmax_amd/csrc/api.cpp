@@ -95,10 +95,15 @@ Layout layout(const cmoe_problem& p, int K) {
   Layout L;
   L.mask_words = (int)((N + 31) / 32);
   // work-tile height: about 1.5x the mean rows per expert, in 16-row MFMA
-  // tiles (1, 2, 4 or 8); experts with more rows get several tiles
+  // tiles (1, 2, 4, 6 or 8); experts with more rows get several tiles
   const size_t want = (NK * 3 / 2 + E - 1) / E;
-  L.mt_max = 1;
-  while (L.mt_max < 8 && (size_t)16 * L.mt_max < want) L.mt_max *= 2;
+  static const int kTileChoices[] = {1, 2, 4, 6, 8};
+  L.mt_max = 8;
+  for (int mt : kTileChoices)
+    if ((size_t)16 * mt >= want) {
+      L.mt_max = mt;
+      break;
+    }
   const size_t T = 16 * (size_t)L.mt_max;
   L.max_tiles = (int)(NK / T + (E < NK ? E : NK) + (N + T - 1) / T + 1);
   const size_t hsz = p.act_dtype == CMOE_F32 ? 4 : 2;

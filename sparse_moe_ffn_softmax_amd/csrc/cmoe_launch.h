@@ -10,7 +10,7 @@
 
 namespace cmoe {
 
-// Rows of one grouped-GEMM work tile: 16 * mt_max, mt_max in {1, 2, 4, 8} MFMA
+// Rows of one grouped-GEMM work tile: 16 * mt_max, mt_max in {1, 2, 4, 6, 8} MFMA
 // row tiles, chosen per call from the expected rows per expert (see carve()).
 constexpr int kMaxTileRows = 128;
 // h columns produced by one expert_up workgroup (one 16-column MFMA tile of 8
@@ -35,7 +35,7 @@ struct Plan {
   int N, H, E, I, Is, R, B, K;
   int act, wt;           // cmoe_dtype codes
   int max_tiles;         // grid bound for the grouped GEMMs
-  int mt_max;            // MFMA row tiles per work tile: 1, 2, 4 or 8
+  int mt_max;            // MFMA row tiles per work tile: 1, 2, 4, 6 or 8
   int tile_rows;         // 16 * mt_max
   int mask_words;        // ceil(N / 32)
   float* logits;         // [N,E]

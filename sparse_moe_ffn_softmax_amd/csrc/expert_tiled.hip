@@ -276,6 +276,7 @@ static void launch_tiled_mt(const TiledArgs& a, int mt_max, unsigned grid, hipSt
   switch (mt_max) {
     case 2: launch_tiled<kUp, F, 2>(a, grid, s); break;
     case 4: launch_tiled<kUp, F, 4>(a, grid, s); break;
+    case 6: launch_tiled<kUp, F, 6>(a, grid, s); break;
     default: launch_tiled<kUp, F, 8>(a, grid, s); break;
   }
 }
