@@ -84,16 +84,15 @@ cmoe_status check_problem(const cmoe_problem* p, int32_t top_k) {
 }
 
 struct Layout {
-  size_t logits, topk, gates, counts, offsets, pair_row, pair_pos, rowmask, tiles,
-      tile_count, sync, h, y, total;
-  int max_tiles, mask_words, mt_max;
+  size_t logits, topk, gates, counts, offsets, pair_row, pair_pos, blockmask, blockpre, tiles,
+      tile_count, h, y, total;
+  int max_tiles, mt_max;
 };
 
 Layout layout(const cmoe_problem& p, int K) {
   const size_t N = (size_t)p.block_rows * p.num_blocks, E = p.num_experts, H = p.hidden;
   const size_t NK = N * K;
   Layout L;
-  L.mask_words = (int)((N + 31) / 32);
   // work-tile height: about 1.5x the mean rows per expert, in 16-row MFMA
   // tiles (1, 2, 4, 6 or 8); experts with more rows get several tiles
   const size_t want = (NK * 3 / 2 + E - 1) / E;
@@ -120,10 +119,11 @@ Layout layout(const cmoe_problem& p, int K) {
   L.offsets = take((E + 1) * 4);
   L.pair_row = take(NK * 4);
   L.pair_pos = take(NK * 4);
-  L.rowmask = take(E * L.mask_words * 4);
+  const size_t B = p.num_blocks;
+  L.blockmask = take(B * E * 4);
+  L.blockpre = take(B * E * 4);
   L.tiles = take((size_t)L.max_tiles * sizeof(cmoe::Tile));
   L.tile_count = take(4);
-  L.sync = take(16 * 4);
   L.h = take((NK * p.inter + N * p.shared_inter) * hsz);
   L.y = take((NK + N) * H * 4);
   L.total = off;
@@ -152,7 +152,6 @@ void carve(Plan& p, const cmoe_problem& pr, int K, void* ws, const cmoe_routing*
   p.max_tiles = L.max_tiles;
   p.mt_max = L.mt_max;
   p.tile_rows = 16 * L.mt_max;
-  p.mask_words = L.mask_words;
   p.logits = (rt && rt->logits) ? rt->logits : reinterpret_cast<float*>(base + L.logits);
   p.topk = (rt && rt->topk_idx) ? rt->topk_idx : reinterpret_cast<int32_t*>(base + L.topk);
   p.gates = (rt && rt->gates) ? rt->gates : reinterpret_cast<float*>(base + L.gates);
@@ -160,10 +159,10 @@ void carve(Plan& p, const cmoe_problem& pr, int K, void* ws, const cmoe_routing*
   p.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
   p.pair_row = reinterpret_cast<int32_t*>(base + L.pair_row);
   p.pair_pos = reinterpret_cast<int32_t*>(base + L.pair_pos);
-  p.rowmask = reinterpret_cast<uint32_t*>(base + L.rowmask);
+  p.blockmask = reinterpret_cast<uint32_t*>(base + L.blockmask);
+  p.blockpre = reinterpret_cast<int32_t*>(base + L.blockpre);
   p.tiles = reinterpret_cast<Tile*>(base + L.tiles);
   p.tile_count = reinterpret_cast<int32_t*>(base + L.tile_count);
-  p.sync = reinterpret_cast<int32_t*>(base + L.sync);
   p.h = base + L.h;
   p.y = reinterpret_cast<float*>(base + L.y);
   p.coreset_ids = rt ? rt->coreset_ids : nullptr;
@@ -274,7 +273,10 @@ static cmoe_status forward_impl(const cmoe_problem* problem, const cmoe_weights*
     }
     switch (stage) {
       case 0: e = cmoe::launch_router(plan, x, w->router_w, w->router_b, st); break;
-      case 1: e = cmoe::launch_route_blocks(plan, mass_threshold, st); break;
+      case 1:
+        e = cmoe::launch_route_blocks(plan, mass_threshold, st);
+        if (e == hipSuccess && plan.B > 1) e = cmoe::launch_permute_blocks(plan, st);
+        break;
       case 2:
         e = plan.mt_max == 1 ? cmoe::launch_expert_up(plan, *w, x, st)
                              : cmoe::launch_expert_tiled(plan, *w, x, true, st);

@@ -37,7 +37,6 @@ struct Plan {
   int max_tiles;         // grid bound for the grouped GEMMs
   int mt_max;            // MFMA row tiles per work tile: 1, 2, 4, 6 or 8
   int tile_rows;         // 16 * mt_max
-  int mask_words;        // ceil(N / 32)
   float* logits;         // [N,E]
   int32_t* topk;         // [N,K]
   float* gates;          // [N,K]
@@ -45,10 +44,10 @@ struct Plan {
   int32_t* offsets;      // [E+1]
   int32_t* pair_row;     // [N*K]  source row of each routed pair, expert-major
   int32_t* pair_pos;     // [N*K]  pair position of (row, slot), -1 if unused
-  uint32_t* rowmask;     // [E, mask_words] bit r set if row r routes to expert e
+  uint32_t* blockmask;   // [B, E] bit r set iff row r of block b routes to expert e
+  int32_t* blockpre;     // [B, E] pairs of expert e in the blocks before b
   Tile* tiles;           // [max_tiles]
   int32_t* tile_count;   // [1]
-  int32_t* sync;         // [16] call-local counters, zeroed by the router kernel
   void* h;               // routed [N*K, I] then shared [N, Is]; act_dtype elements
   float* y;              // [N*K + N][H] fp32: routed pairs, then shared rows
   // optional caller outputs
@@ -67,8 +66,10 @@ void carve(Plan& p, const cmoe_problem& pr, int top_k, void* ws, const cmoe_rout
 
 hipError_t launch_router(const Plan& p, const void* x, const float* router_w,
                          const float* router_b, hipStream_t s);
-// per-block routing; the last block also builds the permutation and work list
+// per-block routing; a one-block call also builds the permutation and the
+// work list in the same kernel, a many-block call with launch_permute_blocks
 hipError_t launch_route_blocks(const Plan& p, float tau, hipStream_t s);
+hipError_t launch_permute_blocks(const Plan& p, hipStream_t s);
 // mt_max == 1: register-operand kernels (expert_gemm.hip)
 hipError_t launch_expert_up(const Plan& p, const cmoe_weights& w, const void* x, hipStream_t s);
 hipError_t launch_expert_down(const Plan& p, const cmoe_weights& w, hipStream_t s);

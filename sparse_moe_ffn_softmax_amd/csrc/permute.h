@@ -17,9 +17,9 @@
 //  * permute_single: the call is one block of at most 32 rows, whose routing
 //    workgroup still holds the top-k result and one mask word per expert in
 //    LDS; two barriers and no global round trips.
-//  * permute_block: many blocks; the workgroup that finishes its routing
-//    last reads every block's top-k back and builds the masks in LDS (N <=
-//    2048 rows at E = 256) or in the workspace.
+//  * many blocks (permute_blocks.hip): every routing workgroup publishes one
+//    mask word per expert; a scan kernel turns them into per-block prefixes
+//    and counts, and one workgroup per block places its own rows.
 #pragma once
 #include "cmoe_device.h"
 #include "cmoe_launch.h"
@@ -47,10 +47,11 @@ struct PermuteLds {
 };
 
 // Run by one whole wave (lanes 0..63): expert e = 4*lane + i has L.cnt[e]
-// pairs.  Writes the exclusive offsets (LDS and the call's buffers) and the
-// work list: ceil(count / T) tiles per expert, experts ascending, then the
-// shared expert's tiles over the N rows in order.
-__device__ __forceinline__ void offsets_and_tiles(const Plan& p, PermuteLds& L) {
+// pairs.  Writes the exclusive offsets to LDS and, with publish, to the
+// call's buffers together with the work list: ceil(count / T) tiles per
+// expert, experts ascending, then the shared expert's tiles over the N rows
+// in order.
+__device__ __forceinline__ void offsets_and_tiles(const Plan& p, PermuteLds& L, bool publish) {
   const int lane = threadIdx.x & 63;
   const int E = p.E, T = p.tile_rows;
   int c[4], nt[4], csum = 0, tsum = 0;
@@ -70,6 +71,8 @@ __device__ __forceinline__ void offsets_and_tiles(const Plan& p, PermuteLds& L) 
     const int e = 4 * lane + i;
     if (e < E) {
       L.off[e] = coff;
+    }
+    if (e < E && publish) {
       p.counts[e] = c[i];
       p.offsets[e] = coff;
       if (p.out_counts) p.out_counts[e] = c[i];
@@ -86,8 +89,9 @@ __device__ __forceinline__ void offsets_and_tiles(const Plan& p, PermuteLds& L) 
     coff += c[i];
     toff += nt[i];
   }
+  if (lane == 0) L.off[E] = ctot;
+  if (!publish) return;
   if (lane == 0) {
-    L.off[E] = ctot;
     p.offsets[E] = ctot;
     if (p.out_offsets) p.out_offsets[E] = ctot;
   }
@@ -106,7 +110,7 @@ __device__ __forceinline__ void offsets_and_tiles(const Plan& p, PermuteLds& L) 
 // One block of N <= 32 rows: tk_s[N*K] holds the block's top-k (-1 for an
 // empty slot) and mask_s[e] bit r is set iff row r routes to expert e.
 // Called by all 1024 threads after a barrier that follows those writes.
-__device__ void permute_single(const Plan& p, PermuteLds& L, const uint32_t* mask_s,
+__device__ inline void permute_single(const Plan& p, PermuteLds& L, const uint32_t* mask_s,
                                const int* tk_s) {
   const int tid = threadIdx.x;
   const int NK = p.N * p.K;
@@ -116,7 +120,7 @@ __device__ void permute_single(const Plan& p, PermuteLds& L, const uint32_t* mas
       const int e = 4 * tid + i;
       if (e < p.E) L.cnt[e] = __popc(mask_s[e]);
     }
-    offsets_and_tiles(p, L);
+    offsets_and_tiles(p, L, true);
   }
   __syncthreads();
   if (tid < NK) {
@@ -132,86 +136,6 @@ __device__ void permute_single(const Plan& p, PermuteLds& L, const uint32_t* mas
   }
   if (p.out_perm)
     for (int i = L.off[p.E] + tid; i < NK; i += 1024) p.out_perm[i] = -1;
-}
-
-// Row masks of E x W words (W = ceil(N/32)): in LDS when they fit (N <= 2048
-// rows at E = 256), else in the workspace.  A coarse per-expert popcount
-// prefix over groups of G mask words always lives in LDS; a pair's rank adds
-// the popcounts of at most G-1 words of its group.
-constexpr int kLdsMaskWords = 16384;
-constexpr int kPrefixWords = 8192;
-
-// The whole permutation for many blocks, run by one workgroup of 1024
-// threads.  mask_lds: kLdsMaskWords words (used when kLdsMask); pref_lds:
-// kPrefixWords words.
-template <bool kLdsMask>
-__device__ void permute_block(const Plan& p, PermuteLds& L, uint32_t* mask_lds, int32_t* pref_lds) {
-  const int tid = threadIdx.x;
-  const int N = p.N, K = p.K, E = p.E, W = p.mask_words;
-  const int NK = N * K;
-  uint32_t* masks = kLdsMask ? mask_lds : p.rowmask;
-  auto mask_load = [&](size_t i) -> uint32_t {
-    if constexpr (kLdsMask) return mask_lds[i];
-    else return __hip_atomic_load(p.rowmask + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  };
-
-  for (int i = tid; i < E * W; i += 1024) {
-    if constexpr (kLdsMask) mask_lds[i] = 0u;
-    else __hip_atomic_store(p.rowmask + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-
-  for (int i = tid; i < NK; i += 1024) {
-    const int e = p.topk[i];
-    if (e >= 0) {
-      const int r = i / K;
-      atomicOr(masks + (size_t)e * W + (r >> 5), 1u << (r & 31));
-    }
-  }
-  __syncthreads();
-
-  // coarse popcount prefix per expert over groups of G words; the last
-  // running total is the expert's count
-  int G = 1;
-  while (E * ((W + G - 1) / G) > kPrefixWords) G <<= 1;
-  const int J = (W + G - 1) / G;
-  for (int i = tid; i < E * J; i += 1024) {
-    const int e = i / J, j = i % J;
-    int c = 0;
-    for (int w = j * G; w < min(W, j * G + G); ++w) c += __popc(mask_load((size_t)e * W + w));
-    pref_lds[i] = c;
-  }
-  __syncthreads();
-  for (int e = tid; e < E; e += 1024) {
-    int run = 0;
-    for (int j = 0; j < J; ++j) {
-      const int c = pref_lds[e * J + j];
-      pref_lds[e * J + j] = run;
-      run += c;
-    }
-    L.cnt[e] = run;
-  }
-  __syncthreads();
-  if (tid < 64) offsets_and_tiles(p, L);
-  __syncthreads();
-
-  // positions
-  for (int i = tid; i < NK; i += 1024) {
-    const int e = p.topk[i];
-    int pos = -1;
-    if (e >= 0) {
-      const int r = i / K, w = r >> 5, j = w / G;
-      int rank = pref_lds[e * J + j];
-      for (int w2 = j * G; w2 < w; ++w2) rank += __popc(mask_load((size_t)e * W + w2));
-      rank += __popc(mask_load((size_t)e * W + w) & ((1u << (r & 31)) - 1u));
-      pos = L.off[e] + rank;
-      p.pair_row[pos] = r;
-      if (p.out_perm) p.out_perm[pos] = i;
-    }
-    p.pair_pos[i] = pos;
-  }
-  if (p.out_perm)
-    for (int i = L.off[E] + tid; i < NK; i += 1024) p.out_perm[i] = -1;
 }
 
 }  // namespace cmoe

@@ -36,10 +36,10 @@
 // are ordered by (mass desc, id asc) with four 64-wide bitonic sorts in
 // registers and a binary-search merge of the four sorted runs.
 //
-// The workgroup that finishes last (device-scope counter, zeroed by the
-// router kernel earlier on the stream) goes on to build the row -> expert
-// permutation and the GEMM work list for the whole call (permute.h), so the
-// call needs no separate launch for it.
+// A one-block call goes on to build the row -> expert permutation and the
+// GEMM work list in the same kernel (permute.h); with many blocks every block
+// publishes its rows per expert as one mask word each, and two small kernels
+// queued next build the permutation (permute_blocks.hip).
 #include "cmoe_device.h"
 #include "cmoe_launch.h"
 #include "permute.h"
@@ -237,7 +237,6 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
   __shared__ uint32_t mask1_s[kMaxExperts];  // one-block calls: rows per expert
   __shared__ int tk_s[kMaxRows * 8];          // this block's top-k
   __shared__ int m_sh;
-  __shared__ int last_sh;
   __shared__ PermuteLds perm_lds;
 
   const int tid = threadIdx.x;
@@ -465,32 +464,19 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
     }
   }
 
+  __syncthreads();
   if (plan.B == 1) {
     // a one-block call: its own routing is the whole call
-    __syncthreads();
     permute_single(plan, perm_lds, mask1_s, tk_s);
     return;
   }
-  // the last block to finish builds the permutation for the whole call
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) last_sh = atomicAdd(plan.sync, 1) == plan.B - 1;
-  __syncthreads();
-  if (!last_sh) return;
-  __threadfence();
-  // the probability and logit buffers are dead now: masks and prefix reuse them
-  if (plan.E * plan.mask_words <= kLdsMaskWords)
-    permute_block<true>(plan, perm_lds, reinterpret_cast<uint32_t*>(p_s), reinterpret_cast<int32_t*>(l_s));
-  else
-    permute_block<false>(plan, perm_lds, nullptr, reinterpret_cast<int32_t*>(l_s));
+  // many blocks: publish this block's rows per expert; the permutation is
+  // built by the kernels queued next (permute_blocks.hip)
+  if (tid < E) plan.blockmask[(size_t)b * E + tid] = mask1_s[tid];
 }
 
 static_assert(sizeof(double) * kMaxRows * kPStride >= sizeof(uint64_t) * 8 * kThreads,
               "the sorted top-k candidate lists reuse the probability buffer");
-static_assert(sizeof(double) * kMaxRows * kPStride >= sizeof(uint32_t) * kLdsMaskWords,
-              "the permutation's LDS masks reuse the probability buffer");
-static_assert(sizeof(float) * kMaxRows * kMaxExperts >= sizeof(int32_t) * kPrefixWords,
-              "the permutation's popcount prefix reuses the logit buffer");
 
 hipError_t launch_route_blocks(const Plan& p, float tau, hipStream_t s) {
   route_block_kernel<<<p.B, kThreads, 0, s>>>(p, tau);

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
                                                             const float* __restrict__ w,
                                                             const float* __restrict__ bias,
                                                             float* __restrict__ logits, int N,
-                                                            int H, int E, int32_t* __restrict__ sync) {
+                                                            int H, int E) {
   constexpr int RT = 8 * TR;                 // rows per workgroup
   constexpr int ET = 4 * TE;                 // experts per workgroup
   constexpr int KP = KB + 4;                 // padded LDS row (breaks bank aliasing)
@@ -69,8 +69,6 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
   auto part = reinterpret_cast<float(*)[RT][ET + 1]>(&xs[0][0][0][0]);
 
   const int tid = threadIdx.x;
-  // zero the call-local counters used by the kernels queued after this one
-  if (blockIdx.x == 0 && blockIdx.y == 0 && tid < 16) sync[tid] = 0;
   const int c = tid >> 5;  // chunk run by this thread
   const int q = tid & 31;
   const int rq = q & 7;    // row group
@@ -191,10 +189,10 @@ static void launch_shape(const Plan& p, const void* x, const float* w, const flo
   dim3 grid((p.N + 8 * TR - 1) / (8 * TR), (p.E + 4 * TE - 1) / (4 * TE));
   if (p.act == CMOE_BF16)
     router_logits_kernel<TR, TE, KB, NBUF, uint16_t><<<grid, 256, 0, s>>>(
-        static_cast<const uint16_t*>(x), w, b, p.logits, p.N, p.H, p.E, p.sync);
+        static_cast<const uint16_t*>(x), w, b, p.logits, p.N, p.H, p.E);
   else
     router_logits_kernel<TR, TE, KB, NBUF, float><<<grid, 256, 0, s>>>(
-        static_cast<const float*>(x), w, b, p.logits, p.N, p.H, p.E, p.sync);
+        static_cast<const float*>(x), w, b, p.logits, p.N, p.H, p.E);
 }
 
 hipError_t launch_router(const Plan& p, const void* x, const float* router_w,
