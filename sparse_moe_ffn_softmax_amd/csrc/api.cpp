@@ -86,7 +86,7 @@ cmoe_status check_problem(const cmoe_problem* p, int32_t top_k) {
 struct Layout {
   size_t logits, topk, gates, counts, offsets, pair_row, pair_pos, blockmask, blockpre, tiles,
       tile_count, h, y, total;
-  int max_tiles, mt_max;
+  int max_tiles, mt_max, y_act;
 };
 
 Layout layout(const cmoe_problem& p, int K) {
@@ -125,7 +125,11 @@ Layout layout(const cmoe_problem& p, int K) {
   L.tiles = take((size_t)L.max_tiles * sizeof(cmoe::Tile));
   L.tile_count = take(4);
   L.h = take((NK * p.inter + N * p.shared_inter) * hsz);
-  L.y = take((NK + N) * H * 4);
+  // Per-pair down outputs: fp32 for small calls; with many rows per expert
+  // (mt_max > 1) the buffer is large (about 150 MB at 2048 rows) and is
+  // stored in the activation dtype, halving its write and read traffic.
+  L.y_act = L.mt_max > 1 && p.act_dtype == CMOE_BF16;
+  L.y = take((NK + N) * H * (L.y_act ? 2 : 4));
   L.total = off;
   return L;
 }
@@ -164,7 +168,8 @@ void carve(Plan& p, const cmoe_problem& pr, int K, void* ws, const cmoe_routing*
   p.tiles = reinterpret_cast<Tile*>(base + L.tiles);
   p.tile_count = reinterpret_cast<int32_t*>(base + L.tile_count);
   p.h = base + L.h;
-  p.y = reinterpret_cast<float*>(base + L.y);
+  p.y = base + L.y;
+  p.y_act = L.y_act;
   p.coreset_ids = rt ? rt->coreset_ids : nullptr;
   p.coreset_size = rt ? rt->coreset_size : nullptr;
   p.block_mass = rt ? rt->block_mass : nullptr;

@@ -49,7 +49,8 @@ struct Plan {
   Tile* tiles;           // [max_tiles]
   int32_t* tile_count;   // [1]
   void* h;               // routed [N*K, I] then shared [N, Is]; act_dtype elements
-  float* y;              // [N*K + N][H] fp32: routed pairs, then shared rows
+  void* y;               // [N*K + N][H]: routed pairs, then shared rows
+  int y_act;             // y stored in act_dtype (else fp32), see carve()
   // optional caller outputs
   int32_t* coreset_ids;
   int32_t* coreset_size;

@@ -5,6 +5,8 @@
 //   out[r] = y_shared[r] + sum_j gate[r,j] * y[pos(r,j)]     (slots ascending)
 //
 // accumulated in fp32 with one rounding to the activation dtype at the end.
+// y is fp32, or bf16 for calls with many rows per expert (the down GEMM
+// rounds each pair's output once there).
 // The order is fixed, so results are bitwise identical from run to run (no
 // floating-point atomics anywhere on the path).
 #include "cmoe_device.h"
@@ -26,8 +28,16 @@ __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, f32x4 v) {
   *reinterpret_cast<u32x2*>(p) = o;
 }
 
-template <typename OT>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
+// four y values from fp32 or bf16 storage
+__device__ __forceinline__ f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 load4(const uint16_t* p) {
+  const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+  return f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xFFFF0000u),
+               __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xFFFF0000u)};
+}
+
+template <typename OT, typename YT>
+__global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
                                                       const int32_t* __restrict__ pair_pos,
                                                       const float* __restrict__ gates,
                                                       OT* __restrict__ out, int N, int H, int K,
@@ -45,12 +55,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     g[j] = j < K ? gates[(size_t)r * K + j] : 0.0f;
   }
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (has_shared) acc = *reinterpret_cast<const f32x4*>(y + ((size_t)N * K + r) * H + c);
+  if (has_shared) acc = load4(y + ((size_t)N * K + r) * H + c);
   f32x4 v[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j)
-    v[j] = pos[j] >= 0 ? *reinterpret_cast<const f32x4*>(y + (size_t)pos[j] * H + c)
-                       : f32x4{0.f, 0.f, 0.f, 0.f};
+    v[j] = pos[j] >= 0 ? load4(y + (size_t)pos[j] * H + c) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     if (pos[j] < 0) continue;
@@ -62,13 +71,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 hipError_t launch_combine(const Plan& p, void* out, hipStream_t s) {
   dim3 grid((p.H / 4 + 255) / 256, p.N);
-  if (p.act == CMOE_BF16)
-    combine_kernel<uint16_t><<<grid, 256, 0, s>>>(p.y, p.pair_pos, p.gates,
-                                                  static_cast<uint16_t*>(out), p.N, p.H, p.K,
-                                                  p.Is > 0);
-  else
-    combine_kernel<float><<<grid, 256, 0, s>>>(p.y, p.pair_pos, p.gates, static_cast<float*>(out),
-                                               p.N, p.H, p.K, p.Is > 0);
+  const int sh = p.Is > 0;
+  if (p.act == CMOE_BF16) {
+    uint16_t* o = static_cast<uint16_t*>(out);
+    if (p.y_act)
+      combine_kernel<uint16_t, uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(p.y), p.pair_pos,
+                                                              p.gates, o, p.N, p.H, p.K, sh);
+    else
+      combine_kernel<uint16_t, float><<<grid, 256, 0, s>>>(static_cast<const float*>(p.y), p.pair_pos,
+                                                           p.gates, o, p.N, p.H, p.K, sh);
+  } else {
+    combine_kernel<float, float><<<grid, 256, 0, s>>>(static_cast<const float*>(p.y), p.pair_pos, p.gates,
+                                                      static_cast<float*>(out), p.N, p.H, p.K, sh);
+  }
   return hipGetLastError();
 }
 

@@ -330,7 +330,7 @@ hipError_t launch_expert_down(const Plan& p, const cmoe_weights& w, hipStream_t 
   a.tiles = p.tiles;
   a.tile_count = p.tile_count;
   a.h = p.h;
-  a.y = p.y;
+  a.y = static_cast<float*>(p.y);  // fp32 whenever these kernels run
   a.N = p.N;
   a.H = p.H;
   a.E = p.E;

@@ -41,7 +41,8 @@ struct TiledArgs {
   const int32_t* tile_count;
   const int32_t* pair_row;
   void* h;           // [N*K*I + N*Is] activation dtype
-  float* y;          // [N*K + N, H]
+  void* y;           // [N*K + N, H], activation dtype (y_act) or fp32
+  int y_act;
   int N, H, E, I, Is, K, n_slices;
 };
 
@@ -253,13 +254,17 @@ __global__ __launch_bounds__(kTiledThreads) void expert_down_tiled_kernel(TiledA
   f32x4 acc[MT];
   G::run(As, asrc, brow, bsc, inter, mt_act, acc);
 
-  float* y = a.y + ((shared ? (size_t)a.N * a.K : 0) + (size_t)t.start) * H;
+  const size_t y0 = ((shared ? (size_t)a.N * a.K : 0) + (size_t)t.start) * H;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int m = mt * 16 + kg * 4 + v;
-      if (m < t.rows) y[(size_t)m * H + c0 + col] = acc[mt][v];
+      if (m < t.rows) {
+        const size_t at = y0 + (size_t)m * H + c0 + col;
+        if (a.y_act) store_act<AT>(static_cast<AT*>(a.y) + at, acc[mt][v]);
+        else static_cast<float*>(a.y)[at] = acc[mt][v];
+      }
     }
 }
 
@@ -294,6 +299,7 @@ hipError_t launch_expert_tiled(const Plan& p, const cmoe_weights& w, const void*
   a.pair_row = p.pair_row;
   a.h = p.h;
   a.y = p.y;
+  a.y_act = p.y_act;
   a.N = p.N;
   a.H = p.H;
   a.E = p.E;

@@ -62,11 +62,13 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
   constexpr int WV = ET * 8 * KB / 4;        // w vectors per slice
   constexpr int XPT = (XV + 255) / 256;      // per thread
   constexpr int WPT = (WV + 255) / 256;
-  __shared__ float xs[NBUF][8][RT][KP];
-  __shared__ float ws[NBUF][8][ET][KP];
-  // the chunk partial sums reuse the x staging buffer once the k loop is done
-  static_assert(sizeof(float) * 8 * RT * (ET + 1) <= sizeof(xs), "partials must fit in xs");
-  auto part = reinterpret_cast<float(*)[RT][ET + 1]>(&xs[0][0][0][0]);
+  // one LDS buffer: the x and w staging slices, and (once the k loop is
+  // done) the chunk partial sums over them
+  constexpr int kXs = NBUF * 8 * RT * KP, kWs = NBUF * 8 * ET * KP, kPart = 8 * RT * (ET + 1);
+  __shared__ float smem[(kXs + kWs) > kPart ? (kXs + kWs) : kPart];
+  auto xs = reinterpret_cast<float(*)[8][RT][KP]>(smem);
+  auto ws = reinterpret_cast<float(*)[8][ET][KP]>(smem + kXs);
+  auto part = reinterpret_cast<float(*)[RT][ET + 1]>(smem);
 
   const int tid = threadIdx.x;
   const int c = tid >> 5;  // chunk run by this thread
