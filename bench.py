@@ -224,10 +224,15 @@ def main():
     device_ms = stage_ms.sum(1)
     if dom_bytes is not None:
         achieved = float(dom_bytes.sum() / (stage_ms[:, dom].sum() * 1e-3) / 1e9)
-        traffic = measured_traffic(f"{dom_name}_kernel", wl.name, "expert_gemm.hip")
+        # the library's work-tile rule: 16-row tiles run the register-operand
+        # kernels (expert_gemm.hip), taller tiles the LDS-tiled ones
+        want = -(-(N * K * 3 // 2) // E)
+        tiled = want > 16
+        kname = f"expert_{'up' if dom == 2 else 'down'}{'_tiled' if tiled else ''}_kernel"
+        traffic = measured_traffic(kname, wl.name, "expert_tiled.hip" if tiled else "expert_gemm.hip")
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                    "traffic": traffic, "kernel": f"expert_{'up' if dom == 2 else 'down'}_kernel",
+                    "traffic": traffic, "kernel": kname,
                     "algorithmic_bytes_per_launch": int(dom_bytes.mean()),
                     "avg_launch_us": round(float(stage_ms[:, dom].mean() * 1e3), 2)}
     else:
