@@ -65,6 +65,25 @@ size_t workspace_bytes(const cmoe_problem& pr, int top_k);
 // workspace copies where the layout is the same.
 void carve(Plan& p, const cmoe_problem& pr, int top_k, void* ws, const cmoe_routing* rt);
 
+// XCD-aware work mapping for the LDS-tiled grouped GEMMs.  Workgroups are
+// dispatched to the 8 XCDs round-robin by id, and each XCD has its own L2;
+// every column slice of a tile reads the tile's gathered activation rows (up
+// to 128 rows).  Tile t is therefore given to XCD t % 8, with its slices on
+// consecutive ids of that XCD, so the rows come from memory once per tile
+// instead of once per slice (64 blocks: gate/up reads 624 MB instead of 917).
+// The one-row-tile kernels keep the plain mapping: their activations are a
+// few KiB, and whole experts per XCD only unbalance the XCDs.  The mapping
+// only affects locality: any dispatch order computes the same.
+constexpr int kXcds = 8;
+__host__ __device__ inline unsigned tile_grid(int max_tiles, int n_slices) {
+  return (unsigned)((max_tiles + kXcds - 1) / kXcds) * kXcds * (unsigned)n_slices;
+}
+__device__ inline void tile_of_block(unsigned g, int n_slices, int& slot, int& slice) {
+  const unsigned xcd = g % kXcds, local = g / kXcds;
+  slot = (int)(local / (unsigned)n_slices) * kXcds + (int)xcd;
+  slice = (int)(local % (unsigned)n_slices);
+}
+
 hipError_t launch_router(const Plan& p, const void* x, const float* router_w,
                          const float* router_b, hipStream_t s);
 // per-block routing; a one-block call also builds the permutation and the

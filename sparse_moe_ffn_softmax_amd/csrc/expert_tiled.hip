@@ -177,7 +177,8 @@ __global__ __launch_bounds__(kTiledThreads) void expert_up_tiled_kernel(TiledArg
   using WT = typename G::WT;
   using Fr = Frag<F>;
   __shared__ typename G::Lds As;
-  const int slot = blockIdx.x / a.n_slices, slice = blockIdx.x % a.n_slices;
+  int slot, slice;
+  tile_of_block(blockIdx.x, a.n_slices, slot, slice);
   if (slot >= *a.tile_count) return;
   const Tile t = a.tiles[slot];
   const bool shared = t.expert == a.E;
@@ -226,7 +227,8 @@ __global__ __launch_bounds__(kTiledThreads) void expert_down_tiled_kernel(TiledA
   using WT = typename G::WT;
   using Fr = Frag<F>;
   __shared__ typename G::Lds As;
-  const int slot = blockIdx.x / a.n_slices, slice = blockIdx.x % a.n_slices;
+  int slot, slice;
+  tile_of_block(blockIdx.x, a.n_slices, slot, slice);
   if (slot >= *a.tile_count) return;
   const Tile t = a.tiles[slot];
   const bool shared = t.expert == a.E;
@@ -307,7 +309,7 @@ hipError_t launch_expert_tiled(const Plan& p, const cmoe_weights& w, const void*
   a.Is = p.Is;
   a.K = p.K;
   a.n_slices = up ? (p.I > p.Is ? p.I : p.Is) / kTiledUpCols : p.H / kTiledDownCols;
-  const unsigned grid = (unsigned)p.max_tiles * (unsigned)a.n_slices;
+  const unsigned grid = tile_grid(p.max_tiles, a.n_slices);
   const WFmt f = p.wt == CMOE_FP8_E4M3 ? WFmt::FP8 : p.wt == CMOE_F32 ? WFmt::F32 : WFmt::BF16;
   if (up) {
     if (f == WFmt::FP8) launch_tiled_mt<true, WFmt::FP8>(a, p.mt_max, grid, s);
