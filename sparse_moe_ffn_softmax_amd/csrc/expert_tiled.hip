@@ -78,7 +78,7 @@ struct TiledGemm {
 
   static __device__ __forceinline__ void run(Lds& As, const AT* const (&asrc)[AV],
                                              const WT* brow, const float* bsc, int Kdim,
-                                             int mt_act, f32x4 (&acc)[MT]) {
+                                             int /*mt_act*/, f32x4 (&acc)[MT]) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int col = lane & 15, kg = lane >> 4;
     const int seg = tid % VPR, r0 = tid / VPR;
@@ -110,19 +110,23 @@ struct TiledGemm {
         for (int u = 0; u < U; ++u) b[u] = Fr::load_b(brow + k0 + u * Fr::kStep);
       }
     };
+    // Every row tile runs (rows past the tile are zeros in LDS): a guard per
+    // row tile would make each MFMA wait for its own LDS read.  Per k step the
+    // MT activation fragments are read first, then the MT MFMAs issue.
     auto compute = [&](typename Fr::B (&b)[U], int buf, int k0) {
       if constexpr (F == WFmt::FP8) {
         f32x4 tmp[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) tmp[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int u = 0; u < U; ++u) {
+          typename Fr::A av[MT];
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            if (mt < mt_act) {
-              const typename Fr::A av = Fr::load_a(&As[buf][mt * 16 + col][koff(u, kg)]);
-              tmp[mt] = Fr::mma(av, b[u], tmp[mt]);
-            }
+          for (int mt = 0; mt < MT; ++mt) av[mt] = Fr::load_a(&As[buf][mt * 16 + col][koff(u, kg)]);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) tmp[mt] = Fr::mma(av[mt], b[u], tmp[mt]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
         const float sc = bsc[k0 / 128];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -131,12 +135,11 @@ struct TiledGemm {
       } else {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+          typename Fr::A av[MT];
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            if (mt < mt_act) {
-              const typename Fr::A av = Fr::load_a(&As[buf][mt * 16 + col][koff(u, kg)]);
-              acc[mt] = Fr::mma(av, b[u], acc[mt]);
-            }
+          for (int mt = 0; mt < MT; ++mt) av[mt] = Fr::load_a(&As[buf][mt * 16 + col][koff(u, kg)]);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[mt] = Fr::mma(av[mt], b[u], acc[mt]);
           // keep the scheduler from hoisting every k step's operands at once
           __builtin_amdgcn_sched_barrier(0);
         }
