@@ -24,6 +24,8 @@
 #include "cmoe_launch.h"
 #include "expert_frag.h"
 
+#include <type_traits>
+
 namespace cmoe {
 
 constexpr int kTiledWaves = 8;                  // waves per workgroup, 16 MFMA columns each
@@ -46,11 +48,21 @@ struct TiledArgs {
   int N, H, E, I, Is, K, n_slices;
 };
 
+constexpr int kTiledMaxStages = 128;  // fp8 block scales held per weight row (hidden <= 16384)
+
+template <int B, int E, class Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // One workgroup's GEMM: acc[mt] (16 x 16 each) for this wave's 16 columns,
 // over k in [0, Kdim).  asrc[i]: source row pointer (stage 0) of the i-th
-// activation vector this thread stages, or nullptr for rows past the tile;
-// brow: this lane's weight row at its first k (blane); bsc: its fp8 block
-// scales.
+// activation vector this thread stages (rows past the tile repeat the tile's
+// first row, so that every load is unconditional); brow: this lane's weight
+// row at its first k (blane); bsc: its fp8 block scales, one per 128 k, in LDS.
 template <WFmt F, int MT>
 struct TiledGemm {
   using Fr = Frag<F>;
@@ -62,7 +74,10 @@ struct TiledGemm {
   static constexpr int VPR = 16;                    // 16-byte vectors per row per stage
   static constexpr int RPP = kTiledThreads / VPR;   // rows staged per pass of the workgroup
   static constexpr int AV = T / RPP;                // vectors per thread per stage
-  static constexpr int PAD = 16 / (int)sizeof(AT);
+  // 288-byte rows: the MFMA fragment reads (16 rows, one 16-byte unit each)
+  // are free of bank conflicts (a 272-byte pitch measured 3.7 conflict cycles
+  // per read on gfx950)
+  static constexpr int PAD = 32 / (int)sizeof(AT);
   using Lds = AT[2][T][KS + PAD];
   // k order inside a stage.  MFMA only needs A and B to agree on it, so fp8
   // pairs steps: lane group kg takes k [16kg, 16kg+16) of each 64-deep step
@@ -78,7 +93,7 @@ struct TiledGemm {
 
   static __device__ __forceinline__ void run(Lds& As, const AT* const (&asrc)[AV],
                                              const WT* brow, const float* bsc, int Kdim,
-                                             int /*mt_act*/, f32x4 (&acc)[MT]) {
+                                             f32x4 (&acc)[MT]) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int col = lane & 15, kg = lane >> 4;
     const int seg = tid % VPR, r0 = tid / VPR;
@@ -90,7 +105,7 @@ struct TiledGemm {
     auto load_a = [&](int k0) {
 #pragma unroll
       for (int i = 0; i < AV; ++i)
-        areg[i] = asrc[i] ? *reinterpret_cast<const u32x4*>(asrc[i] + k0) : u32x4{0u, 0u, 0u, 0u};
+        areg[i] = *reinterpret_cast<const u32x4*>(asrc[i] + k0);
     };
     auto store_a = [&](int buf) {
 #pragma unroll
@@ -146,29 +161,74 @@ struct TiledGemm {
       }
     };
 
+    // Schedule: while stage s feeds the MFMAs, stage s+1's activations and
+    // weights are in flight.  The compiler counts outstanding loads to place
+    // its waits, and that count is only exact where every load is
+    // unconditional: a conditional prefetch (or a load issued after the
+    // prefetches and consumed in the same stage, as a per-stage scale load
+    // was) makes it wait for everything, prefetch included.  So the
+    // activations of rows past the tile are real loads, the scales come from
+    // LDS, the last stage is peeled, and the common stage counts are fully
+    // unrolled (a loop header also merges the counts conservatively).
     const int S = Kdim / KS;
     load_a(0);
     load_b(b0, 0);
     store_a(0);
     __syncthreads();
-    for (int s = 0; s < S; s += 2) {
-      // stage s from buffer 0 / b0, prefetching stage s+1 into buffer 1 / b1
-      if (s + 1 < S) {
-        load_a((s + 1) * KS);
-        load_b(b1, (s + 1) * KS);
-      }
+    auto unrolled = [&](auto SC) {
+      constexpr int NS = decltype(SC)::value;
+      static_for<0, NS>([&](auto J) {
+        constexpr int st = decltype(J)::value;
+        constexpr bool more = st + 1 < NS;
+        if constexpr (st % 2 == 0) {
+          if constexpr (more) {
+            load_a((st + 1) * KS);
+            load_b(b1, (st + 1) * KS);
+          }
+          compute(b0, 0, st * KS);
+        } else {
+          if constexpr (more) {
+            load_a((st + 1) * KS);
+            load_b(b0, (st + 1) * KS);
+          }
+          compute(b1, 1, st * KS);
+        }
+        if constexpr (more) {
+          store_a((st + 1) % 2);
+          __syncthreads();
+        }
+      });
+    };
+    if (S == 16) {
+      unrolled(std::integral_constant<int, 16>{});
+      return;
+    }
+    if (S == 4) {
+      unrolled(std::integral_constant<int, 4>{});
+      return;
+    }
+    int s = 0;
+    for (; s + 2 < S; s += 2) {
+      load_a((s + 1) * KS);
+      load_b(b1, (s + 1) * KS);
       compute(b0, 0, s * KS);
-      if (s + 1 < S) store_a(1);
+      store_a(1);
       __syncthreads();
-      if (s + 1 >= S) break;
-      // stage s+1 from buffer 1 / b1, prefetching stage s+2 into buffer 0 / b0
-      if (s + 2 < S) {
-        load_a((s + 2) * KS);
-        load_b(b0, (s + 2) * KS);
-      }
+      load_a((s + 2) * KS);
+      load_b(b0, (s + 2) * KS);
       compute(b1, 1, (s + 1) * KS);
-      if (s + 2 < S) store_a(0);
+      store_a(0);
       __syncthreads();
+    }
+    if (s + 1 < S) {
+      load_a((s + 1) * KS);
+      load_b(b1, (s + 1) * KS);
+      compute(b0, 0, s * KS);
+      store_a(1);
+      __syncthreads();
+      compute(b1, 1, (s + 1) * KS);
+    } else {
+      compute(b0, 0, s * KS);
     }
   }
 };
@@ -178,8 +238,8 @@ __global__ __launch_bounds__(kTiledThreads) void expert_up_tiled_kernel(TiledArg
   using G = TiledGemm<F, MT>;
   using AT = typename G::AT;
   using WT = typename G::WT;
-  using Fr = Frag<F>;
   __shared__ typename G::Lds As;
+  __shared__ float sc_s[2][kTiledMaxStages];
   int slot, slice;
   tile_of_block(blockIdx.x, a.n_slices, slot, slice);
   if (slot >= *a.tile_count) return;
@@ -195,9 +255,9 @@ __global__ __launch_bounds__(kTiledThreads) void expert_up_tiled_kernel(TiledArg
 #pragma unroll
   for (int i = 0; i < G::AV; ++i) {
     const int r = tid / G::VPR + i * G::RPP;
-    const int src = r < t.rows ? (shared ? t.start + r : a.pair_row[t.start + r]) : -1;
-    asrc[i] = src >= 0 ? static_cast<const AT*>(a.x) + (size_t)src * H + (tid % G::VPR) * (16 / (int)sizeof(AT))
-                       : nullptr;
+    const int rr = r < t.rows ? r : 0;
+    const int src = shared ? t.start + rr : a.pair_row[t.start + rr];
+    asrc[i] = static_cast<const AT*>(a.x) + (size_t)src * H + (tid % G::VPR) * (16 / (int)sizeof(AT));
   }
   const WT* W = shared ? static_cast<const WT*>(a.sw) : static_cast<const WT*>(a.w) + (size_t)t.expert * 2 * a.I * H;
   const float* S = nullptr;
@@ -205,10 +265,15 @@ __global__ __launch_bounds__(kTiledThreads) void expert_up_tiled_kernel(TiledArg
   const int i0 = slice * kTiledUpCols + wave * 8;
   const int wr = col < 8 ? i0 + col : inter + i0 + col - 8;  // gate row / up row
   const WT* brow = W + (size_t)wr * H + G::blane(kg);
-  const float* bsc = (F == WFmt::FP8) ? S + (size_t)(wr / 128) * (H / 128) : nullptr;
-  const int mt_act = (t.rows + 15) >> 4;
+  if constexpr (F == WFmt::FP8) {
+    // the workgroup's gate rows share one 128-row scale block, its up rows
+    // another; the first stage's barrier orders these writes before any read
+    const int ns = H / 128;
+    const int srow[2] = {(slice * kTiledUpCols) / 128, (inter + slice * kTiledUpCols) / 128};
+    for (int i = tid; i < 2 * ns; i += kTiledThreads) sc_s[i / ns][i % ns] = S[(size_t)srow[i / ns] * ns + i % ns];
+  }
   f32x4 acc[MT];
-  G::run(As, asrc, brow, bsc, H, mt_act, acc);
+  G::run(As, asrc, brow, sc_s[col < 8 ? 0 : 1], H, acc);
 
   AT* h = static_cast<AT*>(a.h) +
           (shared ? (size_t)a.N * a.K * a.I + (size_t)t.start * a.Is : (size_t)t.start * a.I);
@@ -228,8 +293,8 @@ __global__ __launch_bounds__(kTiledThreads) void expert_down_tiled_kernel(TiledA
   using G = TiledGemm<F, MT>;
   using AT = typename G::AT;
   using WT = typename G::WT;
-  using Fr = Frag<F>;
   __shared__ typename G::Lds As;
+  __shared__ float sc_s[2][kTiledMaxStages];
   int slot, slice;
   tile_of_block(blockIdx.x, a.n_slices, slot, slice);
   if (slot >= *a.tile_count) return;
@@ -246,7 +311,7 @@ __global__ __launch_bounds__(kTiledThreads) void expert_down_tiled_kernel(TiledA
 #pragma unroll
   for (int i = 0; i < G::AV; ++i) {
     const int r = tid / G::VPR + i * G::RPP;
-    asrc[i] = r < t.rows ? hb + (size_t)r * inter + (tid % G::VPR) * (16 / (int)sizeof(AT)) : nullptr;
+    asrc[i] = hb + (size_t)(r < t.rows ? r : 0) * inter + (tid % G::VPR) * (16 / (int)sizeof(AT));
   }
   const WT* W = shared ? static_cast<const WT*>(a.sw) : static_cast<const WT*>(a.w) + (size_t)t.expert * H * a.I;
   const float* S = nullptr;
@@ -254,10 +319,13 @@ __global__ __launch_bounds__(kTiledThreads) void expert_down_tiled_kernel(TiledA
   const int c0 = slice * kTiledDownCols + wave * 16;
   const int orow = c0 + col;  // W2 row = output column
   const WT* brow = W + (size_t)orow * inter + G::blane(kg);
-  const float* bsc = (F == WFmt::FP8) ? S + (size_t)(orow / 128) * (inter / 128) : nullptr;
-  const int mt_act = (t.rows + 15) >> 4;
+  if constexpr (F == WFmt::FP8) {
+    // the workgroup's 128 output rows are one scale block row
+    const int ns = inter / 128;
+    for (int i = tid; i < ns; i += kTiledThreads) sc_s[0][i] = S[(size_t)slice * ns + i];
+  }
   f32x4 acc[MT];
-  G::run(As, asrc, brow, bsc, inter, mt_act, acc);
+  G::run(As, asrc, brow, sc_s[0], inter, acc);
 
   const size_t y0 = ((shared ? (size_t)a.N * a.K : 0) + (size_t)t.start) * H;
 #pragma unroll
