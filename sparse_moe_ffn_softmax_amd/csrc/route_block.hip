@@ -36,6 +36,18 @@
 // are ordered by (mass desc, id asc) with four 64-wide bitonic sorts in
 // registers and a binary-search merge of the four sorted runs.
 //
+// The coreset cut needs the serial prefix sum cum[] only where it decides
+// something.  A parallel scan gives every prefix P[i] in another summation
+// order; recursive summation of n non-negative terms is within
+// (n-1) u / (1 - (n-1) u) of the exact sum in relative terms (Higham,
+// "Accuracy and Stability of Numerical Algorithms", 2002, section 4.2), and
+// so is the scan with its depth in place of n-1.  With both bounds far below
+// a margin of 2^-40, an index i is provably below the threshold when
+// P[i] (1 + 2^-40) < tau P[E-1] (1 - 2^-40), and provably at or above it when
+// P[i] (1 - 2^-40) >= tau P[E-1] (1 + 2^-40).  When the first index that is
+// not provably below is provably at or above, it is the cut; otherwise (the
+// threshold lies within about 1e-12 of a prefix sum) the serial sum runs.
+//
 // A one-block call goes on to build the row -> expert permutation and the
 // GEMM work list in the same kernel (permute.h); with many blocks every block
 // publishes its rows per expert as one mask word each, and two small kernels
@@ -234,6 +246,8 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
   __shared__ int rcnt[4][kMaxExperts];
   __shared__ MassKey run_s[4][64];   // four sorted runs of 64 experts
   __shared__ int runpos_s[kMaxExperts];  // an expert's place in its own run
+  __shared__ double wtot_s[4];  // per-wave totals of the prefix scan
+  __shared__ int cut_s;         // first index not provably below the threshold
   __shared__ uint32_t mask1_s[kMaxExperts];  // one-block calls: rows per expert
   __shared__ int tk_s[kMaxRows * 8];          // this block's top-k
   __shared__ int m_sh;
@@ -319,6 +333,7 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
     }
     mass_s[tid] = acc;
   }
+  if (tid == 0) cut_s = kMaxExperts;
   __syncthreads();
 
   // rank under (mass desc, id asc).  Waves 0..3 each sort 64 experts in
@@ -366,35 +381,70 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
   }
   __syncthreads();
 
-  // sequential prefix sum in mass order (the contract's order), one lane;
-  // batches of 16, the next batch's loads in flight while this one adds.
-  // Loads and stores are unconditional (the arrays hold 256 entries; values
-  // past E are never read back).
-  if (tid == 0) {
-    double c = 0.0;
-    double v[16], nxt[16];
+  if (tau < 1.0f) {
+    // the cut, certified from a parallel scan where the bounds decide it
+    // (see the header); tid < 256 holds prefix index tid
+    constexpr double kLo = 1.0 - 0x1p-40, kHi = 1.0 + 0x1p-40;
+    double v = 0.0;
+    if (tid < kMaxExperts) {
+      v = tid < E ? smass_s[tid] : 0.0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = smass_s[i];
-    for (int i0 = 0; i0 < E; i0 += 16) {
-      const int n0 = min(i0 + 16, kMaxExperts - 16);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) nxt[i] = smass_s[n0 + i];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        c = c + v[i];
-        v[i] = c;
+      for (int d = 1; d < 64; d <<= 1) {
+        const double o = __shfl_up(v, d, 64);
+        if (lane >= d) v = v + o;
       }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) cum_s[i0 + i] = v[i];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = nxt[i];
+      if (lane == 63) wtot_s[wave] = v;
     }
-  }
-  __syncthreads();
-  if (tau < 1.0f && tid < E) {
-    const double thr = static_cast<double>(tau) * cum_s[E - 1];
-    // cum is non-decreasing, so exactly one index is the first to reach thr
-    if (cum_s[tid] >= thr && (tid == 0 || cum_s[tid - 1] < thr)) m_sh = tid + 1;
+    __syncthreads();
+    if (tid < kMaxExperts) {
+      double off = 0.0;
+      for (int w = 0; w < wave; ++w) off = off + wtot_s[w];
+      const double pfx = v + off;
+      const double total = ((wtot_s[0] + wtot_s[1]) + wtot_s[2]) + wtot_s[3];
+      cum_s[tid] = pfx;
+      // the first index of this wave that is not provably below the threshold
+      const bool open = tid < E && !(pfx * kHi < static_cast<double>(tau) * total * kLo);
+      const uint64_t bal = __ballot(open);
+      if (bal != 0ull && lane == 0) atomicMin(&cut_s, 64 * wave + __builtin_ctzll(bal));
+    }
+    __syncthreads();
+    const int i0 = cut_s;
+    const double total = ((wtot_s[0] + wtot_s[1]) + wtot_s[2]) + wtot_s[3];
+    const bool certified = i0 < E && cum_s[i0] * kLo >= static_cast<double>(tau) * total * kHi;
+    if (certified) {
+      if (tid == 0) m_sh = i0 + 1;
+    } else {
+      // the serial sum of the contract, one lane; batches of 16, the next
+      // batch's loads in flight while this one adds (loads and stores are
+      // unconditional: the arrays hold 256 entries, values past E unread)
+      __syncthreads();  // everyone has read cum_s (the scan) above
+      if (tid == 0) {
+        double c = 0.0;
+        double x[16], nxt[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = smass_s[i];
+        for (int i0s = 0; i0s < E; i0s += 16) {
+          const int n0 = min(i0s + 16, kMaxExperts - 16);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) nxt[i] = smass_s[n0 + i];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            c = c + x[i];
+            x[i] = c;
+          }
+#pragma unroll
+          for (int i = 0; i < 16; ++i) cum_s[i0s + i] = x[i];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) x[i] = nxt[i];
+        }
+      }
+      __syncthreads();
+      if (tid < E) {
+        const double thr = static_cast<double>(tau) * cum_s[E - 1];
+        // cum is non-decreasing, so exactly one index is the first to reach thr
+        if (cum_s[tid] >= thr && (tid == 0 || cum_s[tid - 1] < thr)) m_sh = tid + 1;
+      }
+    }
   }
   __syncthreads();
   const int m = m_sh;

@@ -91,6 +91,17 @@ def test_uniform_router_closed_form_on_gpu():
     assert np.all(ref["coreset_size"] == 58)          # ceil(fl32(0.9) * 64)
 
 
+@pytest.mark.parametrize("tau,m", [(0.5, 32), (0.25, 16)])
+def test_threshold_on_a_prefix_sum_takes_the_serial_cut(tau, m):
+    """64 equal masses of exactly 0.25 make every prefix sum exact, and
+    tau * total lands on one of them: no error bound can separate them, so
+    the kernel must fall back to the serial prefix sum of the contract."""
+    inp = W.generate(MID.with_(num_experts=64, seed=35))
+    inp = W.with_arrays(inp, router_w=np.zeros_like(inp.router_w))
+    _, _, ref = check(inp, tau=tau)
+    assert np.all(ref["coreset_size"] == m)
+
+
 # ---------------------------------------------------------------------------
 # full-size workloads
 # ---------------------------------------------------------------------------
