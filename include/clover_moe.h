@@ -95,7 +95,10 @@ typedef struct {
     int32_t num_experts;  /* E: 1..256 */
     int32_t inter;        /* I: multiple of 128, 128..8192 */
     int32_t shared_inter; /* Is: 0 (no shared expert) or a multiple of 128, <= 8192 */
-    int32_t block_rows;   /* R: 8, 16 or 32 (CMF model card, "Usage": block size knob) */
+    int32_t block_rows;   /* R: 8, 16 or 32 for diffusion blocks (CMF model card, "Usage": block
+                             size knob); 1, 2 or 4 for autoregressive decode (llama.cpp PR
+                             #31306: the model in AR mode) and for verifying 1-4 drafted
+                             candidates (InfiniLM PR #584, "Summary") */
     int32_t num_blocks;   /* B: 1..1024; N = B*R rows, block b is rows [b*R, (b+1)*R) */
     int32_t act_dtype;    /* cmoe_dtype of x and out: CMOE_F32 or CMOE_BF16 */
     int32_t weight_dtype; /* cmoe_dtype of the expert weights.  Supported pairs

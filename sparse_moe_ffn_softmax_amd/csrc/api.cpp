@@ -64,9 +64,12 @@ cmoe_status check_problem(const cmoe_problem* p, int32_t top_k) {
   if (p->shared_inter > 8192 || p->shared_inter % 128)
     return fail(CMOE_ERR_UNSUPPORTED, "shared_inter=%d: must be 0 or a multiple of 128 up to 8192",
                 p->shared_inter);
-  if (p->block_rows != 8 && p->block_rows != 16 && p->block_rows != 32)
-    return fail(p->block_rows <= 0 ? CMOE_ERR_VALUE : CMOE_ERR_UNSUPPORTED,
-                "block_rows=%d: must be 8, 16 or 32", p->block_rows);
+  // 8, 16, 32: diffusion blocks; 1, 2, 4: autoregressive decode and the
+  // verification of 1-4 drafted candidates
+  const int R = p->block_rows;
+  if (R != 1 && R != 2 && R != 4 && R != 8 && R != 16 && R != 32)
+    return fail(R <= 0 ? CMOE_ERR_VALUE : CMOE_ERR_UNSUPPORTED,
+                "block_rows=%d: must be 1, 2, 4, 8, 16 or 32", R);
   if (p->num_blocks < 1) return fail(CMOE_ERR_VALUE, "num_blocks=%d must be >= 1", p->num_blocks);
   if (p->num_blocks > 1024)
     return fail(CMOE_ERR_UNSUPPORTED, "num_blocks=%d: at most 1024 blocks per call", p->num_blocks);

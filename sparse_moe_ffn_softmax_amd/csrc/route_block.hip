@@ -250,6 +250,7 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
   __shared__ int cut_s;         // first index not provably below the threshold
   __shared__ uint32_t mask1_s[kMaxExperts];  // one-block calls: rows per expert
   __shared__ int tk_s[kMaxRows * 8];          // this block's top-k
+  __shared__ int pick_s[kMaxRows * 8];        // expert taken by each (row, slot)
   __shared__ int m_sh;
   __shared__ PermuteLds perm_lds;
 
@@ -262,9 +263,16 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
   if (tid == 0) m_sh = E;
   if (tid < kMaxExperts) mask1_s[tid] = 0u;
 
+  // The softmax, block mass and coreset are needed below a threshold of 1 and
+  // for the block-mass and coreset outputs.  A full-route call without them
+  // (decode, verification) needs only the row maxima, the top-k of the logits
+  // and the gates, whose u values are recomputed for the chosen experts.
+  const bool need_mass = tau < 1.0f || block_mass != nullptr || coreset_ids != nullptr;
+
   // rows w and w+16 on wave w: logits to LDS, row maxima (exact, order-free),
-  // and u = exp(l - max) as 8 independent chains per lane.  Rows past R and
-  // experts past E hold -inf logits and u = 0 (rows past R: NaN), never read.
+  // and u = exp(l - max) as 8 independent chains per lane (4 when only the
+  // first row exists).  Rows past R and experts past E hold -inf logits; the
+  // u of rows past R is not computed and never read.
   {
     float lv[2][4], mx[2];
 #pragma unroll
@@ -283,170 +291,183 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
       mx[h] = wave_max_f32(mm);
       if (lane == 0) m_s[r] = mx[h];
     }
+    if (need_mass && wave + 16 < R) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int r = wave + 16 * h, e = lane + 64 * s;
+          p_s[pidx(r, e)] = exp_reduced(static_cast<double>(lv[h][s]) - static_cast<double>(mx[h]));
+        }
+    } else if (need_mass && wave < R) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int r = wave + 16 * h, e = lane + 64 * s;
-        p_s[pidx(r, e)] = exp_reduced(static_cast<double>(lv[h][s]) - static_cast<double>(mx[h]));
+        const int e = lane + 64 * s;
+        p_s[pidx(wave, e)] = exp_reduced(static_cast<double>(lv[0][s]) - static_cast<double>(mx[0]));
       }
+    }
   }
   __syncthreads();
 
-  // Z: chunk partial sums, one thread per (row, chunk), then the fixed tree
-  if (tid < kMaxRows * 8) {
-    const int r = tid >> 3, j = tid & 7;
-    if (r < R) {
-      const int lo = (j * E) / 8, hi = ((j + 1) * E) / 8;
+  if (need_mass) {
+
+    // Z: chunk partial sums, one thread per (row, chunk), then the fixed tree
+    if (tid < kMaxRows * 8) {
+      const int r = tid >> 3, j = tid & 7;
+      if (r < R) {
+        const int lo = (j * E) / 8, hi = ((j + 1) * E) / 8;
+        double acc = 0.0;
+  #pragma unroll 8
+        for (int e = lo; e < hi; ++e) acc = acc + p_s[pidx(r, e)];
+        zpart[r][j] = acc;
+      }
+    }
+    __syncthreads();
+    if (tid < R) {
+      double p[8];
+  #pragma unroll
+      for (int j = 0; j < 8; ++j) p[j] = zpart[tid][j];
+      p[0] = p[0] + p[4];
+      p[1] = p[1] + p[5];
+      p[2] = p[2] + p[6];
+      p[3] = p[3] + p[7];
+      p[0] = p[0] + p[2];
+      p[1] = p[1] + p[3];
+      z_s[tid] = p[0] + p[1];
+    }
+    __syncthreads();
+
+    // block mass, one thread per expert: p = u / Z for each row, summed over
+    // rows ascending (the 8 divisions of a group are independent, only the adds
+    // are chained; rows past R, in blocks of 1, 2 or 4 rows, hold no values and
+    // add nothing)
+    if (tid < E) {
       double acc = 0.0;
-#pragma unroll 8
-      for (int e = lo; e < hi; ++e) acc = acc + p_s[pidx(r, e)];
-      zpart[r][j] = acc;
-    }
-  }
-  __syncthreads();
-  if (tid < R) {
-    double p[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) p[j] = zpart[tid][j];
-    p[0] = p[0] + p[4];
-    p[1] = p[1] + p[5];
-    p[2] = p[2] + p[6];
-    p[3] = p[3] + p[7];
-    p[0] = p[0] + p[2];
-    p[1] = p[1] + p[3];
-    z_s[tid] = p[0] + p[1];
-  }
-  __syncthreads();
-
-  // block mass, one thread per expert: p = u / Z for each row, summed over
-  // rows ascending (R is a multiple of 8; the 8 divisions of a group are
-  // independent, only the adds are chained)
-  if (tid < E) {
-    double acc = 0.0;
-    for (int r0 = 0; r0 < R; r0 += 8) {
-      double q[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = p_s[pidx(r0 + i, tid)] / z_s[r0 + i];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc = acc + q[i];
-    }
-    mass_s[tid] = acc;
-  }
-  if (tid == 0) cut_s = kMaxExperts;
-  __syncthreads();
-
-  // rank under (mass desc, id asc).  Waves 0..3 each sort 64 experts in
-  // registers (experts past E carry mass +0 and the largest ids, so they sort
-  // after every real expert); then thread
-  // (expert e, run q) counts the experts of run q that beat e: e's place in
-  // its own run, or a binary search (the beating experts are a prefix of a
-  // sorted run).  The rank is the sum over the four runs.
-  if (wave < 4) {
-    const int e = 64 * wave + lane;
-    MassKey k;
-    k.m = e < E ? static_cast<uint64_t>(__double_as_longlong(mass_s[e])) : 0ull;
-    k.nid = ~static_cast<uint32_t>(e);
-    wave_sort64(k, lane);
-    run_s[wave][lane] = k;
-    runpos_s[~k.nid & 255] = lane;
-  }
-  __syncthreads();
-  {
-    const int e = tid & 255, q = tid >> 8;
-    if (e < E) {
-      int cnt;
-      if (q == (e >> 6)) {
-        cnt = runpos_s[e];
-      } else {
-        MassKey me;
-        me.m = static_cast<uint64_t>(__double_as_longlong(mass_s[e]));
-        me.nid = ~static_cast<uint32_t>(e);
-        cnt = 0;
-#pragma unroll
-        for (int step = 32; step > 0; step >>= 1)
-          if (beats(run_s[q][cnt + step - 1], me)) cnt += step;
-        // the steps reach index 62 at most: all 64 beating e ends at 63
-        if (cnt == 63 && beats(run_s[q][63], me)) cnt = 64;
+      for (int r0 = 0; r0 < R; r0 += 8) {
+        double q[8];
+  #pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = p_s[pidx(r0 + i, tid)] / z_s[r0 + i];
+  #pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (r0 + i < R) acc = acc + q[i];
       }
-      rcnt[q][e] = cnt;
+      mass_s[tid] = acc;
     }
-  }
-  __syncthreads();
-  if (tid < E) {
-    const int rank = rcnt[0][tid] + rcnt[1][tid] + rcnt[2][tid] + rcnt[3][tid];
-    rank_s[tid] = rank;
-    order_s[min(rank, kMaxExperts - 1)] = tid;
-    smass_s[min(rank, kMaxExperts - 1)] = mass_s[tid];
-  }
-  __syncthreads();
+    if (tid == 0) cut_s = kMaxExperts;
+    __syncthreads();
 
-  if (tau < 1.0f) {
-    // the cut, certified from a parallel scan where the bounds decide it
-    // (see the header); tid < 256 holds prefix index tid
-    constexpr double kLo = 1.0 - 0x1p-40, kHi = 1.0 + 0x1p-40;
-    double v = 0.0;
-    if (tid < kMaxExperts) {
-      v = tid < E ? smass_s[tid] : 0.0;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const double o = __shfl_up(v, d, 64);
-        if (lane >= d) v = v + o;
-      }
-      if (lane == 63) wtot_s[wave] = v;
+    // rank under (mass desc, id asc).  Waves 0..3 each sort 64 experts in
+    // registers (experts past E carry mass +0 and the largest ids, so they sort
+    // after every real expert); then thread
+    // (expert e, run q) counts the experts of run q that beat e: e's place in
+    // its own run, or a binary search (the beating experts are a prefix of a
+    // sorted run).  The rank is the sum over the four runs.
+    if (wave < 4) {
+      const int e = 64 * wave + lane;
+      MassKey k;
+      k.m = e < E ? static_cast<uint64_t>(__double_as_longlong(mass_s[e])) : 0ull;
+      k.nid = ~static_cast<uint32_t>(e);
+      wave_sort64(k, lane);
+      run_s[wave][lane] = k;
+      runpos_s[~k.nid & 255] = lane;
     }
     __syncthreads();
-    if (tid < kMaxExperts) {
-      double off = 0.0;
-      for (int w = 0; w < wave; ++w) off = off + wtot_s[w];
-      const double pfx = v + off;
-      const double total = ((wtot_s[0] + wtot_s[1]) + wtot_s[2]) + wtot_s[3];
-      cum_s[tid] = pfx;
-      // the first index of this wave that is not provably below the threshold
-      const bool open = tid < E && !(pfx * kHi < static_cast<double>(tau) * total * kLo);
-      const uint64_t bal = __ballot(open);
-      if (bal != 0ull && lane == 0) atomicMin(&cut_s, 64 * wave + __builtin_ctzll(bal));
-    }
-    __syncthreads();
-    const int i0 = cut_s;
-    const double total = ((wtot_s[0] + wtot_s[1]) + wtot_s[2]) + wtot_s[3];
-    const bool certified = i0 < E && cum_s[i0] * kLo >= static_cast<double>(tau) * total * kHi;
-    if (certified) {
-      if (tid == 0) m_sh = i0 + 1;
-    } else {
-      // the serial sum of the contract, one lane; batches of 16, the next
-      // batch's loads in flight while this one adds (loads and stores are
-      // unconditional: the arrays hold 256 entries, values past E unread)
-      __syncthreads();  // everyone has read cum_s (the scan) above
-      if (tid == 0) {
-        double c = 0.0;
-        double x[16], nxt[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = smass_s[i];
-        for (int i0s = 0; i0s < E; i0s += 16) {
-          const int n0 = min(i0s + 16, kMaxExperts - 16);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) nxt[i] = smass_s[n0 + i];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            c = c + x[i];
-            x[i] = c;
-          }
-#pragma unroll
-          for (int i = 0; i < 16; ++i) cum_s[i0s + i] = x[i];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) x[i] = nxt[i];
+    {
+      const int e = tid & 255, q = tid >> 8;
+      if (e < E) {
+        int cnt;
+        if (q == (e >> 6)) {
+          cnt = runpos_s[e];
+        } else {
+          MassKey me;
+          me.m = static_cast<uint64_t>(__double_as_longlong(mass_s[e]));
+          me.nid = ~static_cast<uint32_t>(e);
+          cnt = 0;
+  #pragma unroll
+          for (int step = 32; step > 0; step >>= 1)
+            if (beats(run_s[q][cnt + step - 1], me)) cnt += step;
+          // the steps reach index 62 at most: all 64 beating e ends at 63
+          if (cnt == 63 && beats(run_s[q][63], me)) cnt = 64;
         }
+        rcnt[q][e] = cnt;
+      }
+    }
+    __syncthreads();
+    if (tid < E) {
+      const int rank = rcnt[0][tid] + rcnt[1][tid] + rcnt[2][tid] + rcnt[3][tid];
+      rank_s[tid] = rank;
+      order_s[min(rank, kMaxExperts - 1)] = tid;
+      smass_s[min(rank, kMaxExperts - 1)] = mass_s[tid];
+    }
+    __syncthreads();
+
+    if (tau < 1.0f) {
+      // the cut, certified from a parallel scan where the bounds decide it
+      // (see the header); tid < 256 holds prefix index tid
+      constexpr double kLo = 1.0 - 0x1p-40, kHi = 1.0 + 0x1p-40;
+      double v = 0.0;
+      if (tid < kMaxExperts) {
+        v = tid < E ? smass_s[tid] : 0.0;
+  #pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const double o = __shfl_up(v, d, 64);
+          if (lane >= d) v = v + o;
+        }
+        if (lane == 63) wtot_s[wave] = v;
       }
       __syncthreads();
-      if (tid < E) {
-        const double thr = static_cast<double>(tau) * cum_s[E - 1];
-        // cum is non-decreasing, so exactly one index is the first to reach thr
-        if (cum_s[tid] >= thr && (tid == 0 || cum_s[tid - 1] < thr)) m_sh = tid + 1;
+      if (tid < kMaxExperts) {
+        double off = 0.0;
+        for (int w = 0; w < wave; ++w) off = off + wtot_s[w];
+        const double pfx = v + off;
+        const double total = ((wtot_s[0] + wtot_s[1]) + wtot_s[2]) + wtot_s[3];
+        cum_s[tid] = pfx;
+        // the first index of this wave that is not provably below the threshold
+        const bool open = tid < E && !(pfx * kHi < static_cast<double>(tau) * total * kLo);
+        const uint64_t bal = __ballot(open);
+        if (bal != 0ull && lane == 0) atomicMin(&cut_s, 64 * wave + __builtin_ctzll(bal));
+      }
+      __syncthreads();
+      const int i0 = cut_s;
+      const double total = ((wtot_s[0] + wtot_s[1]) + wtot_s[2]) + wtot_s[3];
+      const bool certified = i0 < E && cum_s[i0] * kLo >= static_cast<double>(tau) * total * kHi;
+      if (certified) {
+        if (tid == 0) m_sh = i0 + 1;
+      } else {
+        // the serial sum of the contract, one lane; batches of 16, the next
+        // batch's loads in flight while this one adds (loads and stores are
+        // unconditional: the arrays hold 256 entries, values past E unread)
+        __syncthreads();  // everyone has read cum_s (the scan) above
+        if (tid == 0) {
+          double c = 0.0;
+          double x[16], nxt[16];
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) x[i] = smass_s[i];
+          for (int i0s = 0; i0s < E; i0s += 16) {
+            const int n0 = min(i0s + 16, kMaxExperts - 16);
+  #pragma unroll
+            for (int i = 0; i < 16; ++i) nxt[i] = smass_s[n0 + i];
+  #pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              c = c + x[i];
+              x[i] = c;
+            }
+  #pragma unroll
+            for (int i = 0; i < 16; ++i) cum_s[i0s + i] = x[i];
+  #pragma unroll
+            for (int i = 0; i < 16; ++i) x[i] = nxt[i];
+          }
+        }
+        __syncthreads();
+        if (tid < E) {
+          const double thr = static_cast<double>(tau) * cum_s[E - 1];
+          // cum is non-decreasing, so exactly one index is the first to reach thr
+          if (cum_s[tid] >= thr && (tid == 0 || cum_s[tid - 1] < thr)) m_sh = tid + 1;
+        }
       }
     }
-  }
-  __syncthreads();
+    __syncthreads();
+  }  // need_mass
   const int m = m_sh;
 
   if (coreset_ids && tid < E) coreset_ids[(size_t)b * E + tid] = tid < m ? order_s[tid] : -1;
@@ -456,9 +477,10 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
   // restricted top-k: half a wave per row (rows 2w and 2w+1 on wave w); each
   // lane sorts its 8 candidates (experts (lane&31) + 32*s) by key into LDS,
   // and every slot takes the best head of the half-wave: the largest high
-  // word, then the largest low word among the lanes holding it.  The lane
-  // whose head was taken moves its pointer on.
-  {
+  // word (logit), then, only if several lanes hold it, the largest low word
+  // (lowest id).  The lane whose head was taken records it and moves on.
+  // Waves whose two rows are past R (blocks of fewer than 32 rows) skip it.
+  if (2 * wave < R) {
     const int half = lane >> 5, hl = lane & 31;
     const int r = 2 * wave + half;
     const bool row_ok = r < R;
@@ -466,7 +488,7 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int e = hl + 32 * s;
-      const bool ok = row_ok && e < E && rank_s[e] < m;
+      const bool ok = row_ok && e < E && (m >= E || rank_s[e] < m);
       key[s] = ok ? (static_cast<uint64_t>(logit_key(l_s[r][e])) << 32) | static_cast<uint32_t>(~e) : 0ull;
     }
     sort8_desc(key);
@@ -475,23 +497,28 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
     for (int s = 1; s < 8; ++s) lst[s * kThreads + tid] = key[s];
     uint64_t head = key[0];
     int ptr = 0;
-    int my_e = -1;  // lane hl keeps the expert of slot hl
-    int k_eff = 0;
+    int k_eff = 0;  // slots filled in this lane's row
     for (int j = 0; j < K; ++j) {
       const uint32_t hh = static_cast<uint32_t>(head >> 32), hlo = static_cast<uint32_t>(head);
       const uint32_t bh = half_max_u32(hh);
-      const uint32_t bl = half_max_u32(hh == bh ? hlo : 0u);
-      const bool found = (bh | bl) != 0u;
-      if (found) {
-        if (hl == j) my_e = static_cast<int>(~bl);
-        k_eff = j + 1;
+      const bool top = head != 0ull && hh == bh;  // (a real key has ~id != 0 below)
+      const uint64_t tb = __ballot(top);
+      const uint32_t tlo = static_cast<uint32_t>(tb), thi = static_cast<uint32_t>(tb >> 32);
+      bool popped = top;
+      if (__builtin_popcount(tlo) > 1 || __builtin_popcount(thi) > 1) {
+        // equal logits in some row of this wave: the lowest id wins
+        const uint32_t bl = half_max_u32(top ? hlo : 0u);
+        popped = top && hlo == bl;
       }
-      const bool popped = found && hh == bh && hlo == bl;
+      if (popped) pick_s[r * 8 + j] = static_cast<int>(~hlo);
+      k_eff += (half ? thi : tlo) != 0u ? 1 : 0;
       ptr += popped ? 1 : 0;
       const uint64_t nxt = lst[min(ptr, 7) * kThreads + tid];
       head = popped ? (ptr < 8 ? nxt : 0ull) : head;
-      if (__ballot(found) == 0ull) break;  // both rows exhausted
+      if (tb == 0ull) break;  // both rows exhausted
     }
+    __builtin_amdgcn_wave_barrier();
+    const int my_e = hl < k_eff ? pick_s[r * 8 + hl] : -1;  // lane hl keeps slot hl
     // gates: u of the chosen experts (recomputed: same operations, same
     // bits); each lane sums its row's slots in order (empty slots add +0)
     const double u = my_e >= 0

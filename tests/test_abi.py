@@ -79,6 +79,11 @@ def call(prob=None, w=None, x=fake(10), tau=0.9, k=8, out=fake(11), routing=None
                                         out, rt, ws, ws_bytes, None)
 
 
+@pytest.mark.parametrize("rows", [1, 2, 4, 8, 16, 32])
+def test_decode_verify_and_diffusion_block_heights_accepted(rows):
+    assert cm.clover_moe_workspace_size(problem(block_rows=rows), 8) > 0
+
+
 def test_workspace_size_grows_with_rows_and_is_host_only():
     a = cm.clover_moe_workspace_size(problem(), 8)
     b = cm.clover_moe_workspace_size(problem(num_blocks=16), 8)
@@ -119,6 +124,8 @@ def test_invalid_calls_rejected(kw, expect):
     (dict(shared_inter=-128), 8, cm.CMOE_ERR_VALUE),
     (dict(shared_inter=100), 8, cm.CMOE_ERR_UNSUPPORTED),
     (dict(block_rows=24), 8, cm.CMOE_ERR_UNSUPPORTED),
+    (dict(block_rows=3), 8, cm.CMOE_ERR_UNSUPPORTED),
+    (dict(block_rows=64), 8, cm.CMOE_ERR_UNSUPPORTED),
     (dict(block_rows=0), 8, cm.CMOE_ERR_VALUE),
     (dict(num_blocks=0), 8, cm.CMOE_ERR_VALUE),
     (dict(num_blocks=2048), 8, cm.CMOE_ERR_UNSUPPORTED),

@@ -102,9 +102,30 @@ def test_threshold_on_a_prefix_sum_takes_the_serial_cut(tau, m):
     assert np.all(ref["coreset_size"] == m)
 
 
+# decode (one row per block) and verification (2-4 rows) calls: rows past R in
+# the routing kernel's row groups must add nothing to the block mass
+@pytest.mark.parametrize("wl,tau", [
+    (MID.with_(name="mid_rows1", block_rows=1, num_blocks=7, seed=71), 1.0),
+    (MID.with_(name="mid_rows1_tau", block_rows=1, num_blocks=7, seed=71), 0.9),
+    (MID.with_(name="mid_rows2", block_rows=2, num_blocks=5, seed=72), 0.9),
+    (MID.with_(name="mid_rows4", block_rows=4, num_blocks=3, seed=73), 1.0),
+    (MID.with_(name="mid_rows4_fp8", block_rows=4, num_blocks=2, weight_dtype=W.FP8, seed=74), 0.9),
+    (MID.with_(name="mid_rows1_f32", block_rows=1, num_blocks=3, act_dtype=W.F32, weight_dtype=W.F32,
+               seed=75), 1.0),
+    (FEW.with_(name="few_rows2_E256", block_rows=2, num_blocks=1, seed=76), 0.9),
+], ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_decode_and_verify_rows(wl, tau):
+    check(W.generate(wl), tau=tau)
+
+
 # ---------------------------------------------------------------------------
 # full-size workloads
 # ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["decode1_bf16", "verify4_bf16"])
+def test_decode_verify_full(name):
+    check(W.generate(W.WORKLOADS[name]), threads=16)
+
 
 @pytest.fixture(scope="module")
 def block32():

@@ -210,11 +210,12 @@ def _coreset_invariants(mass, tau, ids, m):
         assert cums[m - 2] < thr
 
 
-@pytest.mark.parametrize("tau", [0.9, 0.95, 0.8, 0.5, 1.0])
-def test_coreset_is_minimum_cardinality_set_by_brute_force(tau):
+@pytest.mark.parametrize("tau,rows", [(0.9, 8), (0.95, 8), (0.8, 8), (0.5, 8), (1.0, 8), (0.9, 1), (0.8, 2)])
+def test_coreset_is_minimum_cardinality_set_by_brute_force(tau, rows):
     """All 2^16 expert subsets at E = 16: no set smaller than the coreset carries
-    tau of the block's routing mass (exact rational sums)."""
-    inp = W.generate(W.WORKLOADS["tiny_fp32"].with_(bias_sigma=0.3))
+    tau of the block's routing mass (exact rational sums).  One- and two-row
+    blocks (decode and verify calls) included."""
+    inp = W.generate(W.WORKLOADS["tiny_fp32"].with_(bias_sigma=0.3, block_rows=rows))
     l = oracle.router_logits(inp)
     _, p = oracle.softmax(inp, l)
     mass = oracle.block_mass(inp, p)[0]
@@ -319,10 +320,12 @@ def test_topk_gates_counts_and_permutation(tau, k):
     assert np.all(r["perm"][valid.sum():] == -1)
 
 
-def test_full_route_equals_plain_topk_of_softmax():
-    """tau = 1.0 (full-route replay): the coreset is every expert and routing is
-    plain top-k of the softmax, renormalised (torch.topk on fp64 softmax)."""
-    wl = W.WORKLOADS["tiny_fp32"].with_(num_blocks=4)
+@pytest.mark.parametrize("rows,blocks", [(8, 4), (1, 5), (2, 3), (4, 3)])
+def test_full_route_equals_plain_topk_of_softmax(rows, blocks):
+    """tau = 1.0 (full-route replay, and the plain top-k of decode and verify
+    calls): the coreset is every expert and routing is plain top-k of the
+    softmax, renormalised (torch.topk on fp64 softmax)."""
+    wl = W.WORKLOADS["tiny_fp32"].with_(block_rows=rows, num_blocks=blocks)
     inp = W.generate(wl)
     r = oracle.forward(inp, tau=1.0, ffn=False)
     assert np.all(r["coreset_size"] == wl.num_experts)
@@ -400,11 +403,13 @@ def _numpy_shared(inp):
                    _dequant(inp.shared_w2, inp.shared_w2_scale, wd))
 
 
-@pytest.mark.parametrize("variant", ["fp32", "bf16", "fp8"])
+@pytest.mark.parametrize("variant", ["fp32", "bf16", "fp8", "rows1", "rows4"])
 def test_sparse_ffn_equals_dense_brute_force(variant):
     """Every expert on every row (numpy fp64 matmuls), combined through the
     dense [N,E] gate matrix that is zero off the route."""
     wl = W.WORKLOADS["tiny_fp32"].with_(num_blocks=2)
+    if variant in ("rows1", "rows4"):
+        wl = wl.with_(block_rows=int(variant[4:]), num_blocks=3)
     if variant == "bf16":
         wl = wl.with_(act_dtype=W.BF16, weight_dtype=W.BF16)
     if variant == "fp8":

@@ -44,7 +44,7 @@ class Workload:
     """Shape, dtypes and seed of one synthetic workload."""
     name: str
     num_blocks: int       # B
-    block_rows: int       # R_blk (8, 16 or 32)
+    block_rows: int       # R_blk (8, 16 or 32; 1, 2 or 4 for decode / verify calls)
     hidden: int           # H
     num_experts: int      # E
     top_k: int            # k
@@ -77,6 +77,10 @@ WORKLOADS: Dict[str, Workload] = {
     "blocks16_bf16": Workload("blocks16_bf16", 16, 32, 2048, 256, 8, 512, 512, BF16, BF16, 0.9, seed=3),
     # 64 blocks x 32 rows, fp8 e4m3 expert weights with fp32 128x128 block scales
     "blocks64_fp8": Workload("blocks64_fp8", 64, 32, 2048, 256, 8, 512, 512, BF16, FP8, 0.9, seed=4),
+    # autoregressive decode: one row per call, plain top-8 (threshold 1)
+    "decode1_bf16": Workload("decode1_bf16", 1, 1, 2048, 256, 8, 512, 512, BF16, BF16, 1.0, seed=5),
+    # verification of 4 drafted candidates in one call, plain top-8
+    "verify4_bf16": Workload("verify4_bf16", 1, 4, 2048, 256, 8, 512, 512, BF16, BF16, 1.0, seed=6),
 }
 
 # Threshold / top-k sweep run on the skewed workload (1.0 = unrestricted top-k;
