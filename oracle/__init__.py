@@ -67,7 +67,7 @@ def lib():
         L.orc_e4m3_to_double.argtypes = [ctypes.c_uint8]
         L.orc_router_logits.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int]
         L.orc_softmax.argtypes = [ctypes.c_void_p] * 4
-        L.orc_block_mass.argtypes = [ctypes.c_void_p] * 3
+        L.orc_block_mass.argtypes = [ctypes.c_void_p] * 4
         L.orc_coreset.restype = ctypes.c_int
         L.orc_coreset.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_void_p]
         L.orc_row_topk.restype = ctypes.c_int
@@ -78,6 +78,10 @@ def lib():
         L.orc_forward.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
                                   ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                   ctypes.c_int]
+        L.orc_forward_ex.restype = ctypes.c_int
+        L.orc_forward_ex.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         _lib = L
     return _lib
 
@@ -152,12 +156,14 @@ def softmax(inp, logits: np.ndarray):
     return u, pr
 
 
-def block_mass(inp, prob: np.ndarray) -> np.ndarray:
+def block_mass(inp, prob: np.ndarray, live: Optional[np.ndarray] = None) -> np.ndarray:
     wl = inp.wl
     prob = np.ascontiguousarray(prob, dtype=np.float64)
+    if live is not None:
+        live = np.ascontiguousarray(live, dtype=np.uint8)
     mass = np.zeros((wl.num_blocks, wl.num_experts), dtype=np.float64)
     p = _problem(inp)
-    lib().orc_block_mass(ctypes.byref(p), _ptr(prob), _ptr(mass))
+    lib().orc_block_mass(ctypes.byref(p), _ptr(prob), _ptr(live), _ptr(mass))
     return mass
 
 
@@ -192,13 +198,20 @@ def expert_ffn(hidden: int, inter: int, wdtype: str, w13, w13_scale, w2, w2_scal
 
 
 def forward(inp, tau: Optional[float] = None, top_k: Optional[int] = None,
-            rows: Optional[np.ndarray] = None, threads: int = 0, ffn: bool = True) -> dict:
+            rows: Optional[np.ndarray] = None, threads: int = 0, ffn: bool = True,
+            expert_budget: Optional[int] = None, live_rows: Optional[np.ndarray] = None) -> dict:
     """Whole call.  ``rows``: row indices whose FFN output is computed (None =
-    all).  Returns a dict with 'out' (fp64 [N,H], NaN for rows not computed)
-    and every routing array."""
+    all).  ``expert_budget`` and ``live_rows`` default to the workload's
+    (``inp.wl.expert_budget``, ``inp.live_rows``).  Returns a dict with 'out'
+    (fp64 [N,H], NaN for rows not computed and for resolved rows) and every
+    routing array."""
     wl = inp.wl
     tau = wl.mass_threshold if tau is None else tau
     K = wl.top_k if top_k is None else top_k
+    budget = wl.expert_budget if expert_budget is None else expert_budget
+    live = inp.live_rows if live_rows is None else live_rows
+    if live is not None:
+        live = np.ascontiguousarray(live, dtype=np.uint8)
     N, E, B, H = wl.rows, wl.num_experts, wl.num_blocks, wl.hidden
     res = {
         "topk_idx": np.zeros((N, K), np.int32), "gates": np.zeros((N, K), np.float32),
@@ -219,8 +232,9 @@ def forward(inp, tau: Optional[float] = None, top_k: Optional[int] = None,
             mask[np.asarray(rows)] = 1
     p = _problem(inp)
     w = _weights(inp)
-    rc = lib().orc_forward(ctypes.byref(p), ctypes.byref(w), _ptr(inp.x), ctypes.c_float(tau), K,
-                           _ptr(out), ctypes.byref(rt), _ptr(mask), threads)
+    rc = lib().orc_forward_ex(ctypes.byref(p), ctypes.byref(w), _ptr(inp.x), ctypes.c_float(tau), K,
+                              int(budget), _ptr(live), _ptr(out), ctypes.byref(rt), _ptr(mask),
+                              threads)
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (code {rc})")
     res["out"] = out

@@ -208,16 +208,18 @@ void orc_softmax(const orc_problem* p, const float* logits, double* u, double* p
 
 /* ------------------------------------------------------------------------ */
 /* 3. block routing mass: mass[b,e] = sum of p[r,e] over the block's rows,   */
-/* rows ascending, fp64.  Block b is rows [b*R, (b+1)*R).                    */
+/* rows ascending, fp64.  Block b is rows [b*R, (b+1)*R).  Only the rows     */
+/* evaluated in this pass count (live[r] != 0; NULL = all).                  */
 /* ------------------------------------------------------------------------ */
 
-void orc_block_mass(const orc_problem* p, const double* prob, double* mass)
+void orc_block_mass(const orc_problem* p, const double* prob, const uint8_t* live, double* mass)
 {
     const int E = p->num_experts, R = p->block_rows;
     for (int b = 0; b < p->num_blocks; ++b)
         for (int e = 0; e < E; ++e) {
             double acc = 0.0;
-            for (int r = b * R; r < (b + 1) * R; ++r) acc = acc + prob[(size_t)r * E + e];
+            for (int r = b * R; r < (b + 1) * R; ++r)
+                if (!live || live[r]) acc = acc + prob[(size_t)r * E + e];
             mass[(size_t)b * E + e] = acc;
         }
 }
@@ -337,11 +339,19 @@ int orc_forward(const orc_problem* p, const orc_weights* w, const void* x,
                 float tau, int top_k, double* out, orc_routing* rt,
                 const uint8_t* row_mask, int threads)
 {
+    return orc_forward_ex(p, w, x, tau, top_k, 0, NULL, out, rt, row_mask, threads);
+}
+
+int orc_forward_ex(const orc_problem* p, const orc_weights* w, const void* x,
+                   float tau, int top_k, int expert_budget, const uint8_t* live,
+                   double* out, orc_routing* rt, const uint8_t* row_mask, int threads)
+{
     const int H = p->hidden, E = p->num_experts, I = p->inter, Is = p->shared_inter;
     const int R = p->block_rows, B = p->num_blocks, N = R * B, K = top_k;
     if (H <= 0 || E <= 0 || I <= 0 || Is < 0 || R <= 0 || B <= 0) return 1;
     if (K < 1 || K > E) return 2;
     if (!(tau > 0.0f && tau <= 1.0f)) return 3;
+    if (expert_budget < 0 || expert_budget > E) return 5;
     if (p->weight_dtype == ORC_FP8_E4M3 &&
         (H % 128 || I % 128 || Is % 128 || !w->w13_scale || !w->w2_scale)) return 4;
 
@@ -358,19 +368,31 @@ int orc_forward(const orc_problem* p, const orc_weights* w, const void* x,
     /* 1-3 */
     orc_router_logits(p, x, w->router_w, w->router_b, logits, threads);
     orc_softmax(p, logits, u, prob);
-    orc_block_mass(p, prob, mass);
+    orc_block_mass(p, prob, live, mass);
 
-    /* 4-5, block by block */
+    /* 4-5, block by block: coreset, budget cut, top-k of the live rows */
     for (int b = 0; b < B; ++b) {
         int32_t* bid = ids + (size_t)b * E;
         int m = orc_coreset(mass + (size_t)b * E, E, tau, bid);
+        if (expert_budget > 0 && m > expert_budget) m = expert_budget;
+        int any_live = 0;
+        for (int r = b * R; r < (b + 1) * R; ++r) any_live |= !live || live[r];
+        if (!any_live) m = 0;
         csize[b] = m;
         for (int i = m; i < E; ++i) bid[i] = -1;
         memset(in_set, 0, (size_t)E);
         for (int i = 0; i < m; ++i) in_set[bid[i]] = 1;
-        for (int r = b * R; r < (b + 1) * R; ++r)
+        for (int r = b * R; r < (b + 1) * R; ++r) {
+            if (live && !live[r]) {
+                for (int j = 0; j < K; ++j) {
+                    idx[(size_t)r * K + j] = -1;
+                    gates[(size_t)r * K + j] = 0.0f;
+                }
+                continue;
+            }
             orc_row_topk(logits + (size_t)r * E, u + (size_t)r * E, in_set, E, K,
                          idx + (size_t)r * K, gates + (size_t)r * K);
+        }
     }
 
     /* 6. counts, offsets and the stable expert-major order of (row, slot) */
@@ -417,7 +439,7 @@ int orc_forward(const orc_problem* p, const orc_weights* w, const void* x,
 #pragma omp parallel for schedule(dynamic, 1)
 #endif
         for (int r = 0; r < N; ++r) {
-            if (row_mask && !row_mask[r]) continue;
+            if ((row_mask && !row_mask[r]) || (live && !live[r])) continue;
             double* xr = (double*)malloc(sizeof(double) * (size_t)H);
             double* y = (double*)malloc(sizeof(double) * (size_t)H);
             double* acc = out + (size_t)r * H;

@@ -85,8 +85,10 @@ void orc_router_logits(const orc_problem* p, const void* x, const float* router_
 /* u[N,E] = exp(l - max_row) and p[N,E] = u / Z_row (fp64). */
 void orc_softmax(const orc_problem* p, const float* logits, double* u, double* prob);
 
-/* mass[B,E] = sum over each block's rows (ascending) of prob. */
-void orc_block_mass(const orc_problem* p, const double* prob, double* mass);
+/* mass[B,E] = sum over each block's rows (ascending) of prob.  live[N]
+ * (NULL = every row) marks the rows evaluated in this pass; the others add
+ * nothing. */
+void orc_block_mass(const orc_problem* p, const double* prob, const uint8_t* live, double* mass);
 
 /* Coreset of one block: writes ids[0..m-1] (experts by mass desc, id asc),
  * returns m.  tau >= 1 selects all E experts. */
@@ -118,6 +120,19 @@ typedef struct {
 int orc_forward(const orc_problem* p, const orc_weights* w, const void* x,
                 float tau, int top_k, double* out, orc_routing* routing,
                 const uint8_t* row_mask, int threads);
+
+/* orc_forward with an expert budget and live rows (InfiniLM PR #604,
+ * "Summary" and "Motivation": expert-budget / live-row reuse, the live rows
+ * refreshed in full every few passes by the caller).
+ *  - expert_budget: 0 = none, else 1..E; a block's coreset is cut to its
+ *    first expert_budget experts (mass order) after the threshold cut.
+ *  - live_rows[N] (NULL = all live): a row with 0 is resolved and reuses its
+ *    cached output: it adds nothing to its block's mass, gets no route
+ *    (idx -1, gate 0) and its row of `out` is left untouched.  A block with
+ *    no live row has an empty coreset. */
+int orc_forward_ex(const orc_problem* p, const orc_weights* w, const void* x,
+                   float tau, int top_k, int expert_budget, const uint8_t* live_rows,
+                   double* out, orc_routing* routing, const uint8_t* row_mask, int threads);
 
 /* fp64 SwiGLU FFN of one expert weight set on one input row (widened to fp64):
  * y[H] = W2 * (silu(W13[0:I] x) * (W13[I:2I] x)).  wdtype as in orc_problem. */

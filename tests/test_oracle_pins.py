@@ -3,6 +3,7 @@ brute force -- never to the oracle itself.
 
 Every test here runs on the CPU.
 """
+import dataclasses
 import itertools
 import json
 import math
@@ -471,3 +472,82 @@ def test_oracle_rejects_bad_arguments():
             oracle.forward(inp, tau=tau, ffn=False)
     with pytest.raises(ValueError):
         oracle.forward(inp, top_k=17, ffn=False)
+
+
+# ----------------------------------------------------------------------------
+# expert budget and live rows (InfiniLM PR #604, "Summary"/"Motivation")
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("budget", [1, 3, 6])
+def test_budget_keeps_the_heaviest_experts_and_rows_rank_within_them(budget):
+    """The budget keeps the first `budget` experts of the unbudgeted coreset
+    (mass order); every row's slots are then a brute-force sort of its logits
+    over that set, (logit desc, id asc)."""
+    wl = W.WORKLOADS["tiny_fp32"].with_(num_blocks=2, bias_sigma=0.3)
+    inp = W.generate(wl)
+    free = oracle.forward(inp, ffn=False)
+    cut = oracle.forward(inp, ffn=False, expert_budget=budget)
+    R, K = wl.block_rows, wl.top_k
+    for b in range(wl.num_blocks):
+        m = min(free["coreset_size"][b], budget)
+        assert cut["coreset_size"][b] == m
+        keep = free["coreset_ids"][b][:m]
+        np.testing.assert_array_equal(cut["coreset_ids"][b][:m], keep)
+        assert np.all(cut["coreset_ids"][b][m:] == -1)
+        for r in range(b * R, (b + 1) * R):
+            ranked = sorted(keep, key=lambda e: (-float(cut["logits"][r, e]), e))[:K]
+            want = list(ranked) + [-1] * (K - len(ranked))
+            np.testing.assert_array_equal(cut["topk_idx"][r], want)
+            assert abs(float(cut["gates"][r].astype(np.float64).sum()) - 1.0) < K * 2.0 ** -24
+
+
+def test_budget_zero_or_all_experts_changes_nothing():
+    inp = W.generate(W.WORKLOADS["tiny_fp32"].with_(num_blocks=2, seed=7))
+    a = oracle.forward(inp)
+    for budget in (0, inp.wl.num_experts):
+        c = oracle.forward(inp, expert_budget=budget)
+        for k in ("topk_idx", "gates", "coreset_ids", "coreset_size"):
+            np.testing.assert_array_equal(a[k], c[k])
+        np.testing.assert_array_equal(a["out"], c["out"])
+
+
+def test_live_rows_route_like_a_block_made_of_them():
+    """A block whose live rows are L routes (and computes) those rows exactly as
+    a block consisting of the rows L alone: resolved rows add nothing to the
+    block's mass and take no slots."""
+    wl = W.WORKLOADS["tiny_fp32"].with_(seed=8)
+    inp = W.generate(wl)
+    L = np.array([1, 2, 5, 7])
+    live = np.zeros(wl.rows, np.uint8)
+    live[L] = 1
+    masked = oracle.forward(inp, live_rows=live)
+    alone = dataclasses.replace(inp, wl=wl.with_(block_rows=len(L)), x=np.ascontiguousarray(inp.x[L]))
+    ref = oracle.forward(alone)
+    for k in ("coreset_ids", "coreset_size", "block_mass"):
+        np.testing.assert_array_equal(masked[k], ref[k])
+    np.testing.assert_array_equal(masked["topk_idx"][L], ref["topk_idx"])
+    np.testing.assert_array_equal(masked["gates"][L], ref["gates"])
+    np.testing.assert_array_equal(masked["out"][L], ref["out"])
+
+
+def test_resolved_rows_take_no_route_and_keep_their_output():
+    wl = W.WORKLOADS["tiny_fp32"].with_(num_blocks=3, live_fraction=0.5, seed=9)
+    inp = W.generate(wl)
+    live = inp.live_rows.astype(bool)
+    assert 0 < live.sum() < wl.rows
+    r = oracle.forward(inp)
+    assert np.all(r["topk_idx"][~live] == -1) and np.all(r["gates"][~live] == 0)
+    assert np.all(np.isnan(r["out"][~live])) and not np.any(np.isnan(r["out"][live]))
+    assert r["expert_counts"].sum() == int((r["topk_idx"] >= 0).sum())
+    assert int((r["topk_idx"][live] >= 0).sum()) == live.sum() * wl.top_k
+
+
+def test_block_without_live_rows_has_an_empty_coreset():
+    wl = W.WORKLOADS["tiny_fp32"].with_(num_blocks=2, seed=10)
+    inp = W.generate(wl)
+    live = np.ones(wl.rows, np.uint8)
+    live[: wl.block_rows] = 0
+    r = oracle.forward(inp, live_rows=live)
+    assert r["coreset_size"][0] == 0 and np.all(r["coreset_ids"][0] == -1)
+    assert np.all(r["block_mass"][0] == 0) and r["coreset_size"][1] > 0
+    assert np.all(r["topk_idx"][: wl.block_rows] == -1)

@@ -20,7 +20,10 @@ ascending order its W13[e] and W2[e] are drawn after all W13 (i.e. all W13
 first, expert by expert, then all W2 expert by expert), then shared W13, shared
 W2.  Every draw is ``standard_normal(shape, float32) * sigma``; the router bias
 uses sigma = ``bias_sigma``.  Router weights are rounded to bf16 and stored as
-fp32 (bf16-valued) whenever activations are bf16.
+fp32 (bf16-valued) whenever activations are bf16.  Workloads with a
+``live_fraction`` below 1 also carry a live-row mask, drawn last from its own
+generator ``default_rng((seed, 0x11FE))``: row r is live when a uniform draw is
+below the fraction.
 """
 from __future__ import annotations
 
@@ -56,6 +59,8 @@ class Workload:
     seed: int
     sigma: float = 0.02
     bias_sigma: Optional[float] = None
+    expert_budget: int = 0        # 0 = none; else the cap on each block's coreset
+    live_fraction: float = 1.0    # < 1: that share of rows live, the rest resolved
 
     @property
     def rows(self) -> int:
@@ -108,6 +113,7 @@ class MoEInputs:
     shared_w13_scale: Optional[np.ndarray]
     shared_w2: Optional[np.ndarray]     # [H, Is]
     shared_w2_scale: Optional[np.ndarray]
+    live_rows: Optional[np.ndarray] = None  # [N] uint8, 1 = live (None: every row live)
 
 
 # ----------------------------------------------------------------------------
@@ -199,7 +205,11 @@ def generate(wl: Workload) -> MoEInputs:
         sw2, sw2_s = _store_weight(draw((H, Is), wl.sigma), wl.weight_dtype)
     else:
         sw13 = sw13_s = sw2 = sw2_s = None
-    return MoEInputs(wl, x, rw, rb, w13, w13_scale, w2, w2_scale, sw13, sw13_s, sw2, sw2_s)
+    live = None
+    if wl.live_fraction < 1.0:
+        # its own stream, so that the other draws do not depend on the mask
+        live = (np.random.default_rng((wl.seed, 0x11FE)).random(N) < wl.live_fraction).astype(np.uint8)
+    return MoEInputs(wl, x, rw, rb, w13, w13_scale, w2, w2_scale, sw13, sw13_s, sw2, sw2_s, live)
 
 
 def with_arrays(inp: MoEInputs, **kw) -> MoEInputs:
