@@ -156,9 +156,13 @@ def main():
 
     stream = torch.cuda.current_stream()
     x = dp.tensors["x"]
+    # expert budget / live rows: the _ex entry point with the workload's options
+    opts = None
+    if wl.expert_budget or dp.tensors.get("live_rows") is not None:
+        opts = cm.make_options(wl.expert_budget, dp.tensors.get("live_rows"))
     for i in range(args.warmup):
         cm.clover_moe_block_forward(dp.problem, layers[i % len(layers)], x, tau, K, out,
-                                    routings[i], ws, stream=stream)
+                                    routings[i], ws, stream=stream, options=opts)
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
@@ -168,7 +172,7 @@ def main():
     for s in range(args.steps):
         i = args.warmup + s
         cm.clover_moe_block_forward(dp.problem, layers[i % len(layers)], x, tau, K, out,
-                                    routings[i], ws, stream=stream)
+                                    routings[i], ws, stream=stream, options=opts)
     torch.cuda.synchronize()
     t_end = time.perf_counter()
     print(f"[bench] timed {args.steps} steps", file=sys.stderr, flush=True)
@@ -178,7 +182,7 @@ def main():
     for s in range(args.steps):
         i = args.warmup + s
         cm.clover_moe_block_forward_staged(dp.problem, layers[i % len(layers)], x, tau, K, out,
-                                           routings[i], ws, events[s], stream=stream)
+                                           routings[i], ws, events[s], stream=stream, options=opts)
     torch.cuda.synchronize()
     print(f"[bench] stage pass done", file=sys.stderr, flush=True)
 

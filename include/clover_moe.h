@@ -133,6 +133,28 @@ typedef struct {
     double* block_mass;      /* [B,E] routing mass of each expert in each block */
 } cmoe_routing;
 
+/* Options of one call (host struct; pass NULL for the defaults: no budget,
+ * every row live).  They follow the expert-budget / live-row reuse of
+ * InfiniLM PR #604 ("Summary"; "Motivation": live rows refreshed in full
+ * every five passes, which is the caller's schedule: a refresh pass passes
+ * live_rows = NULL).
+ *
+ *  expert_budget: 0 = none, else 1..E.  Each block's coreset is cut to its
+ *                 first expert_budget experts in (mass desc, id asc) order,
+ *                 after the threshold cut; coreset_size reports the cut size.
+ *  live_rows:     [N] uint8, device, 16-byte aligned, or NULL = every row
+ *                 live.  A row with 0 is resolved: it reuses the caller's
+ *                 cached output (its row of `out` is not written), adds
+ *                 nothing to its block's routing mass and takes no route
+ *                 (topk_idx -1, gates 0).  A block with no live row has an
+ *                 empty coreset (size 0, ids -1).  Its logits are still
+ *                 computed.
+ */
+typedef struct {
+    int32_t expert_budget;
+    const uint8_t* live_rows;
+} cmoe_options;
+
 /* Bytes of device workspace clover_moe_block_forward needs for this problem
  * and top_k.  Host-only; queues no work.  Writes *bytes on success. */
 cmoe_status clover_moe_workspace_size(const cmoe_problem* problem, int32_t top_k, size_t* bytes);
@@ -154,6 +176,15 @@ cmoe_status clover_moe_block_forward(const cmoe_problem* problem, const cmoe_wei
                                      void* out, const cmoe_routing* routing,
                                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* clover_moe_block_forward with options (see cmoe_options; NULL = none).
+ * Errors: expert_budget outside [0, E] is CMOE_ERR_VALUE; a live_rows range
+ * that is misaligned or overlaps an output is CMOE_ERR_ALIGN / CMOE_ERR_ALIAS. */
+cmoe_status clover_moe_block_forward_ex(const cmoe_problem* problem, const cmoe_weights* weights,
+                                        const void* x, float mass_threshold, int32_t top_k,
+                                        const cmoe_options* options, void* out,
+                                        const cmoe_routing* routing, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
 /* Number of kernel stages clover_moe_block_forward queues, in order:
  * 0 router logits, 1 per-block routing (softmax, mass, coreset, top-k, gates;
  * the last block also builds the row permutation and the GEMM work list),
@@ -161,7 +192,7 @@ cmoe_status clover_moe_block_forward(const cmoe_problem* problem, const cmoe_wei
  * shared expert. */
 #define CLOVER_MOE_NUM_STAGES 5
 
-/* Same operation as clover_moe_block_forward, for profiling: records
+/* Same operation as clover_moe_block_forward_ex, for profiling: records
  * stage_events[i] (i = 0..CLOVER_MOE_NUM_STAGES-1) on `stream` right before
  * stage i is queued and stage_events[CLOVER_MOE_NUM_STAGES] after the last
  * one.  stage_events points to n_events = CLOVER_MOE_NUM_STAGES + 1 host
@@ -170,7 +201,8 @@ cmoe_status clover_moe_block_forward(const cmoe_problem* problem, const cmoe_wei
  * of stage i. */
 cmoe_status clover_moe_block_forward_staged(const cmoe_problem* problem, const cmoe_weights* weights,
                                             const void* x, float mass_threshold, int32_t top_k,
-                                            void* out, const cmoe_routing* routing,
+                                            const cmoe_options* options, void* out,
+                                            const cmoe_routing* routing,
                                             void* workspace, size_t workspace_bytes, void* stream,
                                             void* const* stage_events, int32_t n_events);
 

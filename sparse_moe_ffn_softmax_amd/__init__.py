@@ -21,7 +21,7 @@ CMOE_ERR_ALIGN, CMOE_ERR_ALIAS, CMOE_ERR_WORKSPACE, CMOE_ERR_HIP = 4, 5, 6, 7
 CMOE_F32, CMOE_BF16, CMOE_FP8_E4M3 = 0, 1, 2
 DTYPE_CODES = {"f32": CMOE_F32, "bf16": CMOE_BF16, "fp8_e4m3": CMOE_FP8_E4M3}
 
-EXPORTED = ("clover_moe_workspace_size", "clover_moe_block_forward",
+EXPORTED = ("clover_moe_workspace_size", "clover_moe_block_forward", "clover_moe_block_forward_ex",
             "clover_moe_block_forward_staged", "clover_moe_status_string", "clover_moe_last_error")
 NUM_STAGES = 5
 STAGE_NAMES = ("router", "route_blocks", "expert_up", "expert_down", "combine")
@@ -43,6 +43,10 @@ class cmoe_routing(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("topk_idx", "gates", "coreset_ids", "coreset_size", "expert_counts",
                  "expert_offsets", "perm", "logits", "block_mass")]
+
+
+class cmoe_options(ctypes.Structure):
+    _fields_ = [("expert_budget", ctypes.c_int32), ("live_rows", ctypes.c_void_p)]
 
 
 class ClovermoeError(RuntimeError):
@@ -70,9 +74,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         ctypes.POINTER(cmoe_problem), ctypes.POINTER(cmoe_weights), ctypes.c_void_p, ctypes.c_float,
         ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(cmoe_routing), ctypes.c_void_p,
         ctypes.c_size_t, ctypes.c_void_p]
+    ex_args = [ctypes.POINTER(cmoe_problem), ctypes.POINTER(cmoe_weights), ctypes.c_void_p, ctypes.c_float,
+               ctypes.c_int32, ctypes.POINTER(cmoe_options), ctypes.c_void_p, ctypes.POINTER(cmoe_routing),
+               ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.clover_moe_block_forward_ex.restype = ctypes.c_int
+    L.clover_moe_block_forward_ex.argtypes = ex_args
     L.clover_moe_block_forward_staged.restype = ctypes.c_int
-    L.clover_moe_block_forward_staged.argtypes = L.clover_moe_block_forward.argtypes + [
-        ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]
+    L.clover_moe_block_forward_staged.argtypes = ex_args + [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]
     L.clover_moe_status_string.restype = ctypes.c_char_p
     L.clover_moe_status_string.argtypes = [ctypes.c_int]
     L.clover_moe_last_error.restype = ctypes.c_char_p
@@ -110,10 +118,12 @@ def _ptr(t) -> Optional[int]:
 
 def clover_moe_block_forward(problem: cmoe_problem, weights: cmoe_weights, x, mass_threshold: float,
                              top_k: int, out, routing: Optional[cmoe_routing], workspace,
-                             workspace_bytes: Optional[int] = None, stream=None) -> None:
+                             workspace_bytes: Optional[int] = None, stream=None,
+                             options: Optional[cmoe_options] = None) -> None:
     """Queue one call on `stream` (a torch.cuda.Stream, a raw hipStream_t int,
     or None for torch's current stream).  x, out, workspace: torch tensors or
-    raw device pointers."""
+    raw device pointers.  With `options` the call goes through
+    clover_moe_block_forward_ex."""
     import torch
     if stream is None:
         stream = torch.cuda.current_stream().cuda_stream
@@ -122,15 +132,21 @@ def clover_moe_block_forward(problem: cmoe_problem, weights: cmoe_weights, x, ma
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size()
     rt = ctypes.byref(routing) if routing is not None else None
-    _check(load_library().clover_moe_block_forward(
-        ctypes.byref(problem), ctypes.byref(weights), _ptr(x), ctypes.c_float(mass_threshold),
-        top_k, _ptr(out), rt, _ptr(workspace), workspace_bytes, stream))
+    if options is None:
+        _check(load_library().clover_moe_block_forward(
+            ctypes.byref(problem), ctypes.byref(weights), _ptr(x), ctypes.c_float(mass_threshold),
+            top_k, _ptr(out), rt, _ptr(workspace), workspace_bytes, stream))
+    else:
+        _check(load_library().clover_moe_block_forward_ex(
+            ctypes.byref(problem), ctypes.byref(weights), _ptr(x), ctypes.c_float(mass_threshold),
+            top_k, ctypes.byref(options), _ptr(out), rt, _ptr(workspace), workspace_bytes, stream))
 
 
 def clover_moe_block_forward_staged(problem: cmoe_problem, weights: cmoe_weights, x,
                                     mass_threshold: float, top_k: int, out,
                                     routing: Optional[cmoe_routing], workspace, stage_events,
-                                    workspace_bytes: Optional[int] = None, stream=None) -> None:
+                                    workspace_bytes: Optional[int] = None, stream=None,
+                                    options: Optional[cmoe_options] = None) -> None:
     """As clover_moe_block_forward, recording the NUM_STAGES + 1 raw hipEvent_t
     handles in `stage_events` (ints) around the stages."""
     import torch
@@ -142,9 +158,10 @@ def clover_moe_block_forward_staged(problem: cmoe_problem, weights: cmoe_weights
         workspace_bytes = workspace.numel() * workspace.element_size()
     ev = (ctypes.c_void_p * len(stage_events))(*stage_events)
     rt = ctypes.byref(routing) if routing is not None else None
+    opt = ctypes.byref(options) if options is not None else None
     _check(load_library().clover_moe_block_forward_staged(
         ctypes.byref(problem), ctypes.byref(weights), _ptr(x), ctypes.c_float(mass_threshold),
-        top_k, _ptr(out), rt, _ptr(workspace), workspace_bytes, stream, ev, len(stage_events)))
+        top_k, opt, _ptr(out), rt, _ptr(workspace), workspace_bytes, stream, ev, len(stage_events)))
 
 
 # ---------------------------------------------------------------------------
@@ -163,6 +180,11 @@ def make_weights(router_w, w13, w2, router_b=None, w13_scale=None, w2_scale=None
     return cmoe_weights(_ptr(router_w), _ptr(router_b), _ptr(w13), _ptr(w13_scale), _ptr(w2),
                         _ptr(w2_scale), _ptr(shared_w13), _ptr(shared_w13_scale), _ptr(shared_w2),
                         _ptr(shared_w2_scale))
+
+
+def make_options(expert_budget: int = 0, live_rows=None) -> cmoe_options:
+    """live_rows: a [N] uint8 device tensor (1 = live) or None."""
+    return cmoe_options(int(expert_budget), _ptr(live_rows))
 
 
 def make_routing(**tensors) -> cmoe_routing:
@@ -202,6 +224,8 @@ def upload(inp, device="cuda") -> DeviceProblem:
     names = ("x", "router_w", "router_b", "w13", "w13_scale", "w2", "w2_scale", "shared_w13",
              "shared_w13_scale", "shared_w2", "shared_w2_scale")
     ts = {n: dev(getattr(inp, n)) for n in names}
+    live = getattr(inp, "live_rows", None)
+    ts["live_rows"] = None if live is None else torch.from_numpy(np.ascontiguousarray(live, np.uint8)).to(device)
     prob = make_problem(wl.hidden, wl.num_experts, wl.inter, wl.shared_inter, wl.block_rows,
                         wl.num_blocks, wl.act_dtype, wl.weight_dtype)
     w = make_weights(ts["router_w"], ts["w13"], ts["w2"], ts["router_b"], ts["w13_scale"],
@@ -216,8 +240,9 @@ def alloc_workspace(problem: cmoe_problem, top_k: int, device="cuda"):
     return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 
 
-def alloc_routing(problem: cmoe_problem, top_k: int, device="cuda"):
-    """Device tensors for every optional routing output, plus the struct."""
+def alloc_routing(problem: cmoe_problem, top_k: int, device="cuda", names=None):
+    """Device tensors for the optional routing outputs (all, or those named),
+    plus the struct."""
     import torch
     N = problem.block_rows * problem.num_blocks
     E, B = problem.num_experts, problem.num_blocks
@@ -233,4 +258,6 @@ def alloc_routing(problem: cmoe_problem, top_k: int, device="cuda"):
         "logits": torch.empty((N, E), dtype=f32, device=device),
         "block_mass": torch.empty((B, E), dtype=torch.float64, device=device),
     }
+    if names is not None:
+        t = {k: v for k, v in t.items() if k in names}
     return t, make_routing(**t)

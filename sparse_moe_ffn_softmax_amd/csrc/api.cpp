@@ -156,6 +156,8 @@ void carve(Plan& p, const cmoe_problem& pr, int K, void* ws, const cmoe_routing*
   p.K = K;
   p.act = pr.act_dtype;
   p.wt = pr.weight_dtype;
+  p.live = nullptr;
+  p.budget = 0;
   p.max_tiles = L.max_tiles;
   p.mt_max = L.mt_max;
   p.tile_rows = 16 * L.mt_max;
@@ -194,7 +196,8 @@ cmoe_status clover_moe_workspace_size(const cmoe_problem* problem, int32_t top_k
 }
 
 static cmoe_status forward_impl(const cmoe_problem* problem, const cmoe_weights* w,
-                                const void* x, float mass_threshold, int32_t top_k, void* out,
+                                const void* x, float mass_threshold, int32_t top_k,
+                                const cmoe_options* options, void* out,
                                 const cmoe_routing* routing, void* workspace,
                                 size_t workspace_bytes, void* stream, void* const* events,
                                 int32_t n_events) {
@@ -215,6 +218,11 @@ static cmoe_status forward_impl(const cmoe_problem* problem, const cmoe_weights*
     return fail(CMOE_ERR_NULL, "fp8 weights need every 128x128 block-scale array");
   if (!(mass_threshold > 0.0f && mass_threshold <= 1.0f))
     return fail(CMOE_ERR_VALUE, "mass_threshold=%g must be in (0, 1]", (double)mass_threshold);
+  const int budget = options ? options->expert_budget : 0;
+  const uint8_t* live = options ? options->live_rows : nullptr;
+  if (budget < 0 || budget > p.num_experts)
+    return fail(CMOE_ERR_VALUE, "expert_budget=%d must be in [0, num_experts=%d]", budget,
+                p.num_experts);
 
   const size_t need = cmoe::workspace_bytes(p, top_k);
   if (!workspace || workspace_bytes < need)
@@ -233,6 +241,7 @@ static cmoe_status forward_impl(const cmoe_problem* problem, const cmoe_weights*
       {"w2", (uintptr_t)w->w2, E * H * I * wsz, false},
       {"shared_w13", Is ? (uintptr_t)w->shared_w13 : 0, 2 * Is * H * wsz, false},
       {"shared_w2", Is ? (uintptr_t)w->shared_w2 : 0, H * Is * wsz, false},
+      {"live_rows", (uintptr_t)live, N, false},
       {"out", (uintptr_t)out, N * H * asz, true},
       {"workspace", (uintptr_t)workspace, need, true},
   };
@@ -272,6 +281,8 @@ static cmoe_status forward_impl(const cmoe_problem* problem, const cmoe_weights*
 
   cmoe::Plan plan;
   cmoe::carve(plan, p, top_k, workspace, routing);
+  plan.live = live;
+  plan.budget = budget;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   for (int stage = 0; stage <= CLOVER_MOE_NUM_STAGES && e == hipSuccess; ++stage) {
@@ -305,17 +316,27 @@ cmoe_status clover_moe_block_forward(const cmoe_problem* problem, const cmoe_wei
                                      const void* x, float mass_threshold, int32_t top_k, void* out,
                                      const cmoe_routing* routing, void* workspace,
                                      size_t workspace_bytes, void* stream) {
-  return forward_impl(problem, w, x, mass_threshold, top_k, out, routing, workspace,
+  return forward_impl(problem, w, x, mass_threshold, top_k, nullptr, out, routing, workspace,
+                      workspace_bytes, stream, nullptr, 0);
+}
+
+cmoe_status clover_moe_block_forward_ex(const cmoe_problem* problem, const cmoe_weights* w,
+                                        const void* x, float mass_threshold, int32_t top_k,
+                                        const cmoe_options* options, void* out,
+                                        const cmoe_routing* routing, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  return forward_impl(problem, w, x, mass_threshold, top_k, options, out, routing, workspace,
                       workspace_bytes, stream, nullptr, 0);
 }
 
 cmoe_status clover_moe_block_forward_staged(const cmoe_problem* problem, const cmoe_weights* w,
                                             const void* x, float mass_threshold, int32_t top_k,
-                                            void* out, const cmoe_routing* routing,
-                                            void* workspace, size_t workspace_bytes, void* stream,
+                                            const cmoe_options* options, void* out,
+                                            const cmoe_routing* routing, void* workspace,
+                                            size_t workspace_bytes, void* stream,
                                             void* const* stage_events, int32_t n_events) {
   if (!stage_events) return fail(CMOE_ERR_NULL, "stage_events is NULL");
-  return forward_impl(problem, w, x, mass_threshold, top_k, out, routing, workspace,
+  return forward_impl(problem, w, x, mass_threshold, top_k, options, out, routing, workspace,
                       workspace_bytes, stream, stage_events, n_events);
 }
 

@@ -51,6 +51,8 @@ struct Plan {
   void* h;               // routed [N*K, I] then shared [N, Is]; act_dtype elements
   void* y;               // [N*K + N][H]: routed pairs, then shared rows
   int y_act;             // y stored in act_dtype (else fp32), see carve()
+  const uint8_t* live;   // [N] live-row mask, or nullptr (every row live)
+  int budget;            // coreset cap per block, 0 = none
   // optional caller outputs
   int32_t* coreset_ids;
   int32_t* coreset_size;

@@ -41,10 +41,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
                                                       const int32_t* __restrict__ pair_pos,
                                                       const float* __restrict__ gates,
                                                       OT* __restrict__ out, int N, int H, int K,
-                                                      int has_shared) {
+                                                      int has_shared,
+                                                      const uint8_t* __restrict__ live) {
   const int r = blockIdx.y;
   const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (c >= H) return;
+  if (live && !live[r]) return;  // a resolved row keeps the caller's cached output
   // every load is issued before the first add: positions and gates, then the
   // shared row and the routed rows (K <= 8)
   int pos[8];
@@ -76,13 +78,13 @@ hipError_t launch_combine(const Plan& p, void* out, hipStream_t s) {
     uint16_t* o = static_cast<uint16_t*>(out);
     if (p.y_act)
       combine_kernel<uint16_t, uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(p.y), p.pair_pos,
-                                                              p.gates, o, p.N, p.H, p.K, sh);
+                                                              p.gates, o, p.N, p.H, p.K, sh, p.live);
     else
       combine_kernel<uint16_t, float><<<grid, 256, 0, s>>>(static_cast<const float*>(p.y), p.pair_pos,
-                                                           p.gates, o, p.N, p.H, p.K, sh);
+                                                           p.gates, o, p.N, p.H, p.K, sh, p.live);
   } else {
     combine_kernel<float, float><<<grid, 256, 0, s>>>(static_cast<const float*>(p.y), p.pair_pos, p.gates,
-                                                      static_cast<float*>(out), p.N, p.H, p.K, sh);
+                                                      static_cast<float*>(out), p.N, p.H, p.K, sh, p.live);
   }
   return hipGetLastError();
 }

@@ -252,6 +252,7 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
   __shared__ int tk_s[kMaxRows * 8];          // this block's top-k
   __shared__ int pick_s[kMaxRows * 8];        // expert taken by each (row, slot)
   __shared__ int m_sh;
+  __shared__ uint32_t live_s;  // bit r: row r of the block is live
   __shared__ PermuteLds perm_lds;
 
   const int tid = threadIdx.x;
@@ -262,12 +263,22 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
 
   if (tid == 0) m_sh = E;
   if (tid < kMaxExperts) mask1_s[tid] = 0u;
+  // live rows: all rows of the block unless the call passes a mask; a
+  // resolved row adds nothing to the mass and takes no route
+  const uint8_t* live = plan.live ? plan.live + (size_t)b * R : nullptr;
+  auto row_live = [&](int r) { return r < R && (live == nullptr || live[r] != 0); };
+  if (wave == 0) {
+    const uint64_t lb64 = __ballot(row_live(lane));
+    if (lane == 0) live_s = static_cast<uint32_t>(lb64);
+  }
 
-  // The softmax, block mass and coreset are needed below a threshold of 1 and
-  // for the block-mass and coreset outputs.  A full-route call without them
-  // (decode, verification) needs only the row maxima, the top-k of the logits
-  // and the gates, whose u values are recomputed for the chosen experts.
-  const bool need_mass = tau < 1.0f || block_mass != nullptr || coreset_ids != nullptr;
+  // The softmax, block mass and coreset are needed below a threshold of 1, for
+  // an expert budget (a cut in mass order) and for the block-mass and coreset
+  // outputs.  A full-route call without them (decode, verification) needs
+  // only the row maxima, the top-k of the logits and the gates, whose u
+  // values are recomputed for the chosen experts.
+  const bool need_mass = tau < 1.0f || (plan.budget > 0 && plan.budget < E) || block_mass != nullptr ||
+                         coreset_ids != nullptr;
 
   // rows w and w+16 on wave w: logits to LDS, row maxima (exact, order-free),
   // and u = exp(l - max) as 8 independent chains per lane (4 when only the
@@ -291,7 +302,8 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
       mx[h] = wave_max_f32(mm);
       if (lane == 0) m_s[r] = mx[h];
     }
-    if (need_mass && wave + 16 < R) {
+    const bool u0 = need_mass && row_live(wave), u1 = need_mass && row_live(wave + 16);
+    if (u0 && u1) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -299,11 +311,17 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
           const int r = wave + 16 * h, e = lane + 64 * s;
           p_s[pidx(r, e)] = exp_reduced(static_cast<double>(lv[h][s]) - static_cast<double>(mx[h]));
         }
-    } else if (need_mass && wave < R) {
+    } else if (u0) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int e = lane + 64 * s;
         p_s[pidx(wave, e)] = exp_reduced(static_cast<double>(lv[0][s]) - static_cast<double>(mx[0]));
+      }
+    } else if (u1) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int e = lane + 64 * s;
+        p_s[pidx(wave + 16, e)] = exp_reduced(static_cast<double>(lv[1][s]) - static_cast<double>(mx[1]));
       }
     }
   }
@@ -312,12 +330,13 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
   if (need_mass) {
 
     // Z: chunk partial sums, one thread per (row, chunk), then the fixed tree
+    // (live rows; the others have no u)
     if (tid < kMaxRows * 8) {
       const int r = tid >> 3, j = tid & 7;
-      if (r < R) {
+      if ((live_s >> r) & 1u) {
         const int lo = (j * E) / 8, hi = ((j + 1) * E) / 8;
         double acc = 0.0;
-  #pragma unroll 8
+#pragma unroll 8
         for (int e = lo; e < hi; ++e) acc = acc + p_s[pidx(r, e)];
         zpart[r][j] = acc;
       }
@@ -325,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
     __syncthreads();
     if (tid < R) {
       double p[8];
-  #pragma unroll
+#pragma unroll
       for (int j = 0; j < 8; ++j) p[j] = zpart[tid][j];
       p[0] = p[0] + p[4];
       p[1] = p[1] + p[5];
@@ -339,17 +358,17 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
 
     // block mass, one thread per expert: p = u / Z for each row, summed over
     // rows ascending (the 8 divisions of a group are independent, only the adds
-    // are chained; rows past R, in blocks of 1, 2 or 4 rows, hold no values and
-    // add nothing)
+    // are chained); only live rows add: rows past R (blocks of 1, 2 or 4 rows)
+    // and resolved rows have no u
     if (tid < E) {
       double acc = 0.0;
       for (int r0 = 0; r0 < R; r0 += 8) {
         double q[8];
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 8; ++i) q[i] = p_s[pidx(r0 + i, tid)] / z_s[r0 + i];
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 8; ++i)
-          if (r0 + i < R) acc = acc + q[i];
+          if ((live_s >> (r0 + i)) & 1u) acc = acc + q[i];
       }
       mass_s[tid] = acc;
     }
@@ -383,7 +402,7 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
           me.m = static_cast<uint64_t>(__double_as_longlong(mass_s[e]));
           me.nid = ~static_cast<uint32_t>(e);
           cnt = 0;
-  #pragma unroll
+#pragma unroll
           for (int step = 32; step > 0; step >>= 1)
             if (beats(run_s[q][cnt + step - 1], me)) cnt += step;
           // the steps reach index 62 at most: all 64 beating e ends at 63
@@ -408,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
       double v = 0.0;
       if (tid < kMaxExperts) {
         v = tid < E ? smass_s[tid] : 0.0;
-  #pragma unroll
+#pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
           const double o = __shfl_up(v, d, 64);
           if (lane >= d) v = v + o;
@@ -441,20 +460,20 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
         if (tid == 0) {
           double c = 0.0;
           double x[16], nxt[16];
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < 16; ++i) x[i] = smass_s[i];
           for (int i0s = 0; i0s < E; i0s += 16) {
             const int n0 = min(i0s + 16, kMaxExperts - 16);
-  #pragma unroll
+#pragma unroll
             for (int i = 0; i < 16; ++i) nxt[i] = smass_s[n0 + i];
-  #pragma unroll
+#pragma unroll
             for (int i = 0; i < 16; ++i) {
               c = c + x[i];
               x[i] = c;
             }
-  #pragma unroll
+#pragma unroll
             for (int i = 0; i < 16; ++i) cum_s[i0s + i] = x[i];
-  #pragma unroll
+#pragma unroll
             for (int i = 0; i < 16; ++i) x[i] = nxt[i];
           }
         }
@@ -468,7 +487,8 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
     }
     __syncthreads();
   }  // need_mass
-  const int m = m_sh;
+  // no live row: an empty coreset; else the threshold cut, then the budget
+  const int m = live_s == 0u ? 0 : plan.budget > 0 ? min(m_sh, plan.budget) : m_sh;
 
   if (coreset_ids && tid < E) coreset_ids[(size_t)b * E + tid] = tid < m ? order_s[tid] : -1;
   if (coreset_size && tid == 0) coreset_size[b] = m;
@@ -483,7 +503,7 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
   if (2 * wave < R) {
     const int half = lane >> 5, hl = lane & 31;
     const int r = 2 * wave + half;
-    const bool row_ok = r < R;
+    const bool row_ok = (live_s >> r) & 1u;
     uint64_t key[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -530,7 +550,7 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
     double U = 0.0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) U = U + u_s[r * 8 + j];
-    if (row_ok && hl < K) {
+    if (r < R && hl < K) {  // resolved rows too: their slots are -1 / 0
       const int row = b * R + r;
       const bool ok = hl < k_eff;
       const int e_out = ok ? my_e : -1;

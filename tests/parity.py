@@ -29,16 +29,28 @@ TOL = {
 }
 
 
-def run_gpu(inp, tau: float, top_k: int, dp=None, workspace=None):
-    """One call through the C ABI; returns (out as fp64 numpy, routing dict)."""
+# value `out` is filled with before a call: rows the call must not write
+# (resolved rows) still hold it afterwards; exact in bf16 and fp32
+SENTINEL = 768.0
+
+
+def run_gpu(inp, tau: float, top_k: int, dp=None, workspace=None, outputs=None):
+    """One call through the C ABI; returns (out as fp64 numpy, routing dict).
+    Workloads with an expert budget or live rows go through the _ex entry
+    point with those options.  `outputs`: the routing outputs requested
+    (None = all)."""
     import torch
     wl = inp.wl
     dp = dp or cm.upload(inp)
     ws = workspace if workspace is not None else cm.alloc_workspace(dp.problem, top_k)
-    rt_t, rt = cm.alloc_routing(dp.problem, top_k)
+    rt_t, rt = cm.alloc_routing(dp.problem, top_k, names=outputs)
     odt = torch.bfloat16 if wl.act_dtype == W.BF16 else torch.float32
-    out = torch.empty((wl.rows, wl.hidden), dtype=odt, device="cuda")
-    cm.clover_moe_block_forward(dp.problem, dp.weights, dp.tensors["x"], tau, top_k, out, rt, ws)
+    out = torch.full((wl.rows, wl.hidden), SENTINEL, dtype=odt, device="cuda")
+    opts = None
+    if wl.expert_budget or dp.tensors.get("live_rows") is not None:
+        opts = cm.make_options(wl.expert_budget, dp.tensors.get("live_rows"))
+    cm.clover_moe_block_forward(dp.problem, dp.weights, dp.tensors["x"], tau, top_k, out, rt, ws,
+                                options=opts)
     torch.cuda.synchronize()
     res = {k: v.cpu().numpy() for k, v in rt_t.items()}
     return out.double().cpu().numpy(), res
@@ -55,6 +67,8 @@ def bits(a: np.ndarray) -> np.ndarray:
 
 def assert_routing_equal(gpu: dict, ref: dict):
     for k in ROUTING_KEYS:
+        if k not in gpu:
+            continue
         g, r = bits(gpu[k]), bits(ref[k])
         assert g.shape == r.shape, (k, g.shape, r.shape)
         if not np.array_equal(g, r):
@@ -79,16 +93,25 @@ def assert_ffn_close(out, ref, weight_dtype, rows=None):
     return mx, mean
 
 
-def check(inp, tau=None, top_k=None, rows=None, threads=0, dp=None):
-    """Full parity check of one call; returns (max_rel, mean_rel, oracle result)."""
+def check(inp, tau=None, top_k=None, rows=None, threads=0, dp=None, outputs=None):
+    """Full parity check of one call; returns (max_rel, mean_rel, oracle result).
+    `outputs`: the routing outputs the call requests (None = all)."""
     wl = inp.wl
     tau = wl.mass_threshold if tau is None else tau
     top_k = wl.top_k if top_k is None else top_k
     print(f"[parity] {wl.name} B={wl.num_blocks} R={wl.block_rows} H={wl.hidden} E={wl.num_experts} "
           f"I={wl.inter} Is={wl.shared_inter} {wl.act_dtype}/{wl.weight_dtype} tau={tau} k={top_k}",
           flush=True)
-    out, gpu = run_gpu(inp, tau, top_k, dp=dp)
+    out, gpu = run_gpu(inp, tau, top_k, dp=dp, outputs=outputs)
     ref = oracle.forward(inp, tau=tau, top_k=top_k, rows=rows, threads=threads)
     assert_routing_equal(gpu, ref)
+    if inp.live_rows is not None:
+        # resolved rows keep the caller's cached output; compare the live ones
+        live = inp.live_rows.astype(bool)
+        assert np.all(out[~live] == SENTINEL), "a resolved row of out was written"
+        sel = np.flatnonzero(live)
+        rows = sel if rows is None else np.intersect1d(np.asarray(rows), sel)
+        if rows.size == 0:
+            return 0.0, 0.0, ref
     mx, mean = assert_ffn_close(out, ref["out"], wl.weight_dtype, rows)
     return mx, mean, ref

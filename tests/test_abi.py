@@ -152,6 +152,27 @@ def test_missing_weights_rejected():
     assert call(w=weights(router_b=fake(13, 4))) == cm.CMOE_ERR_ALIGN
 
 
+def call_ex(opts, **kw):
+    prob = problem()
+    k = 8
+    lib = cm.load_library()
+    return lib.clover_moe_block_forward_ex(ctypes.byref(prob), ctypes.byref(weights()), fake(10),
+                                           ctypes.c_float(0.9), k, ctypes.byref(opts), fake(11), None,
+                                           fake(12), cm.clover_moe_workspace_size(prob, k), None)
+
+
+@pytest.mark.parametrize("opts,expect", [
+    (dict(expert_budget=-1), cm.CMOE_ERR_VALUE),
+    (dict(expert_budget=257), cm.CMOE_ERR_VALUE),
+    (dict(expert_budget=64, live_rows=fake(13, 3)), cm.CMOE_ERR_ALIGN),
+    (dict(live_rows=fake(11) + 32), cm.CMOE_ERR_ALIAS),        # inside out
+    (dict(live_rows=fake(12)), cm.CMOE_ERR_ALIAS),             # the workspace
+])
+def test_invalid_options_rejected(opts, expect):
+    assert call_ex(cm.cmoe_options(opts.get("expert_budget", 0), opts.get("live_rows"))) == expect
+    assert cm.clover_moe_last_error()
+
+
 def test_routing_outputs_checked_for_alias_and_alignment():
     r = cm.make_routing(topk_idx=fake(20), gates=fake(21), logits=fake(1))   # logits on router_w
     assert call(routing=r) == cm.CMOE_ERR_ALIAS

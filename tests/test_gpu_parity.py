@@ -118,11 +118,50 @@ def test_decode_and_verify_rows(wl, tau):
     check(W.generate(wl), tau=tau)
 
 
+# expert budget and live rows: resolved rows keep their cached output (the
+# sentinel `out` is filled with), add nothing to the mass and take no route
+@pytest.mark.parametrize("wl,tau", [
+    (MID.with_(name="mid_budget8", expert_budget=8, seed=81), 0.9),
+    (MID.with_(name="mid_budget1", expert_budget=1, seed=82), 0.9),
+    (MID.with_(name="mid_budget5_tau1", expert_budget=5, seed=83), 1.0),
+    (MID.with_(name="mid_live50", live_fraction=0.5, seed=84), 0.9),
+    (MID.with_(name="mid_live50_budget6", live_fraction=0.5, expert_budget=6, seed=85), 0.9),
+    (MID.with_(name="mid_live30_fp8", live_fraction=0.3, weight_dtype=W.FP8, seed=86), 0.9),
+    (MID.with_(name="mid_rows4_live50", block_rows=4, num_blocks=6, live_fraction=0.5, seed=87), 1.0),
+    (MID.with_(name="mid_f32_live50", act_dtype=W.F32, weight_dtype=W.F32, live_fraction=0.5, seed=89), 0.9),
+    (FEW.with_(name="few_live50_budget32", live_fraction=0.5, expert_budget=32, seed=88), 0.9),
+], ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_budget_and_live_rows(wl, tau):
+    check(W.generate(wl), tau=tau)
+
+
+def test_block_without_live_rows():
+    wl = MID.with_(name="mid_dead_block", seed=90)
+    inp = W.generate(wl)
+    live = np.ones(wl.rows, np.uint8)
+    live[: wl.block_rows] = 0
+    live[2 * wl.block_rows + 3] = 0
+    _, _, ref = check(W.with_arrays(inp, live_rows=live))
+    assert ref["coreset_size"][0] == 0 and ref["coreset_size"][1] > 0
+
+
+@pytest.mark.parametrize("wl", [
+    W.WORKLOADS["decode1_bf16"],
+    MID.with_(name="mid_live50_tau1", live_fraction=0.5, mass_threshold=1.0, seed=91),
+    MID.with_(name="mid_rows2_tau1", block_rows=2, num_blocks=5, mass_threshold=1.0, seed=92),
+], ids=lambda w: w.name)
+def test_full_route_without_mass_outputs(wl):
+    """Threshold 1 with neither block_mass nor coreset_ids requested: the
+    routing kernel runs only the row maxima, top-k and gates."""
+    check(W.generate(wl), tau=1.0, outputs=("topk_idx", "gates", "coreset_size", "expert_counts",
+                                            "expert_offsets", "perm", "logits"))
+
+
 # ---------------------------------------------------------------------------
 # full-size workloads
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["decode1_bf16", "verify4_bf16"])
+@pytest.mark.parametrize("name", ["decode1_bf16", "verify4_bf16", "block32_budget64_live50"])
 def test_decode_verify_full(name):
     check(W.generate(W.WORKLOADS[name]), threads=16)
 

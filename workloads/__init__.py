@@ -86,6 +86,10 @@ WORKLOADS: Dict[str, Workload] = {
     "decode1_bf16": Workload("decode1_bf16", 1, 1, 2048, 256, 8, 512, 512, BF16, BF16, 1.0, seed=5),
     # verification of 4 drafted candidates in one call, plain top-8
     "verify4_bf16": Workload("verify4_bf16", 1, 4, 2048, 256, 8, 512, 512, BF16, BF16, 1.0, seed=6),
+    # expert budget / live-row reuse: one 32-row block whose coreset is capped at
+    # 64 experts, half of whose rows are live (the others reuse cached outputs)
+    "block32_budget64_live50": Workload("block32_budget64_live50", 1, 32, 2048, 256, 8, 512, 512, BF16,
+                                        BF16, 0.9, seed=7, expert_budget=64, live_fraction=0.5),
 }
 
 # Threshold / top-k sweep run on the skewed workload (1.0 = unrestricted top-k;
