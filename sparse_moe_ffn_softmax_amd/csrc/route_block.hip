@@ -21,6 +21,11 @@
 //              ties to the lower id; gate_j = (float)(u_j / sum of u over the
 //              chosen slots in slot order)
 //
+// With call options (InfiniLM PR #604, "Summary": expert-budget / live-row
+// reuse): m is further cut to the expert budget; resolved rows (live mask 0)
+// add nothing to the mass and take no route, and a block without live rows
+// has m = 0.
+//
 // exp is evaluated by Cody & Waite's (1980) argument reduction and the
 // degree-13 Taylor polynomial of exp(r), Horner with fma, then scaled by
 // 2^n; every operation is an IEEE fp64 primitive, so results are bitwise
