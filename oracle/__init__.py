@@ -17,8 +17,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "clover_moe_oracle.c")
 _LIB = os.path.join(_HERE, "libclover_moe_oracle.so")
 
-ORC_F32, ORC_BF16, ORC_FP8 = 0, 1, 2
-_DT = {"f32": ORC_F32, "bf16": ORC_BF16, "fp8_e4m3": ORC_FP8}
+ORC_F32, ORC_BF16, ORC_FP8, ORC_FP4 = 0, 1, 2, 3
+_DT = {"f32": ORC_F32, "bf16": ORC_BF16, "fp8_e4m3": ORC_FP8, "fp4_e2m1": ORC_FP4}
 
 
 def build() -> str:
@@ -65,6 +65,10 @@ def lib():
         L.orc_bf16_to_double.argtypes = [ctypes.c_uint16]
         L.orc_e4m3_to_double.restype = ctypes.c_double
         L.orc_e4m3_to_double.argtypes = [ctypes.c_uint8]
+        L.orc_e2m1_to_double.restype = ctypes.c_double
+        L.orc_e2m1_to_double.argtypes = [ctypes.c_uint8]
+        L.orc_e8m0_to_double.restype = ctypes.c_double
+        L.orc_e8m0_to_double.argtypes = [ctypes.c_uint8]
         L.orc_router_logits.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int]
         L.orc_softmax.argtypes = [ctypes.c_void_p] * 4
         L.orc_block_mass.argtypes = [ctypes.c_void_p] * 4
@@ -130,6 +134,14 @@ def bf16_to_double(bits: int) -> float:
 
 def e4m3_to_double(code: int) -> float:
     return lib().orc_e4m3_to_double(int(code))
+
+
+def e2m1_to_double(code: int) -> float:
+    return lib().orc_e2m1_to_double(int(code))
+
+
+def e8m0_to_double(s: int) -> float:
+    return lib().orc_e8m0_to_double(int(s))
 
 
 # --------------------------------------------------------------------------

@@ -108,6 +108,23 @@ double orc_e4m3_to_double(uint8_t code)
     return sign ? -mag : mag;
 }
 
+/* OCP FP4 E2M1 (low 4 bits of `code`): 1 sign, 2 exponent (bias 1), 1
+ * mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; no NaN or infinity. */
+double orc_e2m1_to_double(uint8_t code)
+{
+    int sign = (code >> 3) & 1;
+    int expo = (code >> 1) & 0x3;
+    int mant = code & 0x1;
+    double mag = expo == 0 ? 0.5 * mant : ldexp(1.0 + 0.5 * mant, expo - 1);
+    return sign ? -mag : mag;
+}
+
+/* OCP E8M0 scale: 2^(s-127), s in 0..254; 255 is NaN. */
+double orc_e8m0_to_double(uint8_t s)
+{
+    return s == 255 ? NAN : ldexp(1.0, (int)s - 127);
+}
+
 static double act_value(int dtype, const void* x, size_t i)
 {
     if (dtype == ORC_BF16) return orc_bf16_to_double(((const uint16_t*)x)[i]);
@@ -115,8 +132,9 @@ static double act_value(int dtype, const void* x, size_t i)
 }
 
 /* Widen row `row` of a [rows, cols] weight matrix to fp64.  fp8 values are
- * code * scale[row/128][col/128], which is exact in fp64. */
-static void widen_weight_row(int dtype, const void* w, const float* scale, int cols,
+ * code * scale[row/128][col/128]; fp4 values are code * 2^(s-127) with s the
+ * E8M0 byte [row][col/32]; both products are exact in fp64. */
+static void widen_weight_row(int dtype, const void* w, const void* scale, int cols,
                              int row, double* dst)
 {
     size_t base = (size_t)row * (size_t)cols;
@@ -124,8 +142,16 @@ static void widen_weight_row(int dtype, const void* w, const float* scale, int c
         switch (dtype) {
         case ORC_F32: dst[c] = (double)((const float*)w)[base + c]; break;
         case ORC_BF16: dst[c] = orc_bf16_to_double(((const uint16_t*)w)[base + c]); break;
+        case ORC_FP4_E2M1: {
+            uint8_t byte = ((const uint8_t*)w)[(base + (size_t)c) / 2];
+            uint8_t code = (c & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 0xF);
+            uint8_t s = ((const uint8_t*)scale)[(size_t)row * (size_t)(cols / 32) + (size_t)(c / 32)];
+            dst[c] = orc_e2m1_to_double(code) * orc_e8m0_to_double(s);
+            break;
+        }
         default: {
-            double s = (double)scale[(size_t)(row / 128) * (size_t)(cols / 128) + (size_t)(c / 128)];
+            const float* sc = (const float*)scale;
+            double s = (double)sc[(size_t)(row / 128) * (size_t)(cols / 128) + (size_t)(c / 128)];
             dst[c] = orc_e4m3_to_double(((const uint8_t*)w)[base + c]) * s;
         }
         }
@@ -299,8 +325,8 @@ int orc_row_topk(const float* logits_row, const double* u_row, const uint8_t* in
 /* h = a * sigmoid(a) * v; y = W2 h.                                          */
 /* ------------------------------------------------------------------------ */
 
-void orc_expert_ffn(int hidden, int inter, int wdtype, const void* w13, const float* w13_scale,
-                    const void* w2, const float* w2_scale, const double* xrow, double* y)
+void orc_expert_ffn(int hidden, int inter, int wdtype, const void* w13, const void* w13_scale,
+                    const void* w2, const void* w2_scale, const double* xrow, double* y)
 {
     double* wrow = (double*)malloc(sizeof(double) * (size_t)(hidden > inter ? hidden : inter));
     double* z = (double*)malloc(sizeof(double) * 2 * (size_t)inter);
@@ -326,9 +352,22 @@ void orc_expert_ffn(int hidden, int inter, int wdtype, const void* w13, const fl
     free(h);
 }
 
-static size_t weight_elem_size(int dtype)
+/* bytes of a [rows, cols] weight matrix, and of its scales, in `dtype` storage */
+static size_t matrix_bytes(int dtype, size_t rows, size_t cols)
 {
-    return dtype == ORC_F32 ? 4 : dtype == ORC_BF16 ? 2 : 1;
+    switch (dtype) {
+    case ORC_F32: return rows * cols * 4;
+    case ORC_BF16: return rows * cols * 2;
+    case ORC_FP4_E2M1: return rows * cols / 2;
+    default: return rows * cols;
+    }
+}
+
+static size_t scale_bytes(int dtype, size_t rows, size_t cols)
+{
+    if (dtype == ORC_FP8_E4M3) return (rows / 128) * (cols / 128) * 4;
+    if (dtype == ORC_FP4_E2M1) return rows * (cols / 32);
+    return 0;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -354,6 +393,8 @@ int orc_forward_ex(const orc_problem* p, const orc_weights* w, const void* x,
     if (expert_budget < 0 || expert_budget > E) return 5;
     if (p->weight_dtype == ORC_FP8_E4M3 &&
         (H % 128 || I % 128 || Is % 128 || !w->w13_scale || !w->w2_scale)) return 4;
+    if (p->weight_dtype == ORC_FP4_E2M1 &&
+        (H % 32 || I % 32 || Is % 32 || !w->w13_scale || !w->w2_scale)) return 4;
 
     float* logits = (float*)malloc(sizeof(float) * (size_t)N * E);
     double* u = (double*)malloc(sizeof(double) * (size_t)N * E);
@@ -429,11 +470,11 @@ int orc_forward_ex(const orc_problem* p, const orc_weights* w, const void* x,
 
     /* 7. FFN of every (row, slot) plus the shared expert, fp64 */
     if (out) {
-        const size_t ew = weight_elem_size(p->weight_dtype);
-        const size_t w13_elems = (size_t)2 * I * H, w2_elems = (size_t)H * I;
-        const size_t w13_sc = (size_t)(2 * I / 128) * (size_t)(H / 128);
-        const size_t w2_sc = (size_t)(H / 128) * (size_t)(I / 128);
-        const int fp8 = p->weight_dtype == ORC_FP8_E4M3;
+        const int wd = p->weight_dtype;
+        const size_t w13_b = matrix_bytes(wd, (size_t)2 * I, (size_t)H);
+        const size_t w2_b = matrix_bytes(wd, (size_t)H, (size_t)I);
+        const size_t w13_sb = scale_bytes(wd, (size_t)2 * I, (size_t)H);
+        const size_t w2_sb = scale_bytes(wd, (size_t)H, (size_t)I);
 #ifdef _OPENMP
         if (threads > 0) omp_set_num_threads(threads);
 #pragma omp parallel for schedule(dynamic, 1)
@@ -453,10 +494,11 @@ int orc_forward_ex(const orc_problem* p, const orc_weights* w, const void* x,
             for (int j = 0; j < K; ++j) {
                 int e = idx[(size_t)r * K + j];
                 if (e < 0) continue;
-                const char* w13e = (const char*)w->w13 + (size_t)e * w13_elems * ew;
-                const char* w2e = (const char*)w->w2 + (size_t)e * w2_elems * ew;
-                orc_expert_ffn(H, I, p->weight_dtype, w13e, fp8 ? w->w13_scale + (size_t)e * w13_sc : NULL,
-                               w2e, fp8 ? w->w2_scale + (size_t)e * w2_sc : NULL, xr, y);
+                const char* w13e = (const char*)w->w13 + (size_t)e * w13_b;
+                const char* w2e = (const char*)w->w2 + (size_t)e * w2_b;
+                const char* s13 = w13_sb ? (const char*)w->w13_scale + (size_t)e * w13_sb : NULL;
+                const char* s2 = w2_sb ? (const char*)w->w2_scale + (size_t)e * w2_sb : NULL;
+                orc_expert_ffn(H, I, wd, w13e, s13, w2e, s2, xr, y);
                 double g = (double)gates[(size_t)r * K + j];
                 for (int c = 0; c < H; ++c) acc[c] += g * y[c];
             }

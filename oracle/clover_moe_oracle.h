@@ -40,8 +40,11 @@
 extern "C" {
 #endif
 
-/* storage dtype codes */
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8_E4M3 = 2 };
+/* storage dtype codes.  ORC_FP4_E2M1: 4-bit E2M1 codes, two per byte (low
+ * nibble first), with one E8M0 scale byte (2^(s-127)) per 32 consecutive
+ * elements of a row (OCP Microscaling MXFP4; a stand-in for the 4-bit
+ * experts of the CMF model card, "Files", whose own layout is not given). */
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8_E4M3 = 2, ORC_FP4_E2M1 = 3 };
 
 typedef struct {
     int hidden;        /* H */
@@ -54,17 +57,19 @@ typedef struct {
     int weight_dtype;  /* ORC_F32, ORC_BF16 or ORC_FP8_E4M3 (expert weights) */
 } orc_problem;
 
+/* Scales: fp8: fp32 per 128x128 block, [rows/128, cols/128] per matrix;
+ * fp4: uint8 E8M0 per 32 elements of a row, [rows, cols/32] per matrix. */
 typedef struct {
     const float* router_w;         /* [E,H] fp32 */
     const float* router_b;         /* [E] fp32 or NULL */
     const void* w13;               /* [E,2I,H]: rows 0..I-1 gate, I..2I-1 up */
-    const float* w13_scale;        /* fp8: [E,2I/128,H/128] */
+    const void* w13_scale;         /* fp8: [E,2I/128,H/128] fp32; fp4: [E,2I,H/32] uint8 */
     const void* w2;                /* [E,H,I] */
-    const float* w2_scale;         /* fp8: [E,H/128,I/128] */
+    const void* w2_scale;          /* fp8: [E,H/128,I/128] fp32; fp4: [E,H,I/32] uint8 */
     const void* shared_w13;        /* [2Is,H] or NULL */
-    const float* shared_w13_scale; /* fp8: [2Is/128,H/128] */
+    const void* shared_w13_scale;  /* fp8: [2Is/128,H/128]; fp4: [2Is,H/32] */
     const void* shared_w2;         /* [H,Is] or NULL */
-    const float* shared_w2_scale;  /* fp8: [H/128,Is/128] */
+    const void* shared_w2_scale;   /* fp8: [H/128,Is/128]; fp4: [H,Is/32] */
 } orc_weights;
 
 /* ---- scalar building blocks (exposed so the tests can pin them) ---- */
@@ -75,6 +80,8 @@ double orc_exp(double d);
 void orc_exp_constants(double out[17]);
 double orc_bf16_to_double(uint16_t bits);
 double orc_e4m3_to_double(uint8_t code);
+double orc_e2m1_to_double(uint8_t code);   /* low 4 bits */
+double orc_e8m0_to_double(uint8_t s);      /* 2^(s-127); s = 255 is NaN */
 
 /* ---- routing stages ---- */
 
@@ -136,8 +143,8 @@ int orc_forward_ex(const orc_problem* p, const orc_weights* w, const void* x,
 
 /* fp64 SwiGLU FFN of one expert weight set on one input row (widened to fp64):
  * y[H] = W2 * (silu(W13[0:I] x) * (W13[I:2I] x)).  wdtype as in orc_problem. */
-void orc_expert_ffn(int hidden, int inter, int wdtype, const void* w13, const float* w13_scale,
-                    const void* w2, const float* w2_scale, const double* xrow, double* y);
+void orc_expert_ffn(int hidden, int inter, int wdtype, const void* w13, const void* w13_scale,
+                    const void* w2, const void* w2_scale, const double* xrow, double* y);
 
 #ifdef __cplusplus
 }

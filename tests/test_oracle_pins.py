@@ -98,6 +98,35 @@ def test_e4m3_decode_all_codes_match_torch():
     assert np.nanmax(ours) == 448.0 and oracle.e4m3_to_double(0x01) == 2.0 ** -9
 
 
+def test_e2m1_decode_matches_ocp_table():
+    for c in range(16):
+        want = (-1.0 if c & 8 else 1.0) * OCP_E2M1[c & 7]
+        got = oracle.e2m1_to_double(c)
+        assert got == want and math.copysign(1.0, got) == math.copysign(1.0, want), c
+
+
+def test_e8m0_decode_matches_torch():
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e8m0fnu).double().numpy()
+    got = np.array([oracle.e8m0_to_double(c) for c in range(256)])
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    np.testing.assert_array_equal(got[:255], ref[:255])
+
+
+def test_mxfp4_storage_roundtrip_of_representable_blocks():
+    """Blocks whose largest magnitude is 6 * 2^e and whose other elements are
+    E2M1 values times 2^e are stored exactly (scale byte e + 127)."""
+    rng = np.random.default_rng(3)
+    e = rng.integers(-20, 5, size=(4, 2))
+    grid = np.array(OCP_E2M1)
+    vals = grid[rng.integers(0, 8, size=(4, 2, 32))] * np.where(rng.random((4, 2, 32)) < 0.5, -1, 1)
+    vals[..., 0] = 6.0
+    w = (vals * np.ldexp(1.0, e)[..., None]).reshape(4, 64).astype(np.float32)
+    codes, scales = W.quantize_mxfp4(w)
+    np.testing.assert_array_equal(scales, (e + 127).astype(np.uint8))
+    np.testing.assert_array_equal(_dequant(codes, scales, W.FP4), w.astype(np.float64))
+
+
 def test_fp8_block_quantisation_roundtrip_is_scale_times_code():
     rng = np.random.default_rng(5)
     w = rng.standard_normal((256, 384)).astype(np.float32) * 0.02
@@ -366,11 +395,21 @@ def test_blocks_are_independent():
 # FFN
 # ----------------------------------------------------------------------------
 
+# OCP Microscaling spec, FP4 E2M1 element values of codes 0..7 (sign in bit 3)
+OCP_E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
 def _dequant(arr, scale, dtype):
     if dtype == W.F32:
         return arr.astype(np.float64)
     if dtype == W.BF16:
         return W.bf16_bits_to_f32(arr).astype(np.float64)
+    if dtype == W.FP4:
+        codes = np.stack([arr & 0xF, arr >> 4], axis=-1).reshape(*arr.shape[:-1], arr.shape[-1] * 2)
+        mag = np.array(OCP_E2M1)[codes & 7]
+        val = np.where(codes & 8, -mag, mag)
+        s = torch.from_numpy(np.ascontiguousarray(scale)).view(torch.float8_e8m0fnu).double().numpy()
+        return val * np.repeat(s, 32, axis=-1)
     q = torch.from_numpy(np.ascontiguousarray(arr)).view(torch.float8_e4m3fn).double().numpy()
     s = np.repeat(np.repeat(scale.astype(np.float64), 128, -2), 128, -1)
     return q * s
@@ -404,7 +443,7 @@ def _numpy_shared(inp):
                    _dequant(inp.shared_w2, inp.shared_w2_scale, wd))
 
 
-@pytest.mark.parametrize("variant", ["fp32", "bf16", "fp8", "rows1", "rows4"])
+@pytest.mark.parametrize("variant", ["fp32", "bf16", "fp8", "fp4", "rows1", "rows4"])
 def test_sparse_ffn_equals_dense_brute_force(variant):
     """Every expert on every row (numpy fp64 matmuls), combined through the
     dense [N,E] gate matrix that is zero off the route."""
@@ -415,6 +454,8 @@ def test_sparse_ffn_equals_dense_brute_force(variant):
         wl = wl.with_(act_dtype=W.BF16, weight_dtype=W.BF16)
     if variant == "fp8":
         wl = wl.with_(act_dtype=W.BF16, weight_dtype=W.FP8)
+    if variant == "fp4":
+        wl = wl.with_(act_dtype=W.BF16, weight_dtype=W.FP4)
     inp = W.generate(wl)
     r = oracle.forward(inp)
     G = np.zeros((wl.rows, wl.num_experts))

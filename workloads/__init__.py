@@ -37,6 +37,7 @@ import numpy as np
 F32 = "f32"
 BF16 = "bf16"
 FP8 = "fp8_e4m3"
+FP4 = "fp4_e2m1"         # MXFP4: E2M1 codes, two per byte, E8M0 scale per 32 elements
 
 FP8_BLOCK = 128          # 128x128 weight blocks with one fp32 scale each
 FP8_MAX = 448.0          # largest finite OCP e4m3fn magnitude
@@ -161,6 +162,40 @@ def quantize_fp8_blocks(w: np.ndarray):
     return codes.reshape(*lead, rows, cols).copy(), scale
 
 
+MX_BLOCK = 32             # elements per E8M0 scale (OCP Microscaling)
+E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])  # magnitudes of codes 0..7
+
+
+def quantize_mxfp4(w: np.ndarray):
+    """Quantise a [..., rows, cols] fp32 array to MXFP4 (OCP Microscaling): per
+    block of 32 consecutive elements of a row, the E8M0 scale 2^e with
+    e = floor(log2(max|W_blk|)) - 2 (the largest E2M1 exponent), and each
+    element rounded to the nearest E2M1 value of W/2^e (ties to the even
+    code, saturating at 6).  An all-zero block gets e = 0.
+
+    Returns (codes uint8 [..., rows, cols/2], element c in byte c/2, low nibble
+    for even c; scales uint8 [..., rows, cols/32] holding e + 127)."""
+    w = np.ascontiguousarray(w, dtype=np.float32).astype(np.float64)
+    *lead, rows, cols = w.shape
+    assert cols % MX_BLOCK == 0
+    blk = w.reshape(*lead, rows, cols // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(blk).max(axis=-1)
+    e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, 0).astype(np.int64)
+    e = np.clip(e, -126, 127)
+    v = blk / np.ldexp(1.0, e)[..., None]
+    mag = np.abs(v)
+    d = np.abs(mag[..., None] - E2M1_GRID)                     # [..., 32, 8]
+    best = d.min(axis=-1, keepdims=True)
+    idx = np.arange(8)
+    # nearest grid value; on a tie the even code (its low bit clear)
+    score = np.where(d == best, 2 - (idx & 1), 0)
+    code = score.argmax(axis=-1).astype(np.uint8)
+    code = code | np.where(v < 0, 8, 0).astype(np.uint8)
+    code = code.reshape(*lead, rows, cols)
+    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
+    return np.ascontiguousarray(packed), np.ascontiguousarray((e + 127).astype(np.uint8))
+
+
 def _store_weight(w32: np.ndarray, dtype: str):
     if dtype == F32:
         return np.ascontiguousarray(w32, dtype=np.float32), None
@@ -168,6 +203,8 @@ def _store_weight(w32: np.ndarray, dtype: str):
         return f32_to_bf16_bits(w32), None
     if dtype == FP8:
         return quantize_fp8_blocks(w32)
+    if dtype == FP4:
+        return quantize_mxfp4(w32)
     raise ValueError(dtype)
 
 
@@ -201,9 +238,9 @@ def generate(wl: Workload) -> MoEInputs:
         w2_sc.append(s)
     w13 = np.stack(w13_parts)
     w2 = np.stack(w2_parts)
-    fp8 = wl.weight_dtype == FP8
-    w13_scale = np.stack(w13_sc) if fp8 else None
-    w2_scale = np.stack(w2_sc) if fp8 else None
+    scaled = wl.weight_dtype in (FP8, FP4)
+    w13_scale = np.stack(w13_sc) if scaled else None
+    w2_scale = np.stack(w2_sc) if scaled else None
     if Is > 0:
         sw13, sw13_s = _store_weight(draw((2 * Is, H), wl.sigma), wl.weight_dtype)
         sw2, sw2_s = _store_weight(draw((H, Is), wl.sigma), wl.weight_dtype)
