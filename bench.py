@@ -36,7 +36,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "fp8_e4m3": 2500.0}  # fp8 weights run on bf16 MFMA
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "fp8_e4m3": 2500.0,  # fp8 and fp4 weights are
+                    "fp4_e2m1": 2500.0}                                    # widened to bf16 MFMA
 
 
 def hip():
@@ -200,14 +201,21 @@ def main():
     cnt = counts[args.warmup:].cpu().numpy().astype(np.int64)  # [steps, E]
     touched = (cnt > 0).sum(1)
     pairs = cnt.sum(1)
-    wsz = {W.F32: 4, W.BF16: 2, W.FP8: 1}[wl.weight_dtype]
+    wsz = {W.F32: 4, W.BF16: 2, W.FP8: 1, W.FP4: 0.5}[wl.weight_dtype]
     asz = {W.F32: 4, W.BF16: 2}[wl.act_dtype]
     hsz = 4 if wl.act_dtype == W.F32 else 2
     fp8 = wl.weight_dtype == W.FP8
-    sc_up = (2 * I // 128) * (H // 128) * 4 if fp8 else 0
-    sc_dn = (H // 128) * (I // 128) * 4 if fp8 else 0
-    sc_up_s = (2 * Is // 128) * (H // 128) * 4 if fp8 and Is else 0
-    sc_dn_s = (H // 128) * (Is // 128) * 4 if fp8 and Is else 0
+    fp4 = wl.weight_dtype == W.FP4
+
+    def scale_bytes(rows, cols):
+        if fp8:
+            return (rows // 128) * (cols // 128) * 4
+        if fp4:
+            return rows * (cols // 32)
+        return 0
+    sc_up, sc_dn = scale_bytes(2 * I, H), scale_bytes(H, I)
+    sc_up_s = scale_bytes(2 * Is, H) if Is else 0
+    sc_dn_s = scale_bytes(H, Is) if Is else 0
     n_sh = N if Is else 0
     # algorithmic bytes per launch of the gate/up kernel: weights of the touched
     # experts (+ shared), x once, h written once
@@ -255,7 +263,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {W.BF16: "bf16", W.F32: "f32", W.FP8: "fp8_e4m3 weights, bf16 activations"}[wl.weight_dtype],
+        "dtype": {W.BF16: "bf16", W.F32: "f32", W.FP8: "fp8_e4m3 weights, bf16 activations",
+                  W.FP4: "fp4_e2m1 (MXFP4) weights, bf16 activations"}[wl.weight_dtype],
         "data": "synthetic (seeded normal inputs and random-init weights of the stated shapes)",
         "config": {"workload": wl.name, "num_blocks": B, "block_rows": wl.block_rows, "hidden": H,
                    "experts": E, "top_k": K, "inter": I, "shared_inter": Is,

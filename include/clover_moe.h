@@ -86,7 +86,11 @@ typedef enum {
 typedef enum {
     CMOE_F32 = 0,
     CMOE_BF16 = 1,
-    CMOE_FP8_E4M3 = 2 /* OCP E4M3 ("e4m3fn", max 448), with fp32 128x128 block scales */
+    CMOE_FP8_E4M3 = 2, /* OCP E4M3 ("e4m3fn", max 448), with fp32 128x128 block scales */
+    CMOE_FP4_E2M1 = 3  /* 4-bit experts (CMF model card, "Files"; its own layout is not
+                          given, the stand-in is OCP Microscaling MXFP4): E2M1 codes, two
+                          per byte, low nibble first, and one E8M0 scale byte 2^(s-127),
+                          s = 1..254, per 32 consecutive elements of a row */
 } cmoe_dtype;
 
 /* Shapes and dtypes (host struct). */
@@ -102,21 +106,26 @@ typedef struct {
     int32_t num_blocks;   /* B: 1..1024; N = B*R rows, block b is rows [b*R, (b+1)*R) */
     int32_t act_dtype;    /* cmoe_dtype of x and out: CMOE_F32 or CMOE_BF16 */
     int32_t weight_dtype; /* cmoe_dtype of the expert weights.  Supported pairs
-                             (act, weight): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3) */
+                             (act, weight): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3),
+                             (BF16, FP4_E2M1) */
 } cmoe_problem;
 
 /* Weights (host struct of device pointers). */
+/* Weight matrices are [rows, cols] row-major in weight_dtype; for FP4_E2M1
+ * that is rows*cols/2 bytes.  Scale arrays: FP8_E4M3: fp32, one per 128x128
+ * block, [rows/128, cols/128] per matrix; FP4_E2M1: uint8 E8M0, one per 32
+ * elements of a row, [rows, cols/32] per matrix; other dtypes: ignored. */
 typedef struct {
-    const float* router_w;         /* [E,H] fp32, required */
-    const float* router_b;         /* [E] fp32 per-expert logit bias, or NULL */
-    const void* w13;               /* [E,2I,H] weight_dtype: rows 0..I-1 gate, I..2I-1 up */
-    const float* w13_scale;        /* fp8 only: [E,2I/128,H/128] fp32; else ignored */
-    const void* w2;                /* [E,H,I] weight_dtype (down projection) */
-    const float* w2_scale;         /* fp8 only: [E,H/128,I/128] fp32 */
-    const void* shared_w13;        /* [2Is,H] weight_dtype; required when Is > 0 */
-    const float* shared_w13_scale; /* fp8 only: [2Is/128,H/128] */
-    const void* shared_w2;         /* [H,Is] weight_dtype; required when Is > 0 */
-    const float* shared_w2_scale;  /* fp8 only: [H/128,Is/128] */
+    const float* router_w;        /* [E,H] fp32, required */
+    const float* router_b;        /* [E] fp32 per-expert logit bias, or NULL */
+    const void* w13;              /* [E,2I,H] weight_dtype: rows 0..I-1 gate, I..2I-1 up */
+    const void* w13_scale;        /* fp8: [E,2I/128,H/128] fp32; fp4: [E,2I,H/32] uint8 */
+    const void* w2;               /* [E,H,I] weight_dtype (down projection) */
+    const void* w2_scale;         /* fp8: [E,H/128,I/128] fp32; fp4: [E,H,I/32] uint8 */
+    const void* shared_w13;       /* [2Is,H] weight_dtype; required when Is > 0 */
+    const void* shared_w13_scale; /* fp8: [2Is/128,H/128]; fp4: [2Is,H/32] */
+    const void* shared_w2;        /* [H,Is] weight_dtype; required when Is > 0 */
+    const void* shared_w2_scale;  /* fp8: [H/128,Is/128]; fp4: [H,Is/32] */
 } cmoe_weights;
 
 /* Optional routing outputs (host struct of device pointers; each may be NULL). */

@@ -18,8 +18,8 @@ LIB_PATH = os.path.join(_PKG, "libclover_moe.so")
 
 CMOE_OK, CMOE_ERR_NULL, CMOE_ERR_VALUE, CMOE_ERR_UNSUPPORTED = 0, 1, 2, 3
 CMOE_ERR_ALIGN, CMOE_ERR_ALIAS, CMOE_ERR_WORKSPACE, CMOE_ERR_HIP = 4, 5, 6, 7
-CMOE_F32, CMOE_BF16, CMOE_FP8_E4M3 = 0, 1, 2
-DTYPE_CODES = {"f32": CMOE_F32, "bf16": CMOE_BF16, "fp8_e4m3": CMOE_FP8_E4M3}
+CMOE_F32, CMOE_BF16, CMOE_FP8_E4M3, CMOE_FP4_E2M1 = 0, 1, 2, 3
+DTYPE_CODES = {"f32": CMOE_F32, "bf16": CMOE_BF16, "fp8_e4m3": CMOE_FP8_E4M3, "fp4_e2m1": CMOE_FP4_E2M1}
 
 EXPORTED = ("clover_moe_workspace_size", "clover_moe_block_forward", "clover_moe_block_forward_ex",
             "clover_moe_block_forward_staged", "clover_moe_status_string", "clover_moe_last_error")

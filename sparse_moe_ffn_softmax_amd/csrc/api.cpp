@@ -75,7 +75,8 @@ cmoe_status check_problem(const cmoe_problem* p, int32_t top_k) {
     return fail(CMOE_ERR_UNSUPPORTED, "num_blocks=%d: at most 1024 blocks per call", p->num_blocks);
   const bool ok_pair = (p->act_dtype == CMOE_F32 && p->weight_dtype == CMOE_F32) ||
                        (p->act_dtype == CMOE_BF16 && p->weight_dtype == CMOE_BF16) ||
-                       (p->act_dtype == CMOE_BF16 && p->weight_dtype == CMOE_FP8_E4M3);
+                       (p->act_dtype == CMOE_BF16 && p->weight_dtype == CMOE_FP8_E4M3) ||
+                       (p->act_dtype == CMOE_BF16 && p->weight_dtype == CMOE_FP4_E2M1);
   if (!ok_pair)
     return fail(CMOE_ERR_UNSUPPORTED,
                 "dtype pair (act=%d, weight=%d) unsupported: use (F32,F32), (BF16,BF16) or (BF16,FP8_E4M3)",
@@ -212,10 +213,11 @@ static cmoe_status forward_impl(const cmoe_problem* problem, const cmoe_weights*
   if (!w->w2) return fail(CMOE_ERR_NULL, "weights->w2 is NULL");
   if (p.shared_inter > 0 && (!w->shared_w13 || !w->shared_w2))
     return fail(CMOE_ERR_NULL, "shared_inter > 0 but the shared expert weights are NULL");
-  const bool fp8 = p.weight_dtype == CMOE_FP8_E4M3;
-  if (fp8 && (!w->w13_scale || !w->w2_scale ||
-              (p.shared_inter > 0 && (!w->shared_w13_scale || !w->shared_w2_scale))))
-    return fail(CMOE_ERR_NULL, "fp8 weights need every 128x128 block-scale array");
+  const bool fp8 = p.weight_dtype == CMOE_FP8_E4M3, fp4 = p.weight_dtype == CMOE_FP4_E2M1;
+  if ((fp8 || fp4) && (!w->w13_scale || !w->w2_scale ||
+                       (p.shared_inter > 0 && (!w->shared_w13_scale || !w->shared_w2_scale))))
+    return fail(CMOE_ERR_NULL, "%s weights need every scale array",
+                fp8 ? "fp8" : "fp4");
   if (!(mass_threshold > 0.0f && mass_threshold <= 1.0f))
     return fail(CMOE_ERR_VALUE, "mass_threshold=%g must be in (0, 1]", (double)mass_threshold);
   const int budget = options ? options->expert_budget : 0;
@@ -232,19 +234,31 @@ static cmoe_status forward_impl(const cmoe_problem* problem, const cmoe_weights*
   // every device range the call touches
   const size_t N = (size_t)p.block_rows * p.num_blocks, E = p.num_experts, H = p.hidden,
                I = p.inter, Is = p.shared_inter, B = p.num_blocks, K = top_k;
-  const size_t asz = dtype_size(p.act_dtype), wsz = dtype_size(p.weight_dtype);
+  const size_t asz = dtype_size(p.act_dtype);
+  // bytes of a [rows, cols] weight matrix in the weight dtype
+  auto wbytes = [&](size_t rows, size_t cols) {
+    return fp4 ? rows * cols / 2 : rows * cols * dtype_size(p.weight_dtype);
+  };
   std::vector<Range> rs = {
       {"x", (uintptr_t)x, N * H * asz, false},
       {"router_w", (uintptr_t)w->router_w, E * H * 4, false},
       {"router_b", (uintptr_t)w->router_b, E * 4, false},
-      {"w13", (uintptr_t)w->w13, E * 2 * I * H * wsz, false},
-      {"w2", (uintptr_t)w->w2, E * H * I * wsz, false},
-      {"shared_w13", Is ? (uintptr_t)w->shared_w13 : 0, 2 * Is * H * wsz, false},
-      {"shared_w2", Is ? (uintptr_t)w->shared_w2 : 0, H * Is * wsz, false},
+      {"w13", (uintptr_t)w->w13, E * wbytes(2 * I, H), false},
+      {"w2", (uintptr_t)w->w2, E * wbytes(H, I), false},
+      {"shared_w13", Is ? (uintptr_t)w->shared_w13 : 0, wbytes(2 * Is, H), false},
+      {"shared_w2", Is ? (uintptr_t)w->shared_w2 : 0, wbytes(H, Is), false},
       {"live_rows", (uintptr_t)live, N, false},
       {"out", (uintptr_t)out, N * H * asz, true},
       {"workspace", (uintptr_t)workspace, need, true},
   };
+  if (fp4) {
+    rs.push_back({"w13_scale", (uintptr_t)w->w13_scale, E * 2 * I * (H / 32), false});
+    rs.push_back({"w2_scale", (uintptr_t)w->w2_scale, E * H * (I / 32), false});
+    if (Is) {
+      rs.push_back({"shared_w13_scale", (uintptr_t)w->shared_w13_scale, 2 * Is * (H / 32), false});
+      rs.push_back({"shared_w2_scale", (uintptr_t)w->shared_w2_scale, H * (Is / 32), false});
+    }
+  }
   if (fp8) {
     rs.push_back({"w13_scale", (uintptr_t)w->w13_scale, E * (2 * I / 128) * (H / 128) * 4, false});
     rs.push_back({"w2_scale", (uintptr_t)w->w2_scale, E * (H / 128) * (I / 128) * 4, false});

@@ -6,12 +6,18 @@
 // D[4*(l/16) + v][l%16], v = 0..3.  v_mfma_f32_16x16x4_f32 uses the same
 // layout with one k per lane.  The k order inside a step only has to be the
 // same for A and B, so each lane loads 16 contiguous bytes of its row.
+//
+// Inside a 128-deep stage, lane group kg (= l/16) covers k kGroupK*kg + u*kStepK
+// .. +kLane at MFMA step u.  For bf16, fp32 and fp8 that is the natural
+// order (kGroupK = kLane, kStepK = kStep).  For fp4 each lane group takes a
+// contiguous 32 k (one MX scale block), so its 32 codes are one 16-byte load
+// and it needs one scale per stage.
 #pragma once
 #include "cmoe_device.h"
 
 namespace cmoe {
 
-enum class WFmt { BF16, F32, FP8 };
+enum class WFmt { BF16, F32, FP8, FP4 };
 
 // ---------------------------------------------------------------------------
 // fragments: what one lane loads for one k step
@@ -23,6 +29,8 @@ template <>
 struct Frag<WFmt::BF16> {
   static constexpr int kStep = 32;  // k per MFMA step
   static constexpr int kLane = 8;   // elements per lane per step
+  static constexpr int kGroupK = kLane, kStepK = kStep;
+  static constexpr int kPack = 1;   // weight elements per WT unit
   using A = u32x4;                  // 8 bf16
   using B = u32x4;
   using AT = uint16_t;
@@ -40,6 +48,8 @@ template <>
 struct Frag<WFmt::F32> {
   static constexpr int kStep = 16;
   static constexpr int kLane = 4;
+  static constexpr int kGroupK = kLane, kStepK = kStep;
+  static constexpr int kPack = 1;
   using A = f32x4;
   using B = f32x4;
   using AT = float;
@@ -60,6 +70,8 @@ template <>
 struct Frag<WFmt::FP8> {
   static constexpr int kStep = 32;
   static constexpr int kLane = 8;
+  static constexpr int kGroupK = kLane, kStepK = kStep;
+  static constexpr int kPack = 1;
   using A = u32x4;  // 8 bf16
   using B = u32x2;  // 8 e4m3 codes
   using AT = uint16_t;
@@ -80,6 +92,41 @@ struct Frag<WFmt::FP8> {
   static __device__ __forceinline__ f32x4 mma(A a, B b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, widen(b)), c, 0, 0,
+                                                   0);
+  }
+};
+
+// MXFP4 (OCP Microscaling): E2M1 codes, two per byte, low nibble first, and
+// one E8M0 scale byte per 32 consecutive elements of a row.  Widened to bf16
+// exactly: an E2M1 value times a power of two is a bf16 value
+// (v_cvt_scalef32_pk_bf16_fp4; nibble order and exactness checked on gfx950
+// over all 256 bytes).  Scale bytes 1..254 (2^-126 .. 2^127) are supported.
+template <>
+struct Frag<WFmt::FP4> {
+  static constexpr int kStep = 32;
+  static constexpr int kLane = 8;
+  static constexpr int kGroupK = 32, kStepK = 8;
+  static constexpr int kPack = 2;
+  using A = u32x4;      // 8 bf16
+  using B = uint32_t;   // 8 E2M1 codes
+  using AT = uint16_t;
+  using WT = uint8_t;
+  static __device__ __forceinline__ A load_a(const AT* p) { return *reinterpret_cast<const u32x4*>(p); }
+  static __device__ __forceinline__ A zero_a() { return u32x4{0u, 0u, 0u, 0u}; }
+  // 2^(s-127) as an fp32 bit pattern (s = 1..254: a normal float)
+  static __device__ __forceinline__ float scale_of(uint32_t s) { return __uint_as_float(s << 23); }
+  static __device__ __forceinline__ u32x4 widen(B b, float sc) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(b, sc, 0);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(b, sc, 1);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(b, sc, 2);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(b, sc, 3);
+    return u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                 __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+  }
+  static __device__ __forceinline__ f32x4 mma(A a, B b, float sc, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, widen(b, sc)), c, 0, 0,
                                                    0);
   }
 };

@@ -36,7 +36,11 @@
 // 128x128 block and bf16 activations (InfiniLM PR #584, "Benchmark": E4M3
 // 128x128 weight blocks with BF16 activations).  fp8 codes are converted to
 // bf16 exactly in registers, each 128-deep k block is accumulated separately
-// and added into the result times its block scale.
+// and added into the result times its block scale.  4-bit weights (the CMF
+// card's "Files" section ships 4-bit experts; the stand-in format here is OCP
+// MXFP4, E2M1 codes with an E8M0 scale per 32 elements) are widened to bf16
+// times their power-of-two scale, which is exact, and need no per-block
+// accumulator.
 #include "cmoe_device.h"
 #include "cmoe_launch.h"
 #include "expert_frag.h"
@@ -58,28 +62,48 @@ struct Stage {
   static constexpr int U = 128 / Frag<F>::kStep;  // MFMA steps per stage
   typename Frag<F>::B b[U];
   typename Frag<F>::A a[MT][U];
+  uint32_t sc;  // fp4: the stage's four E8M0 scale bytes of this lane's row
 };
 
+// wrow: this lane's weight row at its first k of the wave's range (WT units);
+// wscale: fp8: its row of 128x128 block scales at that k (fp32); fp4: its row
+// of E8M0 bytes at that k.
 template <WFmt F, int MT>
 __device__ __forceinline__ void load_stage(Stage<F, MT>& st, const typename Frag<F>::WT* __restrict__ wrow,
+                                           const void* __restrict__ wscale,
                                            const typename Frag<F>::AT* const (&arow)[MT], int k0) {
   using Fr = Frag<F>;
+  if constexpr (F == WFmt::FP4) {
+    // 32 codes (k 32kg .. +32 of the stage) in one load, and the stage's scales
+    const u32x4 v = *reinterpret_cast<const u32x4*>(wrow + k0 / 2);
 #pragma unroll
-  for (int u = 0; u < Stage<F, MT>::U; ++u) st.b[u] = Fr::load_b(wrow + k0 + u * Fr::kStep);
+    for (int u = 0; u < Stage<F, MT>::U; ++u) st.b[u] = v[u];
+    st.sc = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(wscale) + k0 / 32);
+  } else {
+#pragma unroll
+    for (int u = 0; u < Stage<F, MT>::U; ++u) st.b[u] = Fr::load_b(wrow + k0 + u * Fr::kStep);
+  }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int u = 0; u < Stage<F, MT>::U; ++u)
-      st.a[mt][u] = arow[mt] ? Fr::load_a(arow[mt] + k0 + u * Fr::kStep) : Fr::zero_a();
+      st.a[mt][u] = arow[mt] ? Fr::load_a(arow[mt] + k0 + u * Fr::kStepK) : Fr::zero_a();
 }
 
 template <WFmt F, int MT>
-__device__ __forceinline__ void mma_stage(const Stage<F, MT>& st, const float* __restrict__ wscale,
+__device__ __forceinline__ void mma_stage(const Stage<F, MT>& st, const void* __restrict__ wscale,
                                           int k0, f32x4 (&acc)[MT]) {
   using Fr = Frag<F>;
   constexpr int U = Stage<F, MT>::U;
-  if constexpr (F == WFmt::FP8) {
-    const float s = wscale[k0 / 128];
+  if constexpr (F == WFmt::FP4) {
+    const int kg = (threadIdx.x & 63) >> 4;
+    const float sc = Fr::scale_of((st.sc >> (8 * kg)) & 0xFFu);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = Fr::mma(st.a[mt][u], st.b[u], sc, acc[mt]);
+  } else if constexpr (F == WFmt::FP8) {
+    const float s = static_cast<const float*>(wscale)[k0 / 128];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -99,17 +123,17 @@ __device__ __forceinline__ void mma_stage(const Stage<F, MT>& st, const float* _
 template <WFmt F, int MT>
 __device__ __forceinline__ void wave_gemm(const typename Frag<F>::WT* __restrict__ wrow,
                                           const typename Frag<F>::AT* const (&arow)[MT], int K,
-                                          const float* __restrict__ wscale, f32x4 (&acc)[MT]) {
+                                          const void* __restrict__ wscale, f32x4 (&acc)[MT]) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   Stage<F, MT> s0, s1;
-  load_stage<F, MT>(s0, wrow, arow, 0);
+  load_stage<F, MT>(s0, wrow, wscale, arow, 0);
   for (int k0 = 0; k0 < K; k0 += 256) {
     const bool two = k0 + 128 < K;
-    if (two) load_stage<F, MT>(s1, wrow, arow, k0 + 128);
+    if (two) load_stage<F, MT>(s1, wrow, wscale, arow, k0 + 128);
     mma_stage<F, MT>(s0, wscale, k0, acc);
     if (!two) break;
-    if (k0 + 256 < K) load_stage<F, MT>(s0, wrow, arow, k0 + 256);
+    if (k0 + 256 < K) load_stage<F, MT>(s0, wrow, wscale, arow, k0 + 256);
     mma_stage<F, MT>(s1, wscale, k0 + 128, acc);
   }
 }
@@ -117,9 +141,9 @@ __device__ __forceinline__ void wave_gemm(const typename Frag<F>::WT* __restrict
 struct UpArgs {
   const void* x;
   const void* w13;
-  const float* w13_scale;
+  const void* w13_scale;
   const void* sw13;
-  const float* sw13_scale;
+  const void* sw13_scale;
   const Tile* tiles;
   const int32_t* tile_count;
   const int32_t* pair_row;
@@ -143,19 +167,24 @@ __device__ __forceinline__ void up_tile(const UpArgs& a, const Tile& t, int slic
   const int ks = (a.H % 512 == 0) ? 4 : (a.H % 256 == 0) ? 2 : 1;
   const int klen = a.H / ks, kbeg = wave * klen;
   const WT* W = shared ? static_cast<const WT*>(a.sw13)
-                       : static_cast<const WT*>(a.w13) + (size_t)t.expert * 2 * a.I * a.H;
-  const WT* wrow = W + (size_t)wr * a.H + kbeg + kg * Fr::kLane;
-  const float* wscale = nullptr;
+                       : static_cast<const WT*>(a.w13) + (size_t)t.expert * 2 * a.I * a.H / Fr::kPack;
+  const WT* wrow = W + ((size_t)wr * a.H + kbeg + kg * Fr::kGroupK) / Fr::kPack;
+  const void* wscale = nullptr;
   if constexpr (F == WFmt::FP8) {
-    const float* S = shared ? a.sw13_scale : a.w13_scale + (size_t)t.expert * (2 * a.I / 128) * (a.H / 128);
+    const float* S = static_cast<const float*>(shared ? a.sw13_scale : a.w13_scale);
+    if (!shared) S += (size_t)t.expert * (2 * a.I / 128) * (a.H / 128);
     wscale = S + (size_t)(wr / 128) * (a.H / 128) + kbeg / 128;
+  } else if constexpr (F == WFmt::FP4) {
+    const uint8_t* S = static_cast<const uint8_t*>(shared ? a.sw13_scale : a.w13_scale);
+    if (!shared) S += (size_t)t.expert * 2 * a.I * (a.H / 32);
+    wscale = S + (size_t)wr * (a.H / 32) + kbeg / 32;
   }
   const AT* arow[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = mt * 16 + col;
     const int src = m < t.rows ? (shared ? t.start + m : a.pair_row[t.start + m]) : -1;
-    arow[mt] = src >= 0 ? static_cast<const AT*>(a.x) + (size_t)src * a.H + kbeg + kg * Fr::kLane : nullptr;
+    arow[mt] = src >= 0 ? static_cast<const AT*>(a.x) + (size_t)src * a.H + kbeg + kg * Fr::kGroupK : nullptr;
   }
   f32x4 acc[MT];
   if (wave < ks) {
@@ -203,9 +232,9 @@ __global__ __launch_bounds__(256) void expert_up_kernel(UpArgs a) {
 
 struct DownArgs {
   const void* w2;
-  const float* w2_scale;
+  const void* w2_scale;
   const void* sw2;
-  const float* sw2_scale;
+  const void* sw2_scale;
   const Tile* tiles;
   const int32_t* tile_count;
   const void* h;
@@ -224,12 +253,17 @@ __device__ __forceinline__ void down_tile(const DownArgs& a, const Tile& t, int 
   const int inter = shared ? a.Is : a.I;
   const int c0 = slice * kDownCols + wave * 16;
   const WT* W = shared ? static_cast<const WT*>(a.sw2)
-                       : static_cast<const WT*>(a.w2) + (size_t)t.expert * a.H * a.I;
-  const WT* wrow = W + (size_t)(c0 + col) * inter + kg * Fr::kLane;
-  const float* wscale = nullptr;
+                       : static_cast<const WT*>(a.w2) + (size_t)t.expert * a.H * a.I / Fr::kPack;
+  const WT* wrow = W + ((size_t)(c0 + col) * inter + kg * Fr::kGroupK) / Fr::kPack;
+  const void* wscale = nullptr;
   if constexpr (F == WFmt::FP8) {
-    const float* S = shared ? a.sw2_scale : a.w2_scale + (size_t)t.expert * (a.H / 128) * (a.I / 128);
+    const float* S = static_cast<const float*>(shared ? a.sw2_scale : a.w2_scale);
+    if (!shared) S += (size_t)t.expert * (a.H / 128) * (a.I / 128);
     wscale = S + (size_t)((c0 + col) / 128) * (inter / 128);
+  } else if constexpr (F == WFmt::FP4) {
+    const uint8_t* S = static_cast<const uint8_t*>(shared ? a.sw2_scale : a.w2_scale);
+    if (!shared) S += (size_t)t.expert * a.H * (a.I / 32);
+    wscale = S + (size_t)(c0 + col) * (inter / 32);
   }
   const AT* hbase = static_cast<const AT*>(a.h) +
                     (shared ? (size_t)a.N * a.K * a.I + (size_t)t.start * a.Is : (size_t)t.start * a.I);
@@ -237,7 +271,7 @@ __device__ __forceinline__ void down_tile(const DownArgs& a, const Tile& t, int 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = mt * 16 + col;
-    arow[mt] = m < t.rows ? hbase + (size_t)m * inter + kg * Fr::kLane : nullptr;
+    arow[mt] = m < t.rows ? hbase + (size_t)m * inter + kg * Fr::kGroupK : nullptr;
   }
   f32x4 acc[MT];
   wave_gemm<F, MT>(wrow, arow, inter, wscale, acc);
@@ -289,10 +323,12 @@ static void dispatch(WFmt f, int mt_max, unsigned grid, hipStream_t s, const Arg
     case WFmt::BF16: dispatch_mt<WFmt::BF16, Kern>(mt_max, grid, s, a); break;
     case WFmt::F32: dispatch_mt<WFmt::F32, Kern>(mt_max, grid, s, a); break;
     case WFmt::FP8: dispatch_mt<WFmt::FP8, Kern>(mt_max, grid, s, a); break;
+    case WFmt::FP4: dispatch_mt<WFmt::FP4, Kern>(mt_max, grid, s, a); break;
   }
 }
 
 static WFmt fmt_of(const Plan& p) {
+  if (p.wt == CMOE_FP4_E2M1) return WFmt::FP4;
   if (p.wt == CMOE_FP8_E4M3) return WFmt::FP8;
   if (p.wt == CMOE_F32) return WFmt::F32;
   return WFmt::BF16;

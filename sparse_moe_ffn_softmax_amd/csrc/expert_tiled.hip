@@ -6,7 +6,9 @@
 //
 // SwiGLU experts plus a shared expert (Clover-35B-A3B-Preview CMF model card,
 // introduction); fp8 weights are E4M3 with one fp32 scale per 128x128 block
-// and bf16 activations (InfiniLM PR #584, "Benchmark").
+// and bf16 activations (InfiniLM PR #584, "Benchmark"); 4-bit weights are
+// MXFP4 (E2M1 codes, E8M0 scale per 32 elements of a row), widened to bf16
+// exactly with their scale.
 //
 // With tens of rows per expert every weight byte feeds tens of MFMA rows, so
 // the activation tile must not be fetched once per wave.  A workgroup
@@ -36,9 +38,9 @@ constexpr int kTiledDownCols = 16 * kTiledWaves;  // y columns per workgroup
 struct TiledArgs {
   const void* x;     // up: activations [N,H]
   const void* w;     // up: W13 [E,2I,H]; down: W2 [E,H,I]
-  const float* ws;   // fp8 scales of w
+  const void* ws;    // scales of w (fp8: fp32 per 128x128 block; fp4: E8M0 per 32 of a row)
   const void* sw;    // shared expert's matrix
-  const float* sws;  // its fp8 scales
+  const void* sws;   // its scales
   const Tile* tiles;
   const int32_t* tile_count;
   const int32_t* pair_row;
@@ -86,13 +88,18 @@ struct TiledGemm {
   static constexpr bool kPair = (F == WFmt::FP8);
   static_assert(!kPair || U % 2 == 0, "paired fp8 steps");
   static __device__ __forceinline__ int koff(int u, int kg) {
-    return kPair ? 64 * (u / 2) + 16 * kg + 8 * (u % 2) : u * Fr::kStep + kg * Fr::kLane;
+    return kPair ? 64 * (u / 2) + 16 * kg + 8 * (u % 2) : u * Fr::kStepK + kg * Fr::kGroupK;
   }
   // this lane's first weight byte of a stage, relative to its weight row
-  static __device__ __forceinline__ int blane(int kg) { return kPair ? 16 * kg : kg * Fr::kLane; }
+  static __device__ __forceinline__ int blane(int kg) { return kPair ? 16 * kg : kg * Fr::kGroupK / Fr::kPack; }
+  // one stage of this lane's weights; fp4 adds the stage's four E8M0 bytes of its row
+  struct BSet {
+    typename Fr::B b[U];
+    uint32_t sc;
+  };
 
   static __device__ __forceinline__ void run(Lds& As, const AT* const (&asrc)[AV],
-                                             const WT* brow, const float* bsc, int Kdim,
+                                             const WT* brow, const void* bsc, int Kdim,
                                              f32x4 (&acc)[MT]) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int col = lane & 15, kg = lane >> 4;
@@ -101,7 +108,7 @@ struct TiledGemm {
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     u32x4 areg[AV];
-    typename Fr::B b0[U], b1[U];
+    BSet b0, b1;
     auto load_a = [&](int k0) {
 #pragma unroll
       for (int i = 0; i < AV; ++i)
@@ -112,8 +119,17 @@ struct TiledGemm {
       for (int i = 0; i < AV; ++i)
         *reinterpret_cast<u32x4*>(&As[buf][r0 + i * RPP][seg * (16 / (int)sizeof(AT))]) = areg[i];
     };
-    auto load_b = [&](typename Fr::B (&b)[U], int k0) {
-      if constexpr (kPair) {
+    auto load_b = [&](BSet& bs, int k0) {
+      auto& b = bs.b;
+      if constexpr (F == WFmt::FP4) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(brow + k0 / 2);
+#pragma unroll
+        for (int u = 0; u < U; ++u) b[u] = v[u];
+        bs.sc = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(bsc) + k0 / 32);
+        // keep the next stage's loads ahead of this stage's scale use, which
+        // would otherwise be hoisted and wait for every load in flight
+        __builtin_amdgcn_sched_barrier(0);
+      } else if constexpr (kPair) {
 #pragma unroll
         for (int j = 0; j < U / 2; ++j) {
           const u32x4 v = *reinterpret_cast<const u32x4*>(brow + k0 + 64 * j);
@@ -128,8 +144,20 @@ struct TiledGemm {
     // Every row tile runs (rows past the tile are zeros in LDS): a guard per
     // row tile would make each MFMA wait for its own LDS read.  Per k step the
     // MT activation fragments are read first, then the MT MFMAs issue.
-    auto compute = [&](typename Fr::B (&b)[U], int buf, int k0) {
-      if constexpr (F == WFmt::FP8) {
+    auto compute = [&](BSet& bs, int buf, int k0) {
+      auto& b = bs.b;
+      if constexpr (F == WFmt::FP4) {
+        const float sc = Fr::scale_of((bs.sc >> (8 * kg)) & 0xFFu);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          typename Fr::A av[MT];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) av[mt] = Fr::load_a(&As[buf][mt * 16 + col][koff(u, kg)]);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[mt] = Fr::mma(av[mt], b[u], sc, acc[mt]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else if constexpr (F == WFmt::FP8) {
         f32x4 tmp[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) tmp[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -142,7 +170,7 @@ struct TiledGemm {
           for (int mt = 0; mt < MT; ++mt) tmp[mt] = Fr::mma(av[mt], b[u], tmp[mt]);
           __builtin_amdgcn_sched_barrier(0);
         }
-        const float sc = bsc[k0 / 128];
+        const float sc = static_cast<const float*>(bsc)[k0 / 128];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -259,13 +287,21 @@ __global__ __launch_bounds__(kTiledThreads) void expert_up_tiled_kernel(TiledArg
     const int src = shared ? t.start + rr : a.pair_row[t.start + rr];
     asrc[i] = static_cast<const AT*>(a.x) + (size_t)src * H + (tid % G::VPR) * (16 / (int)sizeof(AT));
   }
-  const WT* W = shared ? static_cast<const WT*>(a.sw) : static_cast<const WT*>(a.w) + (size_t)t.expert * 2 * a.I * H;
-  const float* S = nullptr;
-  if constexpr (F == WFmt::FP8) S = shared ? a.sws : a.ws + (size_t)t.expert * (2 * a.I / 128) * (H / 128);
+  const WT* W = shared ? static_cast<const WT*>(a.sw)
+                       : static_cast<const WT*>(a.w) + (size_t)t.expert * 2 * a.I * H / Frag<F>::kPack;
   const int i0 = slice * kTiledUpCols + wave * 8;
   const int wr = col < 8 ? i0 + col : inter + i0 + col - 8;  // gate row / up row
-  const WT* brow = W + (size_t)wr * H + G::blane(kg);
+  const WT* brow = W + (size_t)wr * H / Frag<F>::kPack + G::blane(kg);
+  const void* bsc = sc_s[col < 8 ? 0 : 1];
+  if constexpr (F == WFmt::FP4) {
+    // this lane's row of E8M0 bytes, read stage by stage
+    const uint8_t* S = static_cast<const uint8_t*>(shared ? a.sws : a.ws);
+    if (!shared) S += (size_t)t.expert * 2 * a.I * (H / 32);
+    bsc = S + (size_t)wr * (H / 32);
+  }
   if constexpr (F == WFmt::FP8) {
+    const float* S = static_cast<const float*>(shared ? a.sws : a.ws);
+    if (!shared) S += (size_t)t.expert * (2 * a.I / 128) * (H / 128);
     // the workgroup's gate rows share one 128-row scale block, its up rows
     // another; the first stage's barrier orders these writes before any read
     const int ns = H / 128;
@@ -273,7 +309,7 @@ __global__ __launch_bounds__(kTiledThreads) void expert_up_tiled_kernel(TiledArg
     for (int i = tid; i < 2 * ns; i += kTiledThreads) sc_s[i / ns][i % ns] = S[(size_t)srow[i / ns] * ns + i % ns];
   }
   f32x4 acc[MT];
-  G::run(As, asrc, brow, sc_s[col < 8 ? 0 : 1], H, acc);
+  G::run(As, asrc, brow, bsc, H, acc);
 
   AT* h = static_cast<AT*>(a.h) +
           (shared ? (size_t)a.N * a.K * a.I + (size_t)t.start * a.Is : (size_t)t.start * a.I);
@@ -313,19 +349,26 @@ __global__ __launch_bounds__(kTiledThreads) void expert_down_tiled_kernel(TiledA
     const int r = tid / G::VPR + i * G::RPP;
     asrc[i] = hb + (size_t)(r < t.rows ? r : 0) * inter + (tid % G::VPR) * (16 / (int)sizeof(AT));
   }
-  const WT* W = shared ? static_cast<const WT*>(a.sw) : static_cast<const WT*>(a.w) + (size_t)t.expert * H * a.I;
-  const float* S = nullptr;
-  if constexpr (F == WFmt::FP8) S = shared ? a.sws : a.ws + (size_t)t.expert * (H / 128) * (a.I / 128);
+  const WT* W = shared ? static_cast<const WT*>(a.sw)
+                       : static_cast<const WT*>(a.w) + (size_t)t.expert * H * a.I / Frag<F>::kPack;
   const int c0 = slice * kTiledDownCols + wave * 16;
   const int orow = c0 + col;  // W2 row = output column
-  const WT* brow = W + (size_t)orow * inter + G::blane(kg);
+  const WT* brow = W + (size_t)orow * inter / Frag<F>::kPack + G::blane(kg);
+  const void* bsc = sc_s[0];
+  if constexpr (F == WFmt::FP4) {
+    const uint8_t* S = static_cast<const uint8_t*>(shared ? a.sws : a.ws);
+    if (!shared) S += (size_t)t.expert * H * (a.I / 32);
+    bsc = S + (size_t)orow * (inter / 32);
+  }
   if constexpr (F == WFmt::FP8) {
     // the workgroup's 128 output rows are one scale block row
+    const float* S = static_cast<const float*>(shared ? a.sws : a.ws);
+    if (!shared) S += (size_t)t.expert * (H / 128) * (a.I / 128);
     const int ns = inter / 128;
     for (int i = tid; i < ns; i += kTiledThreads) sc_s[0][i] = S[(size_t)slice * ns + i];
   }
   f32x4 acc[MT];
-  G::run(As, asrc, brow, sc_s[0], inter, acc);
+  G::run(As, asrc, brow, bsc, inter, acc);
 
   const size_t y0 = ((shared ? (size_t)a.N * a.K : 0) + (size_t)t.start) * H;
 #pragma unroll
@@ -381,13 +424,18 @@ hipError_t launch_expert_tiled(const Plan& p, const cmoe_weights& w, const void*
   a.K = p.K;
   a.n_slices = up ? (p.I > p.Is ? p.I : p.Is) / kTiledUpCols : p.H / kTiledDownCols;
   const unsigned grid = tile_grid(p.max_tiles, a.n_slices);
-  const WFmt f = p.wt == CMOE_FP8_E4M3 ? WFmt::FP8 : p.wt == CMOE_F32 ? WFmt::F32 : WFmt::BF16;
+  const WFmt f = p.wt == CMOE_FP4_E2M1   ? WFmt::FP4
+                 : p.wt == CMOE_FP8_E4M3 ? WFmt::FP8
+                 : p.wt == CMOE_F32      ? WFmt::F32
+                                         : WFmt::BF16;
   if (up) {
-    if (f == WFmt::FP8) launch_tiled_mt<true, WFmt::FP8>(a, p.mt_max, grid, s);
+    if (f == WFmt::FP4) launch_tiled_mt<true, WFmt::FP4>(a, p.mt_max, grid, s);
+    else if (f == WFmt::FP8) launch_tiled_mt<true, WFmt::FP8>(a, p.mt_max, grid, s);
     else if (f == WFmt::F32) launch_tiled_mt<true, WFmt::F32>(a, p.mt_max, grid, s);
     else launch_tiled_mt<true, WFmt::BF16>(a, p.mt_max, grid, s);
   } else {
-    if (f == WFmt::FP8) launch_tiled_mt<false, WFmt::FP8>(a, p.mt_max, grid, s);
+    if (f == WFmt::FP4) launch_tiled_mt<false, WFmt::FP4>(a, p.mt_max, grid, s);
+    else if (f == WFmt::FP8) launch_tiled_mt<false, WFmt::FP8>(a, p.mt_max, grid, s);
     else if (f == WFmt::F32) launch_tiled_mt<false, WFmt::F32>(a, p.mt_max, grid, s);
     else launch_tiled_mt<false, WFmt::BF16>(a, p.mt_max, grid, s);
   }

@@ -25,6 +25,8 @@ ROUTING_KEYS = ("logits", "block_mass", "coreset_ids", "coreset_size", "topk_idx
 TOL = {
     W.BF16: dict(max_rel=2e-2, mean_rel=5e-3),
     W.FP8: dict(max_rel=6e-2, mean_rel=None),
+    # 4-bit weights widen to bf16 exactly (code times a power of two): the bf16 bar
+    W.FP4: dict(max_rel=2e-2, mean_rel=5e-3),
     W.F32: dict(max_rel=1e-4, mean_rel=5e-3),
 }
 

@@ -132,6 +132,8 @@ def test_invalid_calls_rejected(kw, expect):
     (dict(act_dtype="f32", weight_dtype="bf16"), 8, cm.CMOE_ERR_UNSUPPORTED),
     (dict(act_dtype="f32", weight_dtype="fp8_e4m3"), 8, cm.CMOE_ERR_UNSUPPORTED),
     (dict(act_dtype="fp8_e4m3", weight_dtype="fp8_e4m3"), 8, cm.CMOE_ERR_UNSUPPORTED),
+    (dict(act_dtype="f32", weight_dtype="fp4_e2m1"), 8, cm.CMOE_ERR_UNSUPPORTED),
+    (dict(act_dtype="fp4_e2m1", weight_dtype="fp4_e2m1"), 8, cm.CMOE_ERR_UNSUPPORTED),
 ])
 def test_invalid_problems_rejected(pkw, k, expect):
     assert call(prob=problem(**pkw), k=k) == expect
@@ -149,6 +151,10 @@ def test_missing_weights_rejected():
     fp8 = problem(weight_dtype="fp8_e4m3")
     assert call(prob=fp8, w=weights(fp8=True, w2_scale=None)) == cm.CMOE_ERR_NULL
     assert call(prob=fp8, w=weights(fp8=True, shared_w13_scale=None)) == cm.CMOE_ERR_NULL
+    fp4 = problem(weight_dtype="fp4_e2m1")
+    assert call(prob=fp4, w=weights(fp8=False)) == cm.CMOE_ERR_NULL
+    assert call(prob=fp4, w=weights(fp8=True, w13_scale=None)) == cm.CMOE_ERR_NULL
+    assert call(prob=fp4, w=weights(fp8=True, w2_scale=fake(7, 8))) == cm.CMOE_ERR_ALIGN
     assert call(w=weights(router_b=fake(13, 4))) == cm.CMOE_ERR_ALIGN
 
 

@@ -102,6 +102,21 @@ def test_threshold_on_a_prefix_sum_takes_the_serial_cut(tau, m):
     assert np.all(ref["coreset_size"] == m)
 
 
+# 4-bit experts (MXFP4: E2M1 codes, E8M0 scale per 32 elements), widened to
+# bf16 exactly in both kernel families
+@pytest.mark.parametrize("wl", [
+    MID.with_(name="mid_fp4", weight_dtype=W.FP4, seed=101),
+    MID.with_(name="mid_fp4_Is_ne_I", weight_dtype=W.FP4, inter=128, shared_inter=384, seed=102),
+    MID.with_(name="mid_fp4_noshared", weight_dtype=W.FP4, shared_inter=0, seed=103),
+    FEW.with_(name="few_fp4", weight_dtype=W.FP4, seed=104),
+    FEW.with_(name="few_fp4_rows1", weight_dtype=W.FP4, block_rows=1, num_blocks=3, seed=105),
+    MID.with_(name="mid_fp4_live50_budget6", weight_dtype=W.FP4, live_fraction=0.5, expert_budget=6,
+              seed=106),
+], ids=lambda w: w.name)
+def test_fp4_weights(wl):
+    check(W.generate(wl))
+
+
 # decode (one row per block) and verification (2-4 rows) calls: rows past R in
 # the routing kernel's row groups must add nothing to the block mass
 @pytest.mark.parametrize("wl,tau", [
@@ -161,7 +176,7 @@ def test_full_route_without_mass_outputs(wl):
 # full-size workloads
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["decode1_bf16", "verify4_bf16", "block32_budget64_live50"])
+@pytest.mark.parametrize("name", ["decode1_bf16", "verify4_bf16", "block32_budget64_live50", "block32_mxfp4"])
 def test_decode_verify_full(name):
     check(W.generate(W.WORKLOADS[name]), threads=16)
 

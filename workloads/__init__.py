@@ -91,6 +91,8 @@ WORKLOADS: Dict[str, Workload] = {
     # 64 experts, half of whose rows are live (the others reuse cached outputs)
     "block32_budget64_live50": Workload("block32_budget64_live50", 1, 32, 2048, 256, 8, 512, 512, BF16,
                                         BF16, 0.9, seed=7, expert_budget=64, live_fraction=0.5),
+    # one 32-row block with 4-bit experts (MXFP4 stand-in), bf16 activations
+    "block32_mxfp4": Workload("block32_mxfp4", 1, 32, 2048, 256, 8, 512, 512, BF16, FP4, 0.9, seed=8),
 }
 
 # Threshold / top-k sweep run on the skewed workload (1.0 = unrestricted top-k;
