@@ -21,10 +21,13 @@
 //                 accumulator); the 4 waves split the hidden dimension and
 //                 their partial sums meet in LDS, added in wave order;
 //   expert_down : 64 y columns, 16 per wave.
+// 4-bit weights are four times smaller, so there a wave takes four (up) or
+// four or two (down, by H) such column tiles, and each activation fragment it
+// loads feeds one MFMA per column tile.
 // Each wave streams its 16 weight rows straight from HBM into MFMA operand
 // registers (no LDS: every weight byte is used by exactly one wave), and the
-// gathered activation rows come from L2.  Rows of a tile beyond its count are
-// zero-filled on load and never stored.
+// gathered activation rows come from L2.  Rows of a tile beyond its count
+// repeat its first row and are never stored.
 //
 // MFMA operand layout (v_mfma_f32_16x16x32_bf16, checked on gfx950): lane l
 // supplies A[l%16][8*(l/16) .. +8] and B[8*(l/16) .. +8][l%16], and receives
@@ -50,93 +53,134 @@ namespace cmoe {
 // ---------------------------------------------------------------------------
 // one wave: acc[mt] (16 rows x 16 cols) = sum_k A_mt[:, k] * W[col, k] over
 // k in [0, K).  wrow: pointer to this lane's weight row at its k offset;
-// arow[mt]: this lane's activation row at its k offset, or nullptr (zeros).
+// arow[mt]: this lane's activation row at its k offset.
 // For fp8, wscale points at this lane's row of 128x128 block scales.
 //
 // K is consumed in stages of 128; the loads of stage s+1 are issued before
 // the MFMAs of stage s, so each wave always has a stage of weights in flight
 // (two register buffers, alternating).
 // ---------------------------------------------------------------------------
-template <WFmt F, int MT>
+template <WFmt F, int MT, int NCT>
 struct Stage {
   static constexpr int U = 128 / Frag<F>::kStep;  // MFMA steps per stage
-  typename Frag<F>::B b[U];
+  typename Frag<F>::B b[NCT][U];
   typename Frag<F>::A a[MT][U];
-  uint32_t sc;  // fp4: the stage's four E8M0 scale bytes of this lane's row
+  uint32_t sc[NCT];  // fp4: the stage's four E8M0 scale bytes of each weight row
 };
 
-// wrow: this lane's weight row at its first k of the wave's range (WT units);
-// wscale: fp8: its row of 128x128 block scales at that k (fp32); fp4: its row
-// of E8M0 bytes at that k.
-template <WFmt F, int MT>
-__device__ __forceinline__ void load_stage(Stage<F, MT>& st, const typename Frag<F>::WT* __restrict__ wrow,
-                                           const void* __restrict__ wscale,
+// A wave computes NCT column tiles (16 weight rows each) over the same MT row
+// tiles, so each activation fragment feeds NCT MFMAs.  wrow[c]: this lane's
+// row of column tile c at its first k of the wave's range (WT units);
+// wscale[c]: fp8: that row's 128x128 block scales at that k (fp32); fp4: its
+// E8M0 bytes at that k.
+template <WFmt F, int MT, int NCT>
+__device__ __forceinline__ void load_stage(Stage<F, MT, NCT>& st,
+                                           const typename Frag<F>::WT* const (&wrow)[NCT],
+                                           const void* const (&wscale)[NCT],
                                            const typename Frag<F>::AT* const (&arow)[MT], int k0) {
   using Fr = Frag<F>;
-  if constexpr (F == WFmt::FP4) {
-    // 32 codes (k 32kg .. +32 of the stage) in one load, and the stage's scales
-    const u32x4 v = *reinterpret_cast<const u32x4*>(wrow + k0 / 2);
+  constexpr int U = Stage<F, MT, NCT>::U;
 #pragma unroll
-    for (int u = 0; u < Stage<F, MT>::U; ++u) st.b[u] = v[u];
-    st.sc = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(wscale) + k0 / 32);
-  } else {
+  for (int c = 0; c < NCT; ++c) {
+    if constexpr (F == WFmt::FP4) {
+      // 32 codes (k 32kg .. +32 of the stage) in one load, and the stage's scales
+      const u32x4 v = *reinterpret_cast<const u32x4*>(wrow[c] + k0 / 2);
 #pragma unroll
-    for (int u = 0; u < Stage<F, MT>::U; ++u) st.b[u] = Fr::load_b(wrow + k0 + u * Fr::kStep);
+      for (int u = 0; u < U; ++u) st.b[c][u] = v[u];
+      st.sc[c] = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(wscale[c]) + k0 / 32);
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) st.b[c][u] = Fr::load_b(wrow[c] + k0 + u * Fr::kStep);
+    }
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int u = 0; u < Stage<F, MT>::U; ++u)
-      st.a[mt][u] = arow[mt] ? Fr::load_a(arow[mt] + k0 + u * Fr::kStepK) : Fr::zero_a();
+    for (int u = 0; u < U; ++u)
+      st.a[mt][u] = Fr::load_a(arow[mt] + k0 + u * Fr::kStepK);
 }
 
-template <WFmt F, int MT>
-__device__ __forceinline__ void mma_stage(const Stage<F, MT>& st, const void* __restrict__ wscale,
-                                          int k0, f32x4 (&acc)[MT]) {
+template <WFmt F, int MT, int NCT>
+__device__ __forceinline__ void mma_stage(const Stage<F, MT, NCT>& st, const void* const (&wscale)[NCT],
+                                          int k0, f32x4 (&acc)[NCT][MT]) {
   using Fr = Frag<F>;
-  constexpr int U = Stage<F, MT>::U;
+  constexpr int U = Stage<F, MT, NCT>::U;
   if constexpr (F == WFmt::FP4) {
     const int kg = (threadIdx.x & 63) >> 4;
-    const float sc = Fr::scale_of((st.sc >> (8 * kg)) & 0xFFu);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int c = 0; c < NCT; ++c) {
+      const float sc = Fr::scale_of((st.sc[c] >> (8 * kg)) & 0xFFu);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] = Fr::mma(st.a[mt][u], st.b[u], sc, acc[mt]);
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[c][mt] = Fr::mma(st.a[mt][u], st.b[c][u], sc, acc[c][mt]);
+    }
   } else if constexpr (F == WFmt::FP8) {
-    const float s = static_cast<const float*>(wscale)[k0 / 128];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NCT; ++c) {
+      const float s = static_cast<const float*>(wscale[c])[k0 / 128];
 #pragma unroll
-      for (int u = 0; u < U; ++u) t = Fr::mma(st.a[mt][u], st.b[u], t);
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[mt][v] = __builtin_fmaf(s, t[v], acc[mt][v]);
+        for (int u = 0; u < U; ++u) t = Fr::mma(st.a[mt][u], st.b[c][u], t);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[c][mt][v] = __builtin_fmaf(s, t[v], acc[c][mt][v]);
+      }
     }
   } else {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] = Fr::mma(st.a[mt][u], st.b[u], acc[mt]);
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[c][mt] = Fr::mma(st.a[mt][u], st.b[c][u], acc[c][mt]);
   }
 }
 
-template <WFmt F, int MT>
-__device__ __forceinline__ void wave_gemm(const typename Frag<F>::WT* __restrict__ wrow,
+// register words one stage holds per lane
+template <WFmt F, int MT, int NCT>
+constexpr int stage_words() { return (int)(sizeof(Stage<F, MT, NCT>) / 4); }
+
+template <WFmt F, int MT, int NCT>
+__device__ __forceinline__ void wave_gemm(const typename Frag<F>::WT* const (&wrow)[NCT],
                                           const typename Frag<F>::AT* const (&arow)[MT], int K,
-                                          const void* __restrict__ wscale, f32x4 (&acc)[MT]) {
+                                          const void* const (&wscale)[NCT], f32x4 (&acc)[NCT][MT]) {
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  Stage<F, MT> s0, s1;
-  load_stage<F, MT>(s0, wrow, wscale, arow, 0);
+  for (int c = 0; c < NCT; ++c)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[c][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // 4-bit weights, K = 512 (the hidden size split four ways, or the expert
+  // width): issue all four stages' loads at once, then consume them in order.
+  // Straight-line code lets the compiler wait for exactly the stage it needs.
+  // (For bf16 the extra registers cost more occupancy than the deeper queue
+  // gains: the two-stage loop below measured about 5% faster there.)
+  if constexpr (F == WFmt::FP4 && 4 * stage_words<F, MT, NCT>() <= 160) {
+    if (K == 512) {
+      Stage<F, MT, NCT> st[4];
+      static_for<0, 4>([&](auto S) { load_stage<F, MT, NCT>(st[S], wrow, wscale, arow, S * 128); });
+      __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the first MFMA
+      static_for<0, 4>([&](auto S) { mma_stage<F, MT, NCT>(st[S], wscale, S * 128, acc); });
+      return;
+    }
+  }
+  Stage<F, MT, NCT> s0, s1;
+  load_stage<F, MT, NCT>(s0, wrow, wscale, arow, 0);
   for (int k0 = 0; k0 < K; k0 += 256) {
     const bool two = k0 + 128 < K;
-    if (two) load_stage<F, MT>(s1, wrow, wscale, arow, k0 + 128);
-    mma_stage<F, MT>(s0, wscale, k0, acc);
+    if (two) load_stage<F, MT, NCT>(s1, wrow, wscale, arow, k0 + 128);
+    mma_stage<F, MT, NCT>(s0, wscale, k0, acc);
     if (!two) break;
-    if (k0 + 256 < K) load_stage<F, MT>(s0, wrow, wscale, arow, k0 + 256);
-    mma_stage<F, MT>(s1, wscale, k0 + 128, acc);
+    if (k0 + 256 < K) load_stage<F, MT, NCT>(s0, wrow, wscale, arow, k0 + 256);
+    mma_stage<F, MT, NCT>(s1, wscale, k0 + 128, acc);
   }
 }
+
+// column tiles per wave: 4-bit weights stream four times fewer bytes per
+// tile, so a wave takes four tiles (the same bytes per workgroup as bf16)
+template <WFmt F>
+constexpr int up_nct() { return F == WFmt::FP4 ? 4 : 1; }
+inline int down_nct(WFmt f, int H) { return f == WFmt::FP4 ? (H % 256 == 0 ? 4 : 2) : 1; }
 
 struct UpArgs {
   const void* x;
@@ -151,83 +195,99 @@ struct UpArgs {
   int N, H, E, I, Is, K, n_slices;
 };
 
-template <WFmt F, int MT>
+template <WFmt F, int MT, int NCT>
 __device__ __forceinline__ void up_tile(const UpArgs& a, const Tile& t, int slice) {
   using Fr = Frag<F>;
   using AT = typename Fr::AT;
   using WT = typename Fr::WT;
-  __shared__ f32x4 red[4][MT][64];
+  __shared__ f32x4 red[4][NCT][MT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kg = lane >> 4;
   const bool shared = t.expert == a.E;
   const int inter = shared ? a.Is : a.I;
-  const int i0 = slice * kUpCols;
-  const int wr = col < 8 ? i0 + col : inter + i0 + col - 8;  // gate row / up row
+  const int i0 = slice * kUpCols * NCT;  // column tile c: h columns i0 + 8c .. +8
   // the waves split the hidden dimension into ks equal parts (multiples of 128)
   const int ks = (a.H % 512 == 0) ? 4 : (a.H % 256 == 0) ? 2 : 1;
   const int klen = a.H / ks, kbeg = wave * klen;
   const WT* W = shared ? static_cast<const WT*>(a.sw13)
                        : static_cast<const WT*>(a.w13) + (size_t)t.expert * 2 * a.I * a.H / Fr::kPack;
-  const WT* wrow = W + ((size_t)wr * a.H + kbeg + kg * Fr::kGroupK) / Fr::kPack;
-  const void* wscale = nullptr;
-  if constexpr (F == WFmt::FP8) {
-    const float* S = static_cast<const float*>(shared ? a.sw13_scale : a.w13_scale);
-    if (!shared) S += (size_t)t.expert * (2 * a.I / 128) * (a.H / 128);
-    wscale = S + (size_t)(wr / 128) * (a.H / 128) + kbeg / 128;
-  } else if constexpr (F == WFmt::FP4) {
-    const uint8_t* S = static_cast<const uint8_t*>(shared ? a.sw13_scale : a.w13_scale);
-    if (!shared) S += (size_t)t.expert * 2 * a.I * (a.H / 32);
-    wscale = S + (size_t)wr * (a.H / 32) + kbeg / 32;
+  const WT* wrow[NCT];
+  const void* wscale[NCT];
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) {
+    const int ic = i0 + 8 * c;
+    const int wr = col < 8 ? ic + col : inter + ic + col - 8;  // gate row / up row
+    wrow[c] = W + ((size_t)wr * a.H + kbeg + kg * Fr::kGroupK) / Fr::kPack;
+    wscale[c] = nullptr;
+    if constexpr (F == WFmt::FP8) {
+      const float* S = static_cast<const float*>(shared ? a.sw13_scale : a.w13_scale);
+      if (!shared) S += (size_t)t.expert * (2 * a.I / 128) * (a.H / 128);
+      wscale[c] = S + (size_t)(wr / 128) * (a.H / 128) + kbeg / 128;
+    } else if constexpr (F == WFmt::FP4) {
+      const uint8_t* S = static_cast<const uint8_t*>(shared ? a.sw13_scale : a.w13_scale);
+      if (!shared) S += (size_t)t.expert * 2 * a.I * (a.H / 32);
+      wscale[c] = S + (size_t)wr * (a.H / 32) + kbeg / 32;
+    }
   }
+  // rows past the tile's count read the tile's first row (every load is
+  // unconditional, so the compiler can keep the next stage in flight); an
+  // MFMA output row depends only on its own A row and those rows are never
+  // stored
   const AT* arow[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int m = mt * 16 + col;
-    const int src = m < t.rows ? (shared ? t.start + m : a.pair_row[t.start + m]) : -1;
-    arow[mt] = src >= 0 ? static_cast<const AT*>(a.x) + (size_t)src * a.H + kbeg + kg * Fr::kGroupK : nullptr;
+    const int m = mt * 16 + col < t.rows ? mt * 16 + col : 0;
+    const int src = shared ? t.start + m : a.pair_row[t.start + m];
+    arow[mt] = static_cast<const AT*>(a.x) + (size_t)src * a.H + kbeg + kg * Fr::kGroupK;
   }
-  f32x4 acc[MT];
+  f32x4 acc[NCT][MT];
   if (wave < ks) {
-    wave_gemm<F, MT>(wrow, arow, klen, wscale, acc);
+    wave_gemm<F, MT, NCT>(wrow, arow, klen, wscale, acc);
   } else {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NCT; ++c)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[c][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) red[wave][mt][lane] = acc[mt];
+  for (int c = 0; c < NCT; ++c)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) red[wave][c][mt][lane] = acc[c][mt];
   __syncthreads();
-  // wave w finishes M-tile w: sum the k parts in wave order, then SwiGLU
-  if (wave >= MT) return;
-  const int mt = wave;
-  f32x4 z = red[0][mt][lane];
-  for (int w = 1; w < ks; ++w) {
-    const f32x4 o = red[w][mt][lane];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) z[v] = z[v] + o[v];
-  }
+  // wave w finishes output tiles w, w+4, ... (column tile c, row tile mt): sum
+  // the k parts in wave order, then SwiGLU
   AT* h = static_cast<AT*>(a.h) +
           (shared ? (size_t)a.N * a.K * a.I + (size_t)t.start * a.Is : (size_t)t.start * a.I);
+  for (int idx = wave; idx < NCT * MT; idx += 4) {
+    const int c = idx % NCT, mt = idx / NCT;
+    f32x4 z = red[0][c][mt][lane];
+    for (int w = 1; w < ks; ++w) {
+      const f32x4 o = red[w][c][mt][lane];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const float g = z[v];
-    const float up = shfl_xor_f(g, 8);
-    const int m = mt * 16 + kg * 4 + v;
-    if (col < 8 && m < t.rows) store_act<AT>(h + (size_t)m * inter + i0 + col, silu(g) * up);
+      for (int v = 0; v < 4; ++v) z[v] = z[v] + o[v];
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float g = z[v];
+      const float up = shfl_xor_f(g, 8);
+      const int m = mt * 16 + kg * 4 + v;
+      if (col < 8 && m < t.rows) store_act<AT>(h + (size_t)m * inter + i0 + 8 * c + col, silu(g) * up);
+    }
   }
 }
 
-template <WFmt F, int MTMAX>
+template <WFmt F, int MTMAX, int NCT>
 __global__ __launch_bounds__(256) void expert_up_kernel(UpArgs a) {
   const int slot = blockIdx.x / a.n_slices, slice = blockIdx.x % a.n_slices;
   if (slot >= *a.tile_count) return;
   const Tile t = a.tiles[slot];
   const int inter = t.expert == a.E ? a.Is : a.I;
-  if (slice * kUpCols >= inter) return;
+  if (slice * kUpCols * NCT >= inter) return;
   const int mt = (t.rows + 15) >> 4;  // 1..MTMAX
-  if constexpr (MTMAX >= 4) if (mt == 4) { up_tile<F, 4>(a, t, slice); return; }
-  if constexpr (MTMAX >= 3) if (mt == 3) { up_tile<F, 3>(a, t, slice); return; }
-  if constexpr (MTMAX >= 2) if (mt == 2) { up_tile<F, 2>(a, t, slice); return; }
-  up_tile<F, 1>(a, t, slice);
+  if constexpr (MTMAX >= 4) if (mt == 4) { up_tile<F, 4, NCT>(a, t, slice); return; }
+  if constexpr (MTMAX >= 3) if (mt == 3) { up_tile<F, 3, NCT>(a, t, slice); return; }
+  if constexpr (MTMAX >= 2) if (mt == 2) { up_tile<F, 2, NCT>(a, t, slice); return; }
+  up_tile<F, 1, NCT>(a, t, slice);
 }
 
 struct DownArgs {
@@ -242,7 +302,7 @@ struct DownArgs {
   int N, H, E, I, Is, K, n_slices;
 };
 
-template <WFmt F, int MT>
+template <WFmt F, int MT, int NCT>
 __device__ __forceinline__ void down_tile(const DownArgs& a, const Tile& t, int slice) {
   using Fr = Frag<F>;
   using AT = typename Fr::AT;
@@ -251,79 +311,75 @@ __device__ __forceinline__ void down_tile(const DownArgs& a, const Tile& t, int 
   const int col = lane & 15, kg = lane >> 4;
   const bool shared = t.expert == a.E;
   const int inter = shared ? a.Is : a.I;
-  const int c0 = slice * kDownCols + wave * 16;
+  // this wave's output columns: c0 + 16c .. +16 for its NCT column tiles
+  const int c0 = (slice * 4 + wave) * 16 * NCT;
   const WT* W = shared ? static_cast<const WT*>(a.sw2)
                        : static_cast<const WT*>(a.w2) + (size_t)t.expert * a.H * a.I / Fr::kPack;
-  const WT* wrow = W + ((size_t)(c0 + col) * inter + kg * Fr::kGroupK) / Fr::kPack;
-  const void* wscale = nullptr;
-  if constexpr (F == WFmt::FP8) {
-    const float* S = static_cast<const float*>(shared ? a.sw2_scale : a.w2_scale);
-    if (!shared) S += (size_t)t.expert * (a.H / 128) * (a.I / 128);
-    wscale = S + (size_t)((c0 + col) / 128) * (inter / 128);
-  } else if constexpr (F == WFmt::FP4) {
-    const uint8_t* S = static_cast<const uint8_t*>(shared ? a.sw2_scale : a.w2_scale);
-    if (!shared) S += (size_t)t.expert * a.H * (a.I / 32);
-    wscale = S + (size_t)(c0 + col) * (inter / 32);
+  const WT* wrow[NCT];
+  const void* wscale[NCT];
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) {
+    const int orow = c0 + 16 * c + col;  // W2 row = output column
+    wrow[c] = W + ((size_t)orow * inter + kg * Fr::kGroupK) / Fr::kPack;
+    wscale[c] = nullptr;
+    if constexpr (F == WFmt::FP8) {
+      const float* S = static_cast<const float*>(shared ? a.sw2_scale : a.w2_scale);
+      if (!shared) S += (size_t)t.expert * (a.H / 128) * (a.I / 128);
+      wscale[c] = S + (size_t)(orow / 128) * (inter / 128);
+    } else if constexpr (F == WFmt::FP4) {
+      const uint8_t* S = static_cast<const uint8_t*>(shared ? a.sw2_scale : a.w2_scale);
+      if (!shared) S += (size_t)t.expert * a.H * (a.I / 32);
+      wscale[c] = S + (size_t)orow * (inter / 32);
+    }
   }
   const AT* hbase = static_cast<const AT*>(a.h) +
                     (shared ? (size_t)a.N * a.K * a.I + (size_t)t.start * a.Is : (size_t)t.start * a.I);
-  const AT* arow[MT];
+  const AT* arow[MT];  // rows past the count read row 0, as in up_tile
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int m = mt * 16 + col;
-    arow[mt] = m < t.rows ? hbase + (size_t)m * inter + kg * Fr::kGroupK : nullptr;
+    const int m = mt * 16 + col < t.rows ? mt * 16 + col : 0;
+    arow[mt] = hbase + (size_t)m * inter + kg * Fr::kGroupK;
   }
-  f32x4 acc[MT];
-  wave_gemm<F, MT>(wrow, arow, inter, wscale, acc);
+  f32x4 acc[NCT][MT];
+  wave_gemm<F, MT, NCT>(wrow, arow, inter, wscale, acc);
 
   float* y = a.y + ((shared ? (size_t)a.N * a.K : 0) + (size_t)t.start) * a.H;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int c = 0; c < NCT; ++c)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = mt * 16 + kg * 4 + v;
-      if (m < t.rows) y[(size_t)m * a.H + c0 + col] = acc[mt][v];
-    }
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = mt * 16 + kg * 4 + v;
+        if (m < t.rows) y[(size_t)m * a.H + c0 + 16 * c + col] = acc[c][mt][v];
+      }
 }
 
-template <WFmt F, int MTMAX>
+template <WFmt F, int MTMAX, int NCT>
 __global__ __launch_bounds__(256) void expert_down_kernel(DownArgs a) {
   const int slot = blockIdx.x / a.n_slices, slice = blockIdx.x % a.n_slices;
   if (slot >= *a.tile_count) return;
   const Tile t = a.tiles[slot];
   const int mt = (t.rows + 15) >> 4;  // 1..MTMAX
-  if constexpr (MTMAX >= 4) if (mt == 4) { down_tile<F, 4>(a, t, slice); return; }
-  if constexpr (MTMAX >= 3) if (mt == 3) { down_tile<F, 3>(a, t, slice); return; }
-  if constexpr (MTMAX >= 2) if (mt == 2) { down_tile<F, 2>(a, t, slice); return; }
-  down_tile<F, 1>(a, t, slice);
+  if constexpr (MTMAX >= 4) if (mt == 4) { down_tile<F, 4, NCT>(a, t, slice); return; }
+  if constexpr (MTMAX >= 3) if (mt == 3) { down_tile<F, 3, NCT>(a, t, slice); return; }
+  if constexpr (MTMAX >= 2) if (mt == 2) { down_tile<F, 2, NCT>(a, t, slice); return; }
+  down_tile<F, 1, NCT>(a, t, slice);
 }
 
-struct UpKernel {
-  template <WFmt F, int M>
-  static void launch(unsigned grid, hipStream_t s, const UpArgs& a) {
-    expert_up_kernel<F, M><<<grid, 256, 0, s>>>(a);
-  }
-};
-struct DownKernel {
-  template <WFmt F, int M>
-  static void launch(unsigned grid, hipStream_t s, const DownArgs& a) {
-    expert_down_kernel<F, M><<<grid, 256, 0, s>>>(a);
-  }
-};
-
-template <WFmt F, typename Kern, typename Args>
-static void dispatch_mt(int, unsigned grid, hipStream_t s, const Args& a) {
-  // these kernels serve single-row-tile calls; many-row tiles run in expert_tiled.hip
-  Kern::template launch<F, 1>(grid, s, a);
+// these kernels serve single-row-tile calls (MTMAX = 1); many-row tiles run in
+// expert_tiled.hip
+template <WFmt F>
+static void launch_up(unsigned grid, hipStream_t s, const UpArgs& a) {
+  expert_up_kernel<F, 1, up_nct<F>()><<<grid, 256, 0, s>>>(a);
 }
-
-template <typename Kern, typename Args>
-static void dispatch(WFmt f, int mt_max, unsigned grid, hipStream_t s, const Args& a) {
-  switch (f) {
-    case WFmt::BF16: dispatch_mt<WFmt::BF16, Kern>(mt_max, grid, s, a); break;
-    case WFmt::F32: dispatch_mt<WFmt::F32, Kern>(mt_max, grid, s, a); break;
-    case WFmt::FP8: dispatch_mt<WFmt::FP8, Kern>(mt_max, grid, s, a); break;
-    case WFmt::FP4: dispatch_mt<WFmt::FP4, Kern>(mt_max, grid, s, a); break;
+template <WFmt F>
+static void launch_down(int nct, unsigned grid, hipStream_t s, const DownArgs& a) {
+  if constexpr (F == WFmt::FP4) {
+    if (nct == 4) expert_down_kernel<F, 1, 4><<<grid, 256, 0, s>>>(a);
+    else expert_down_kernel<F, 1, 2><<<grid, 256, 0, s>>>(a);
+  } else {
+    expert_down_kernel<F, 1, 1><<<grid, 256, 0, s>>>(a);
   }
 }
 
@@ -351,9 +407,16 @@ hipError_t launch_expert_up(const Plan& p, const cmoe_weights& w, const void* x,
   a.I = p.I;
   a.Is = p.Is;
   a.K = p.K;
-  a.n_slices = (p.I > p.Is ? p.I : p.Is) / kUpCols;
+  const WFmt f = fmt_of(p);
+  const int nct = f == WFmt::FP4 ? up_nct<WFmt::FP4>() : 1;
+  a.n_slices = (p.I > p.Is ? p.I : p.Is) / (kUpCols * nct);
   const unsigned grid = (unsigned)p.max_tiles * (unsigned)a.n_slices;
-  dispatch<UpKernel>(fmt_of(p), p.mt_max, grid, s, a);
+  switch (f) {
+    case WFmt::BF16: launch_up<WFmt::BF16>(grid, s, a); break;
+    case WFmt::F32: launch_up<WFmt::F32>(grid, s, a); break;
+    case WFmt::FP8: launch_up<WFmt::FP8>(grid, s, a); break;
+    case WFmt::FP4: launch_up<WFmt::FP4>(grid, s, a); break;
+  }
   return hipGetLastError();
 }
 
@@ -373,9 +436,16 @@ hipError_t launch_expert_down(const Plan& p, const cmoe_weights& w, hipStream_t 
   a.I = p.I;
   a.Is = p.Is;
   a.K = p.K;
-  a.n_slices = p.H / kDownCols;
+  const WFmt f = fmt_of(p);
+  const int nct = down_nct(f, p.H);  // H is a multiple of 128, so of kDownCols * nct
+  a.n_slices = p.H / (kDownCols * nct);
   const unsigned grid = (unsigned)p.max_tiles * (unsigned)a.n_slices;
-  dispatch<DownKernel>(fmt_of(p), p.mt_max, grid, s, a);
+  switch (f) {
+    case WFmt::BF16: launch_down<WFmt::BF16>(nct, grid, s, a); break;
+    case WFmt::F32: launch_down<WFmt::F32>(nct, grid, s, a); break;
+    case WFmt::FP8: launch_down<WFmt::FP8>(nct, grid, s, a); break;
+    case WFmt::FP4: launch_down<WFmt::FP4>(nct, grid, s, a); break;
+  }
   return hipGetLastError();
 }
 

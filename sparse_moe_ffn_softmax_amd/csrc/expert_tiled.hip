@@ -52,14 +52,6 @@ struct TiledArgs {
 
 constexpr int kTiledMaxStages = 128;  // fp8 block scales held per weight row (hidden <= 16384)
 
-template <int B, int E, class Fn>
-__device__ __forceinline__ void static_for(Fn&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
-
 // One workgroup's GEMM: acc[mt] (16 x 16 each) for this wave's 16 columns,
 // over k in [0, Kdim).  asrc[i]: source row pointer (stage 0) of the i-th
 // activation vector this thread stages (rows past the tile repeat the tile's
