@@ -138,6 +138,9 @@ __device__ __forceinline__ void mma_stage(const Stage<F, MT, NCT>& st, const voi
   }
 }
 
+// stages in flight per wave on the fixed four-stage path
+constexpr int kDeepStages = 4;
+
 // register words one stage holds per lane
 template <WFmt F, int MT, int NCT>
 constexpr int stage_words() { return (int)(sizeof(Stage<F, MT, NCT>) / 4); }
@@ -155,12 +158,16 @@ __device__ __forceinline__ void wave_gemm(const typename Frag<F>::WT* const (&wr
   // Straight-line code lets the compiler wait for exactly the stage it needs.
   // (For bf16 the extra registers cost more occupancy than the deeper queue
   // gains: the two-stage loop below measured about 5% faster there.)
-  if constexpr (F == WFmt::FP4 && 4 * stage_words<F, MT, NCT>() <= 160) {
+  if constexpr (F == WFmt::FP4 && kDeepStages * stage_words<F, MT, NCT>() <= 160) {
     if (K == 512) {
       Stage<F, MT, NCT> st[4];
-      static_for<0, 4>([&](auto S) { load_stage<F, MT, NCT>(st[S], wrow, wscale, arow, S * 128); });
-      __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the first MFMA
-      static_for<0, 4>([&](auto S) { mma_stage<F, MT, NCT>(st[S], wscale, S * 128, acc); });
+      static_for<0, kDeepStages>([&](auto S) { load_stage<F, MT, NCT>(st[S], wrow, wscale, arow, S * 128); });
+      static_for<0, 4>([&](auto S) {
+        constexpr int next = S + kDeepStages;
+        if constexpr (next < 4) load_stage<F, MT, NCT>(st[next], wrow, wscale, arow, next * 128);
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of this stage's MFMAs
+        mma_stage<F, MT, NCT>(st[S], wscale, S * 128, acc);
+      });
       return;
     }
   }

@@ -112,6 +112,12 @@ def test_threshold_on_a_prefix_sum_takes_the_serial_cut(tau, m):
     FEW.with_(name="few_fp4_rows1", weight_dtype=W.FP4, block_rows=1, num_blocks=3, seed=105),
     MID.with_(name="mid_fp4_live50_budget6", weight_dtype=W.FP4, live_fraction=0.5, expert_budget=6,
               seed=106),
+    # H = 384: the gate/up waves do not split H, the down kernel takes two
+    # column tiles per wave; I = 512 takes the four-stage down schedule
+    FEW.with_(name="few_fp4_H384_I512", weight_dtype=W.FP4, hidden=384, inter=512, seed=107),
+    # H = 2048, I = 512: the four-stage gate/up and down schedules at small E
+    FEW.with_(name="few_fp4_H2048", weight_dtype=W.FP4, hidden=2048, inter=512, num_experts=64,
+              seed=108),
 ], ids=lambda w: w.name)
 def test_fp4_weights(wl):
     check(W.generate(wl))

@@ -55,7 +55,7 @@ class Workload:
     inter: int            # I  (routed expert intermediate size)
     shared_inter: int     # Is (shared expert intermediate size, 0 = none)
     act_dtype: str        # F32 or BF16
-    weight_dtype: str     # F32, BF16 or FP8
+    weight_dtype: str     # F32, BF16, FP8 or FP4
     mass_threshold: float
     seed: int
     sigma: float = 0.02
@@ -186,12 +186,13 @@ def quantize_mxfp4(w: np.ndarray):
     e = np.clip(e, -126, 127)
     v = blk / np.ldexp(1.0, e)[..., None]
     mag = np.abs(v)
-    d = np.abs(mag[..., None] - E2M1_GRID)                     # [..., 32, 8]
-    best = d.min(axis=-1, keepdims=True)
-    idx = np.arange(8)
-    # nearest grid value; on a tie the even code (its low bit clear)
-    score = np.where(d == best, 2 - (idx & 1), 0)
-    code = score.argmax(axis=-1).astype(np.uint8)
+    # nearest grid value, on a tie the even code (its low bit clear): the code
+    # counts the midpoints below |v|; at the midpoint between codes j and j+1
+    # the code stays j when j is even and becomes j+1 when j is odd
+    code = np.zeros(mag.shape, dtype=np.uint8)
+    for j in range(7):
+        mid = (E2M1_GRID[j] + E2M1_GRID[j + 1]) / 2
+        code += (mag > mid) if j % 2 == 0 else (mag >= mid)
     code = code | np.where(v < 0, 8, 0).astype(np.uint8)
     code = code.reshape(*lead, rows, cols)
     packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
