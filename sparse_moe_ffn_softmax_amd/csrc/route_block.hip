@@ -228,6 +228,10 @@ __device__ __forceinline__ void wave_sort64(MassKey& k, int lane) {
   }
 }
 
+// kMasked: the call passes a live-row mask.  Without one every row of the
+// block is live and the mask is a register value, so the unmasked instance
+// carries no mask load, broadcast or LDS read.
+template <bool kMasked>
 __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float tau) {
   const int R = plan.R, E = plan.E, K = plan.K;
   int32_t* __restrict__ topk = plan.topk;
@@ -268,14 +272,21 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
 
   if (tid == 0) m_sh = E;
   if (tid < kMaxExperts) mask1_s[tid] = 0u;
-  // live rows: all rows of the block unless the call passes a mask; a
-  // resolved row adds nothing to the mass and takes no route
-  const uint8_t* live = plan.live ? plan.live + (size_t)b * R : nullptr;
-  auto row_live = [&](int r) { return r < R && (live == nullptr || live[r] != 0); };
-  if (wave == 0) {
-    const uint64_t lb64 = __ballot(row_live(lane));
-    if (lane == 0) live_s = static_cast<uint32_t>(lb64);
+  // live rows (bit r: row r): all rows of the block unless the call passes a
+  // mask; a resolved row adds nothing to the mass and takes no route.  A mask
+  // is read by wave 0 and broadcast through LDS (read after the first
+  // barrier below).
+  if constexpr (kMasked) {
+    if (wave == 0) {
+      const uint8_t* live = plan.live + (size_t)b * R;
+      const uint64_t lb64 = __ballot(lane < R && live[lane] != 0);
+      if (lane == 0) live_s = static_cast<uint32_t>(lb64);
+    }
   }
+  auto row_is_live = [&](int r) -> bool {
+    if constexpr (kMasked) return (live_s >> r) & 1u;
+    else return r < R;
+  };
 
   // The softmax, block mass and coreset are needed below a threshold of 1, for
   // an expert budget (a cut in mass order) and for the block-mass and coreset
@@ -307,8 +318,9 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
       mx[h] = wave_max_f32(mm);
       if (lane == 0) m_s[r] = mx[h];
     }
-    const bool u0 = need_mass && row_live(wave), u1 = need_mass && row_live(wave + 16);
-    if (u0 && u1) {
+    // both rows when the second exists (the first then exists too: its u is
+    // computed even if it is resolved, and never read), else the first alone
+    if (need_mass && wave + 16 < R) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -316,17 +328,11 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
           const int r = wave + 16 * h, e = lane + 64 * s;
           p_s[pidx(r, e)] = exp_reduced(static_cast<double>(lv[h][s]) - static_cast<double>(mx[h]));
         }
-    } else if (u0) {
+    } else if (need_mass && wave < R) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int e = lane + 64 * s;
         p_s[pidx(wave, e)] = exp_reduced(static_cast<double>(lv[0][s]) - static_cast<double>(mx[0]));
-      }
-    } else if (u1) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int e = lane + 64 * s;
-        p_s[pidx(wave + 16, e)] = exp_reduced(static_cast<double>(lv[1][s]) - static_cast<double>(mx[1]));
       }
     }
   }
@@ -338,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
     // (live rows; the others have no u)
     if (tid < kMaxRows * 8) {
       const int r = tid >> 3, j = tid & 7;
-      if ((live_s >> r) & 1u) {
+      if (row_is_live(r)) {
         const int lo = (j * E) / 8, hi = ((j + 1) * E) / 8;
         double acc = 0.0;
 #pragma unroll 8
@@ -373,7 +379,7 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
         for (int i = 0; i < 8; ++i) q[i] = p_s[pidx(r0 + i, tid)] / z_s[r0 + i];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          if ((live_s >> (r0 + i)) & 1u) acc = acc + q[i];
+          if (row_is_live(r0 + i)) acc = acc + q[i];
       }
       mass_s[tid] = acc;
     }
@@ -493,7 +499,8 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
     __syncthreads();
   }  // need_mass
   // no live row: an empty coreset; else the threshold cut, then the budget
-  const int m = live_s == 0u ? 0 : plan.budget > 0 ? min(m_sh, plan.budget) : m_sh;
+  int m = plan.budget > 0 ? min(m_sh, plan.budget) : m_sh;
+  if constexpr (kMasked) m = live_s == 0u ? 0 : m;
 
   if (coreset_ids && tid < E) coreset_ids[(size_t)b * E + tid] = tid < m ? order_s[tid] : -1;
   if (coreset_size && tid == 0) coreset_size[b] = m;
@@ -508,7 +515,7 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
   if (2 * wave < R) {
     const int half = lane >> 5, hl = lane & 31;
     const int r = 2 * wave + half;
-    const bool row_ok = (live_s >> r) & 1u;
+    const bool row_ok = row_is_live(r);
     uint64_t key[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -581,7 +588,8 @@ static_assert(sizeof(double) * kMaxRows * kPStride >= sizeof(uint64_t) * 8 * kTh
               "the sorted top-k candidate lists reuse the probability buffer");
 
 hipError_t launch_route_blocks(const Plan& p, float tau, hipStream_t s) {
-  route_block_kernel<<<p.B, kThreads, 0, s>>>(p, tau);
+  if (p.live) route_block_kernel<true><<<p.B, kThreads, 0, s>>>(p, tau);
+  else route_block_kernel<false><<<p.B, kThreads, 0, s>>>(p, tau);
   return hipGetLastError();
 }
 
