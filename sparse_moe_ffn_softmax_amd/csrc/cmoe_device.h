@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace cmoe {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -27,6 +29,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
+
+// f(integral_constant<int, i>) for i = B .. E-1, unrolled at compile time
+template <int B, int E, class Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // wave-wide shuffle helpers (64 lanes)
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }

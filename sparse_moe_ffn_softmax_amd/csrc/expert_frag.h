@@ -15,18 +15,7 @@
 #pragma once
 #include "cmoe_device.h"
 
-#include <type_traits>
-
 namespace cmoe {
-
-// f(integral_constant<int, i>) for i = B .. E-1, unrolled at compile time
-template <int B, int E, class Fn>
-__device__ __forceinline__ void static_for(Fn&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
 
 enum class WFmt { BF16, F32, FP8, FP4 };
 

@@ -11,7 +11,9 @@
 //
 // Parallel layout: a workgroup of 256 threads owns a tile of RT rows x ET
 // experts; thread group c (32 threads) runs chunk c for every output of the
-// tile, each thread keeping TR x TE independent accumulators.  Operands are
+// tile, each thread keeping TR x TE independent accumulators (rows strided by
+// 8: the 8 row groups of a 16-lane LDS read then hit 8 different bank
+// groups, where contiguous row quartets put two row groups on each).  Operands are
 // staged through LDS in slices of KB positions per chunk.  With NBUF = 2 the
 // slices are double-buffered (the global loads of slice s+1 are in flight
 // while slice s is consumed); with NBUF = 1 one slice covers the whole chunk,
@@ -73,47 +75,54 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
   const int tid = threadIdx.x;
   const int c = tid >> 5;  // chunk run by this thread
   const int q = tid & 31;
-  const int rq = q & 7;    // row group
-  const int eq = q >> 3;   // expert group
+  const int rq = q & 7;    // row group: rows rq, rq + 8, ..., rq + 8(TR-1)
+  const int eq = q >> 3;   // expert group: experts eq*TE .. eq*TE + TE-1
   const int row0 = blockIdx.x * RT;
   const int e0 = blockIdx.y * ET;
   const int L = H / 8;     // chunk length, a multiple of KB
   const int S = L / KB;    // slices (1 when NBUF == 1)
 
-  u32x4 xr[XPT], wr[WPT];
-  auto fetch = [&](int s) {
+  // Staging loads are unconditional (rows past N and experts past E read the
+  // last valid row or expert, and are zeroed when parked in LDS): the
+  // compiler counts outstanding loads to place its waits, and a conditional
+  // load makes it wait for every load in flight.
+  // kDepth register sets of staged loads: on the fixed 16-slice schedule the
+  // loads of slices s+1 .. s+kDepth are in flight while slice s is consumed
+  constexpr int kDepth = NBUF > 1 ? 3 : 1;
+  u32x4 xr_[kDepth][XPT], wr_[kDepth][WPT];
+  auto fetch = [&](int s, int set = 0) {
+    auto& xr = xr_[set];
+    auto& wr = wr_[set];
     const int kb = s * KB;
 #pragma unroll
     for (int t = 0; t < XPT; ++t) {
       const int v = tid + t * 256;
-      u32x4 val = u32x4{0u, 0u, 0u, 0u};
-      if (v < XV) {
+      if (XV % 256 == 0 || v < XV) {
         const int kk = (v % (KB / XN)) * XN, rest = v / (KB / XN), r = rest % RT, cc = rest / RT;
-        const int row = row0 + r;
-        if (row < N) val = *reinterpret_cast<const u32x4*>(x + (size_t)row * H + cc * L + kb + kk);
+        const int row = min(row0 + r, N - 1);
+        xr[t] = *reinterpret_cast<const u32x4*>(x + (size_t)row * H + cc * L + kb + kk);
       }
-      xr[t] = val;
     }
 #pragma unroll
     for (int t = 0; t < WPT; ++t) {
       const int v = tid + t * 256;
-      u32x4 val = u32x4{0u, 0u, 0u, 0u};
-      if (v < WV) {
+      if (WV % 256 == 0 || v < WV) {
         const int kk = (v % (KB / 4)) * 4, rest = v / (KB / 4), e = rest % ET, cc = rest / ET;
-        const int ex = e0 + e;
-        if (ex < E) val = *reinterpret_cast<const u32x4*>(w + (size_t)ex * H + cc * L + kb + kk);
+        const int ex = min(e0 + e, E - 1);
+        wr[t] = *reinterpret_cast<const u32x4*>(w + (size_t)ex * H + cc * L + kb + kk);
       }
-      wr[t] = val;
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](int buf, int set = 0) {
+    auto& xr = xr_[set];
+    auto& wr = wr_[set];
 #pragma unroll
     for (int t = 0; t < XPT; ++t) {
       const int v = tid + t * 256;
-      if (v < XV) {
+      if (XV % 256 == 0 || v < XV) {
         const int kk = (v % (KB / XN)) * XN, rest = v / (KB / XN), r = rest % RT, cc = rest / RT;
         float f[XN];
-        XVec<XT>::widen(xr[t], f);
+        XVec<XT>::widen(row0 + r < N ? xr[t] : u32x4{0u, 0u, 0u, 0u}, f);
 #pragma unroll
         for (int i = 0; i < XN; ++i) xs[buf][cc][r][kk + i] = f[i];
       }
@@ -121,10 +130,11 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
 #pragma unroll
     for (int t = 0; t < WPT; ++t) {
       const int v = tid + t * 256;
-      if (v < WV) {
+      if (WV % 256 == 0 || v < WV) {
         const int kk = (v % (KB / 4)) * 4, rest = v / (KB / 4), e = rest % ET, cc = rest / ET;
+        const bool ok = e0 + e < E;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ws[buf][cc][e][kk + i] = __uint_as_float(wr[t][i]);
+        for (int i = 0; i < 4; ++i) ws[buf][cc][e][kk + i] = ok ? __uint_as_float(wr[t][i]) : 0.0f;
       }
     }
   };
@@ -135,17 +145,12 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
 #pragma unroll
     for (int j = 0; j < TE; ++j) acc[i][j] = 0.0f;
 
-  fetch(0);
-  stash(0);
-  __syncthreads();
-  for (int s = 0; s < S; ++s) {
-    const int buf = NBUF == 1 ? 0 : (s & 1);
-    if (NBUF > 1 && s + 1 < S) fetch(s + 1);
+  auto compute = [&](int buf) {
 #pragma unroll 4
     for (int k = 0; k < KB; k += 4) {
       f32x4 xv[TR], wv[TE];
 #pragma unroll
-      for (int i = 0; i < TR; ++i) xv[i] = *reinterpret_cast<const f32x4*>(&xs[buf][c][rq * TR + i][k]);
+      for (int i = 0; i < TR; ++i) xv[i] = *reinterpret_cast<const f32x4*>(&xs[buf][c][rq + 8 * i][k]);
 #pragma unroll
       for (int j = 0; j < TE; ++j) wv[j] = *reinterpret_cast<const f32x4*>(&ws[buf][c][eq * TE + j][k]);
 #pragma unroll
@@ -155,14 +160,50 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
 #pragma unroll
           for (int j = 0; j < TE; ++j) acc[i][j] = __builtin_fmaf(xv[i][kk], wv[j][kk], acc[i][j]);
     }
-    if (NBUF > 1 && s + 1 < S) stash(buf ^ 1);
-    __syncthreads();
+  };
+
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  if constexpr (NBUF > 1) {
+    if (S == 16) {
+      // fully unrolled, so that every register set has a fixed name and the
+      // waits count exactly: slice s+kDepth is fetched into the set slice s
+      // was parked from
+      static_for<1, kDepth>([&](auto J) { fetch(J, J); });
+      static_for<0, 16>([&](auto J) {
+        constexpr int st = decltype(J)::value;
+        if constexpr (st + kDepth < 16) fetch(st + kDepth, (st + kDepth) % kDepth);
+        compute(st & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (st + 1 < 16) {
+          stash((st + 1) & 1, (st + 1) % kDepth);
+          __syncthreads();
+        }
+      });
+    } else {
+      // slice s+1's loads are in flight while slice s feeds the FMAs; it is
+      // parked in the other buffer only after them (hoisted above them, its
+      // wait for the loads would leave nothing to overlap), and the last
+      // slice is peeled so that the loop body has no conditional load
+      for (int s = 0; s + 1 < S; ++s) {
+        fetch(s + 1);
+        compute(s & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        stash((s + 1) & 1);
+        __syncthreads();
+      }
+      compute((S - 1) & 1);
+    }
+  } else {
+    compute(0);
   }
+  __syncthreads();
 
 #pragma unroll
   for (int i = 0; i < TR; ++i)
 #pragma unroll
-    for (int j = 0; j < TE; ++j) part[c][rq * TR + i][eq * TE + j] = acc[i][j];
+    for (int j = 0; j < TE; ++j) part[c][rq + 8 * i][eq * TE + j] = acc[i][j];
   __syncthreads();
 
   for (int o = tid; o < RT * ET; o += 256) {
