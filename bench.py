@@ -78,8 +78,16 @@ def layer_copies(dp, n_layers, E):
 
 
 def source_digest(name: str) -> str:
+    """SHA-256 (16 hex digits) of a kernel source with its // comments and
+    blank lines removed: the counters stay valid across comment edits, not
+    across code changes."""
     p = os.path.join(ROOT, "sparse_moe_ffn_softmax_amd", "csrc", name)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    code = []
+    for line in open(p).read().splitlines():
+        line = line.split("//", 1)[0].rstrip()
+        if line.strip():
+            code.append(line)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 def measured_traffic(kernel: str, workload: str, src: str):
@@ -92,7 +100,7 @@ def measured_traffic(kernel: str, workload: str, src: str):
         d = json.load(open(p))
     except ValueError:
         return None
-    if d.get("source_sha256_16") != source_digest(src):
+    if d.get("code_sha256_16") != source_digest(src):
         return None
     return d.get("hbm_bytes_per_launch")
 

@@ -10,12 +10,12 @@
 // rows, so this is a weight-streaming (HBM-bound) kernel and the matrix cores
 // only need to keep up.
 //
-// Work decomposition.  The permutation kernel leaves a list of tiles
-// (expert, first pair, up to 16 * MTMAX pairs; MTMAX in 1..4 is picked per call
-// from the mean rows per expert, so a one-block call runs a lean single-tile
-// kernel and many-block calls share each weight byte among up to 64 rows).
-// A workgroup of 4 waves takes one tile and one slice of output columns,
-// 64 KiB of bf16 weights either way:
+// Work decomposition.  The permutation leaves a list of tiles (expert, first
+// pair, row count).  These kernels run the calls whose tiles hold at most 16
+// rows (one MFMA row tile: one block, decode, verification); calls with more
+// rows per expert run the LDS-tiled kernels of expert_tiled.hip.  A
+// workgroup of 4 waves takes one tile and one slice of output columns, 64 KiB
+// of bf16 weights either way:
 //   expert_up   : 8 h columns = one 16-column MFMA tile of 8 gate and the
 //                 matching 8 up columns (SwiGLU pairs lanes l and l+8 of the
 //                 accumulator); the 4 waves split the hidden dimension and
@@ -51,14 +51,15 @@
 namespace cmoe {
 
 // ---------------------------------------------------------------------------
-// one wave: acc[mt] (16 rows x 16 cols) = sum_k A_mt[:, k] * W[col, k] over
-// k in [0, K).  wrow: pointer to this lane's weight row at its k offset;
-// arow[mt]: this lane's activation row at its k offset.
-// For fp8, wscale points at this lane's row of 128x128 block scales.
+// one wave: acc[c][mt] (16 rows x 16 cols) = sum_k A_mt[:, k] * W_c[col, k]
+// over k in [0, K), for NCT column tiles c.  wrow[c]: this lane's weight row
+// of column tile c at its k offset; arow[mt]: this lane's activation row at
+// its k offset; wscale[c]: that row's scales (fp8 128x128 blocks, fp4 E8M0).
 //
 // K is consumed in stages of 128; the loads of stage s+1 are issued before
 // the MFMAs of stage s, so each wave always has a stage of weights in flight
-// (two register buffers, alternating).
+// (two register buffers, alternating), or, on the fixed four-stage path, all
+// four stages at once.
 // ---------------------------------------------------------------------------
 template <WFmt F, int MT, int NCT>
 struct Stage {
