@@ -9,9 +9,9 @@
  *   routed to the top 8 of 256 experts, and a shared expert is always
  *   applied; answers are written in 32-token blocks that are re-run pass
  *   after pass until no mask token remains.
- *   Same card, "Usage": during those passes the block's experts are
- *   restricted to the set that carries 90% of the block's routing; the block
- *   size can be 8, 16 or 32.
+ *   Same card, "Usage": during those passes a block may use only the experts
+ *   that together hold 90% of the block's routing weight; the block size can
+ *   be 8, 16 or 32.
  *   InfiniLM PR #604 (Clover on Hygon), "Summary", "Motivation" and "Notes for
  *   Reviewers": block coreset routing in the preview pass, top-4 preview
  *   routing, and a full-route replay after the approximate preview

@@ -9,16 +9,16 @@
  * Stages, in the order the pages describe the layer:
  *   1. router logits                 (CMF model card, introduction: 256 experts, top-8)
  *   2. softmax over all experts      (same)
- *   3. block routing mass            (CMF model card, "Usage": the set that carries 90%
- *                                     of the block's routing; InfiniLM PR #604 "Summary":
- *                                     block coreset routing)
+ *   3. block routing mass            (CMF model card, "Usage": the experts holding 90%
+ *                                     of the block's routing weight; InfiniLM PR #604
+ *                                     "Summary": block coreset routing)
  *   4. coreset = smallest mass-ordered prefix reaching the threshold
  *   5. restricted top-k + renormalised gates (InfiniLM PR #604 "Motivation": top-4
  *                                     preview routing; "Notes for Reviewers": full-route
  *                                     replay = unrestricted routing)
  *   6. per-expert counts and the expert-major row order
  *   7. routed SwiGLU experts + the shared expert, gate-weighted sum (CMF model card,
- *                                     introduction: "plus a shared expert")
+ *                                     introduction: one shared expert besides the routed ones)
  */
 #include "clover_moe_oracle.h"
 

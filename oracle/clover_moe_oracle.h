@@ -13,10 +13,10 @@
  *  - Clover-35B-A3B-Preview CMF model card, introduction: 256 routed
  *    experts, top-8 per token, plus one shared expert; answers written in
  *    32-token blocks refined by repeated denoising passes.
- *  - same card, "Usage": the block's experts are restricted to the set that
- *    carries 90% of its routing; block sizes 8, 16 or 32.
- *  - same card, "Performance": a pass is one denoising forward over the
- *    32-row block.
+ *  - same card, "Usage": each block may use only the experts that together
+ *    hold 90% of the block's routing weight; the block size is 8, 16 or 32.
+ *  - same card, "Performance": each denoising pass runs the model forward
+ *    once over the whole 32-row block.
  *  - InfiniLM PR #604 (Clover on Hygon), "Summary" and "Motivation": block
  *    coreset routing in the preview pass, top-4 preview routing, full-route
  *    replay after the approximate preview.

@@ -1,6 +1,6 @@
 // combine.hip -- gate-weighted combine of the routed expert outputs plus the
 // shared expert (Clover-35B-A3B-Preview CMF model card, introduction: top-8
-// routed experts plus a shared expert):
+// routed experts and one shared expert besides them):
 //
 //   out[r] = y_shared[r] + sum_j gate[r,j] * y[pos(r,j)]     (slots ascending)
 //

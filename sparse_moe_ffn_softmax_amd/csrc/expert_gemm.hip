@@ -4,8 +4,8 @@
 //   expert_down : y = h W2_e^T                            for every work tile
 //
 // The routed experts and the shared expert are SwiGLU FFNs (Clover-35B-A3B-
-// Preview CMF model card, introduction: 256 routed experts, top-8, plus a
-// shared expert).  Expert weights are streamed from HBM exactly once per
+// Preview CMF model card, introduction: 256 routed experts, eight per token,
+// and one shared expert).  Expert weights are streamed from HBM exactly once per
 // work tile; with one 32-row block per call a touched expert sees about two
 // rows, so this is a weight-streaming (HBM-bound) kernel and the matrix cores
 // only need to keep up.

@@ -4,7 +4,7 @@
 //   expert_up_tiled   : h = silu(X_e W_gate^T) * (X_e W_up^T)
 //   expert_down_tiled : y = h W2_e^T
 //
-// SwiGLU experts plus a shared expert (Clover-35B-A3B-Preview CMF model card,
+// SwiGLU experts and one shared expert (Clover-35B-A3B-Preview CMF model card,
 // introduction); fp8 weights are E4M3 with one fp32 scale per 128x128 block
 // and bf16 activations (InfiniLM PR #584, "Benchmark"); 4-bit weights are
 // MXFP4 (E2M1 codes, E8M0 scale per 32 elements of a row), widened to bf16

@@ -3,10 +3,11 @@
 //
 // Every routed (row, slot) pair gets a position in an expert-major order:
 // experts ascending, and inside an expert rows ascending (the key
-// expert, row*k + slot; a row routes to an expert at most once).  The experts
-// a block uses are then streamed once each, with their rows gathered next to
+// expert, row*k + slot; a row routes to an expert at most once).  Each expert
+// touched by the call is then streamed once, with its rows gathered next to
 // each other (the CMF model card's "Hardware" section describes the same
-// idea on Metal: the experts a block uses are bound as they are routed).
+// idea on Metal, where a block's experts are attached only once its routing
+// has chosen them).
 //
 // The order is built without sorting: a bit mask per expert marks the rows
 // routed to it, so a pair's rank inside its expert is a popcount of the

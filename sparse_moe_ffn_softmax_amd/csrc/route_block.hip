@@ -3,8 +3,8 @@
 // block.
 //
 // What is computed (Clover-35B-A3B-Preview CMF model card: introduction for
-// "256 experts top-8 plus a shared expert", "Usage" for "the block's experts
-// restricted to the set that carries 90% of its routing"; InfiniLM PR #604
+// the 256 routed experts, eight per token, and the shared expert; "Usage" for
+// limiting a block to the experts that hold 90% of its routing weight; InfiniLM PR #604
 // "Summary" for block coreset routing in the preview pass, "Motivation" for
 // top-4 preview routing, "Notes for Reviewers" for the full-route replay):
 //
