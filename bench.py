@@ -120,8 +120,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU sharding is described in DESIGN.md but not built.", file=sys.stderr)
+        print(f"bench.py: this library runs on one GPU only (asked for --gpus {args.gpus}); "
+              "sharding across GPUs is not implemented.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
