@@ -68,9 +68,9 @@ struct TiledGemm {
   static constexpr int VPR = 16;                    // 16-byte vectors per row per stage
   static constexpr int RPP = kTiledThreads / VPR;   // rows staged per pass of the workgroup
   static constexpr int AV = T / RPP;                // vectors per thread per stage
-  // 288-byte rows: the MFMA fragment reads (16 rows, one 16-byte unit each)
-  // are free of bank conflicts (a 272-byte pitch measured 3.7 conflict cycles
-  // per read on gfx950)
+  // 288-byte rows: the MFMA fragment reads (16 rows at one offset, the four
+  // lane groups 64 contiguous bytes) are free of bank conflicts (a 272-byte
+  // pitch measured 3.7 conflict cycles per read on gfx950)
   static constexpr int PAD = 32 / (int)sizeof(AT);
   using Lds = AT[2][T][KS + PAD];
   // k order inside a stage.  MFMA only needs A and B to agree on it, so fp8
@@ -79,9 +79,22 @@ struct TiledGemm {
   // codes per step) instead of two 8-byte ones.
   static constexpr bool kPair = (F == WFmt::FP8);
   static_assert(!kPair || U % 2 == 0, "paired fp8 steps");
+  // element offset, within a stage, of the fragment lane group kg uses at step u
   static __device__ __forceinline__ int koff(int u, int kg) {
     return kPair ? 64 * (u / 2) + 16 * kg + 8 * (u % 2) : u * Fr::kStepK + kg * Fr::kGroupK;
   }
+  // LDS placement of a staged row.  16-byte chunk c of the row (in k order;
+  // the fragment at (u, kg) is chunk koff(u, kg) * sizeof(AT) / 16)
+  // is stored at chunk apos(c), chosen so that the fragment a lane reads at
+  // step u is chunk 4u + kg for every format, the pattern above.  Read in
+  // place, the paired fp8 order (lane groups 32 bytes apart) and the fp4
+  // order (64 bytes apart) measured 4 conflict cycles per read on gfx950.
+  static __device__ __forceinline__ int apos(int c) {
+    if constexpr (kPair) return (c & 8) | ((c & 1) << 2) | ((c >> 1) & 3);  // c = 8(u/2) + 2kg + u%2
+    else if constexpr (F == WFmt::FP4) return ((c & 3) << 2) | (c >> 2);    // c = u + 4kg
+    else return c;                                                          // c = 4u + kg
+  }
+  static __device__ __forceinline__ int aread(int u, int kg) { return (4 * u + kg) * (16 / (int)sizeof(AT)); }
   // this lane's first weight byte of a stage, relative to its weight row
   static __device__ __forceinline__ int blane(int kg) { return kPair ? 16 * kg : kg * Fr::kGroupK / Fr::kPack; }
   // one stage of this lane's weights; fp4 adds the stage's four E8M0 bytes of its row
@@ -109,7 +122,7 @@ struct TiledGemm {
     auto store_a = [&](int buf) {
 #pragma unroll
       for (int i = 0; i < AV; ++i)
-        *reinterpret_cast<u32x4*>(&As[buf][r0 + i * RPP][seg * (16 / (int)sizeof(AT))]) = areg[i];
+        *reinterpret_cast<u32x4*>(&As[buf][r0 + i * RPP][apos(seg) * (16 / (int)sizeof(AT))]) = areg[i];
     };
     auto load_b = [&](BSet& bs, int k0) {
       auto& b = bs.b;
@@ -144,7 +157,7 @@ struct TiledGemm {
         for (int u = 0; u < U; ++u) {
           typename Fr::A av[MT];
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) av[mt] = Fr::load_a(&As[buf][mt * 16 + col][koff(u, kg)]);
+          for (int mt = 0; mt < MT; ++mt) av[mt] = Fr::load_a(&As[buf][mt * 16 + col][aread(u, kg)]);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) acc[mt] = Fr::mma(av[mt], b[u], sc, acc[mt]);
           __builtin_amdgcn_sched_barrier(0);
@@ -157,7 +170,7 @@ struct TiledGemm {
         for (int u = 0; u < U; ++u) {
           typename Fr::A av[MT];
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) av[mt] = Fr::load_a(&As[buf][mt * 16 + col][koff(u, kg)]);
+          for (int mt = 0; mt < MT; ++mt) av[mt] = Fr::load_a(&As[buf][mt * 16 + col][aread(u, kg)]);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) tmp[mt] = Fr::mma(av[mt], b[u], tmp[mt]);
           __builtin_amdgcn_sched_barrier(0);
@@ -172,7 +185,7 @@ struct TiledGemm {
         for (int u = 0; u < U; ++u) {
           typename Fr::A av[MT];
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) av[mt] = Fr::load_a(&As[buf][mt * 16 + col][koff(u, kg)]);
+          for (int mt = 0; mt < MT; ++mt) av[mt] = Fr::load_a(&As[buf][mt * 16 + col][aread(u, kg)]);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) acc[mt] = Fr::mma(av[mt], b[u], acc[mt]);
           // keep the scheduler from hoisting every k step's operands at once
