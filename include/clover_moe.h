@@ -38,8 +38,9 @@
  * for the logits, fp64 softmax with a Cody-Waite exp) so that expert sets,
  * indices, gates and counts are reproducible bit for bit by any conforming
  * implementation.  Step 6 accumulates in fp32 on MFMA; it matches an exact
- * evaluation within a tolerance (bf16: max |err| <= 2e-2 max|ref| and
- * sum|err| <= 5e-3 sum|ref|; fp8 weights: max |err| <= 6e-2 max|ref|).
+ * evaluation within a tolerance (bf16 and 4-bit weights: max |err| <=
+ * 2e-2 max|ref| and sum|err| <= 5e-3 sum|ref|; fp8 weights: max |err| <=
+ * 6e-2 max|ref|).
  *
  * Conventions
  *  - Every pointer argument of clover_moe_block_forward, and every pointer in
@@ -61,6 +62,9 @@
  *  - Non-finite inputs are not checked; their results are undefined.
  *  - Thread safety: calls are independent; the library has no global
  *    mutable state apart from the thread-local error text.
+ *  - A call queues kernels on `stream` and nothing else (no memset, no
+ *    allocation, no host synchronisation), so it can be captured in a HIP
+ *    graph; replays reproduce the eager results bit for bit.
  */
 #ifndef CLOVER_MOE_H
 #define CLOVER_MOE_H
