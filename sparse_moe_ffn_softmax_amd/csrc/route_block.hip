@@ -240,9 +240,8 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
   int32_t* __restrict__ coreset_size = plan.coreset_size;
   double* __restrict__ block_mass = plan.block_mass;
   __shared__ float l_s[kMaxRows][kMaxExperts];
-  // u; then each lane's sorted top-k candidates; then (many blocks) the
-  // permutation's row masks.  One pad slot per 32 experts keeps the
-  // per-chunk serial sums of different (row, chunk) threads on different banks.
+  // u.  One pad slot per 32 experts keeps the per-chunk serial sums of
+  // different (row, chunk) threads on different banks.
   __shared__ double p_s[kMaxRows * kPStride];
   __shared__ double zpart[kMaxRows][8];  // Z partials; later the chosen u
   __shared__ double z_s[kMaxRows];
@@ -507,8 +506,8 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
   if (block_mass && tid < E) block_mass[(size_t)b * E + tid] = mass_s[tid];
 
   // restricted top-k: half a wave per row (rows 2w and 2w+1 on wave w); each
-  // lane sorts its 8 candidates (experts (lane&31) + 32*s) by key into LDS,
-  // and every slot takes the best head of the half-wave: the largest high
+  // lane sorts its 8 candidates (experts (lane&31) + 32*s) by key in
+  // registers, and every slot takes the best head of the half-wave: the largest high
   // word (logit), then, only if several lanes hold it, the largest low word
   // (lowest id).  The lane whose head was taken records it and moves on.
   // Waves whose two rows are past R (blocks of fewer than 32 rows) skip it.
@@ -524,13 +523,13 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
       key[s] = ok ? (static_cast<uint64_t>(logit_key(l_s[r][e])) << 32) | static_cast<uint32_t>(~e) : 0ull;
     }
     sort8_desc(key);
-    uint64_t* lst = reinterpret_cast<uint64_t*>(p_s);  // [slot][thread]
-#pragma unroll
-    for (int s = 1; s < 8; ++s) lst[s * kThreads + tid] = key[s];
-    uint64_t head = key[0];
-    int ptr = 0;
+    // the lane's candidates stay in registers: a lane whose head is taken
+    // shifts its list up by one
     int k_eff = 0;  // slots filled in this lane's row
-    for (int j = 0; j < K; ++j) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j >= K) break;
+      const uint64_t head = key[0];
       const uint32_t hh = static_cast<uint32_t>(head >> 32), hlo = static_cast<uint32_t>(head);
       const uint32_t bh = half_max_u32(hh);
       const bool top = head != 0ull && hh == bh;  // (a real key has ~id != 0 below)
@@ -544,9 +543,9 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
       }
       if (popped) pick_s[r * 8 + j] = static_cast<int>(~hlo);
       k_eff += (half ? thi : tlo) != 0u ? 1 : 0;
-      ptr += popped ? 1 : 0;
-      const uint64_t nxt = lst[min(ptr, 7) * kThreads + tid];
-      head = popped ? (ptr < 8 ? nxt : 0ull) : head;
+#pragma unroll
+      for (int i = 0; i < 7; ++i) key[i] = popped ? key[i + 1] : key[i];
+      key[7] = popped ? 0ull : key[7];
       if (tb == 0ull) break;  // both rows exhausted
     }
     __builtin_amdgcn_wave_barrier();
@@ -583,9 +582,6 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
   // built by the kernels queued next (permute_blocks.hip)
   if (tid < E) plan.blockmask[(size_t)b * E + tid] = mask1_s[tid];
 }
-
-static_assert(sizeof(double) * kMaxRows * kPStride >= sizeof(uint64_t) * 8 * kThreads,
-              "the sorted top-k candidate lists reuse the probability buffer");
 
 hipError_t launch_route_blocks(const Plan& p, float tau, hipStream_t s) {
   if (p.live) route_block_kernel<true><<<p.B, kThreads, 0, s>>>(p, tau);
