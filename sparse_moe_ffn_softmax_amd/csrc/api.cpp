@@ -299,6 +299,8 @@ static cmoe_status forward_impl(const cmoe_problem* problem, const cmoe_weights*
   plan.budget = budget;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
+  // few routed pairs: the down GEMM writes `out` itself (stage 4 is empty)
+  const bool fused = cmoe::down_combine_fits(plan);
   for (int stage = 0; stage <= CLOVER_MOE_NUM_STAGES && e == hipSuccess; ++stage) {
     if (events) {
       e = hipEventRecord(static_cast<hipEvent_t>(events[stage]), st);
@@ -315,10 +317,13 @@ static cmoe_status forward_impl(const cmoe_problem* problem, const cmoe_weights*
                              : cmoe::launch_expert_tiled(plan, *w, x, true, st);
         break;
       case 3:
-        e = plan.mt_max == 1 ? cmoe::launch_expert_down(plan, *w, st)
-                             : cmoe::launch_expert_tiled(plan, *w, x, false, st);
+        e = fused ? cmoe::launch_expert_down_combine(plan, *w, out, st)
+            : plan.mt_max == 1 ? cmoe::launch_expert_down(plan, *w, st)
+                               : cmoe::launch_expert_tiled(plan, *w, x, false, st);
         break;
-      case 4: e = cmoe::launch_combine(plan, out, st); break;
+      case 4:
+        if (!fused) e = cmoe::launch_combine(plan, out, st);
+        break;
       default: break;
     }
   }

@@ -95,6 +95,9 @@ hipError_t launch_permute_blocks(const Plan& p, hipStream_t s);
 // mt_max == 1: register-operand kernels (expert_gemm.hip)
 hipError_t launch_expert_up(const Plan& p, const cmoe_weights& w, const void* x, hipStream_t s);
 hipError_t launch_expert_down(const Plan& p, const cmoe_weights& w, hipStream_t s);
+// calls with few routed pairs: the down GEMM and the combine in one kernel
+bool down_combine_fits(const Plan& p);
+hipError_t launch_expert_down_combine(const Plan& p, const cmoe_weights& w, void* out, hipStream_t s);
 // mt_max > 1: LDS-staged activation tiles (expert_tiled.hip); up = gate/up + SwiGLU, else down
 hipError_t launch_expert_tiled(const Plan& p, const cmoe_weights& w, const void* x, bool up,
                                hipStream_t s);

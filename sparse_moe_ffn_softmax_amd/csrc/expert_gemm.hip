@@ -146,7 +146,7 @@ constexpr int kDeepStages = 4;
 template <WFmt F, int MT, int NCT>
 constexpr int stage_words() { return (int)(sizeof(Stage<F, MT, NCT>) / 4); }
 
-template <WFmt F, int MT, int NCT>
+template <WFmt F, int MT, int NCT, bool DEEP = (F == WFmt::FP4)>
 __device__ __forceinline__ void wave_gemm(const typename Frag<F>::WT* const (&wrow)[NCT],
                                           const typename Frag<F>::AT* const (&arow)[MT], int K,
                                           const void* const (&wscale)[NCT], f32x4 (&acc)[NCT][MT]) {
@@ -154,12 +154,13 @@ __device__ __forceinline__ void wave_gemm(const typename Frag<F>::WT* const (&wr
   for (int c = 0; c < NCT; ++c)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[c][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // 4-bit weights, K = 512 (the hidden size split four ways, or the expert
-  // width): issue all four stages' loads at once, then consume them in order.
-  // Straight-line code lets the compiler wait for exactly the stage it needs.
-  // (For bf16 the extra registers cost more occupancy than the deeper queue
-  // gains: the two-stage loop below measured about 5% faster there.)
-  if constexpr (F == WFmt::FP4 && kDeepStages * stage_words<F, MT, NCT>() <= 160) {
+  // DEEP (4-bit weights, and the fused decode kernel), K = 512 (the hidden
+  // size split four ways, or the expert width): issue all four stages' loads
+  // at once, then consume them in order.  Straight-line code lets the
+  // compiler wait for exactly the stage it needs.  (For a large bf16 grid
+  // the extra registers cost more occupancy than the deeper queue gains: the
+  // two-stage loop below measured about 5% faster there.)
+  if constexpr (DEEP && kDeepStages * stage_words<F, MT, NCT>() <= 160) {
     if (K == 512) {
       Stage<F, MT, NCT> st[4];
       static_for<0, kDeepStages>([&](auto S) { load_stage<F, MT, NCT>(st[S], wrow, wscale, arow, S * 128); });
@@ -316,17 +317,17 @@ struct DownArgs {
   int N, H, E, I, Is, K, n_slices;
 };
 
-template <WFmt F, int MT, int NCT>
-__device__ __forceinline__ void down_tile(const DownArgs& a, const Tile& t, int slice) {
+// acc[c][mt]: the tile's y for its MT row tiles and the NCT 16-column tiles
+// of output columns starting at c0
+template <WFmt F, int MT, int NCT, bool DEEP = (F == WFmt::FP4)>
+__device__ __forceinline__ void down_acc(const DownArgs& a, const Tile& t, int c0, f32x4 (&acc)[NCT][MT]) {
   using Fr = Frag<F>;
   using AT = typename Fr::AT;
   using WT = typename Fr::WT;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int col = lane & 15, kg = lane >> 4;
   const bool shared = t.expert == a.E;
   const int inter = shared ? a.Is : a.I;
-  // this wave's output columns: c0 + 16c .. +16 for its NCT column tiles
-  const int c0 = (slice * 4 + wave) * 16 * NCT;
   const WT* W = shared ? static_cast<const WT*>(a.sw2)
                        : static_cast<const WT*>(a.w2) + (size_t)t.expert * a.H * a.I / Fr::kPack;
   const WT* wrow[NCT];
@@ -354,9 +355,19 @@ __device__ __forceinline__ void down_tile(const DownArgs& a, const Tile& t, int 
     const int m = mt * 16 + col < t.rows ? mt * 16 + col : 0;
     arow[mt] = hbase + (size_t)m * inter + kg * Fr::kGroupK;
   }
-  f32x4 acc[NCT][MT];
-  wave_gemm<F, MT, NCT>(wrow, arow, inter, wscale, acc);
+  wave_gemm<F, MT, NCT, DEEP>(wrow, arow, inter, wscale, acc);
+}
 
+template <WFmt F, int MT, int NCT>
+__device__ __forceinline__ void down_tile(const DownArgs& a, const Tile& t, int slice) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, kg = lane >> 4;
+  // this wave's output columns: c0 + 16c .. +16 for its NCT column tiles
+  const int c0 = (slice * 4 + wave) * 16 * NCT;
+  f32x4 acc[NCT][MT];
+  down_acc<F, MT, NCT>(a, t, c0, acc);
+
+  const bool shared = t.expert == a.E;
   float* y = a.y + ((shared ? (size_t)a.N * a.K : 0) + (size_t)t.start) * a.H;
 #pragma unroll
   for (int c = 0; c < NCT; ++c)
@@ -379,6 +390,54 @@ __global__ __launch_bounds__(256, kMinWavesPerSimd) void expert_down_kernel(Down
   if constexpr (MTMAX >= 3) if (mt == 3) { down_tile<F, 3, NCT>(a, t, slice); return; }
   if constexpr (MTMAX >= 2) if (mt == 2) { down_tile<F, 2, NCT>(a, t, slice); return; }
   down_tile<F, 1, NCT>(a, t, slice);
+}
+
+// Calls with at most kFusedMaxTiles work tiles (one-row decode: 8 experts
+// and the shared one): the down GEMM and the combine in one kernel.  A
+// workgroup owns 16 output columns and runs one wave per work tile, each
+// with all four k stages of its weights in flight; the tiles' y for those
+// columns go to LDS, and after a barrier the combine sums them per row: the
+// shared expert's row first, then fmaf of each filled slot in slot order.
+// The y of a (tile, column) comes from the same MFMA sequence as in
+// expert_down_kernel and the sum is the combine kernel's, so out is bitwise
+// what the two kernels give.
+constexpr int kFusedMaxTiles = 10;
+constexpr int kFusedMaxPairs = 64;  // N*K + N
+
+template <WFmt F>
+__global__ __launch_bounds__(64 * kFusedMaxTiles) void expert_down_combine_kernel(DownArgs a, const int32_t* pair_pos,
+                                                                   const float* gates, void* out,
+                                                                   int out_bf16, const uint8_t* live) {
+  __shared__ float y_s[kFusedMaxPairs][16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int col = lane & 15, kg = lane >> 4;
+  const int c0 = blockIdx.x * 16;
+  const int NK = a.N * a.K;
+  const int nt = *a.tile_count;
+  for (int slot = wave; slot < nt; slot += nw) {
+    const Tile t = a.tiles[slot];
+    f32x4 acc[1][1];
+    down_acc<F, 1, 1, true>(a, t, c0, acc);
+    const int base = (t.expert == a.E ? NK : 0) + t.start;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = kg * 4 + v;
+      if (m < t.rows) y_s[base + m][col] = acc[0][0][v];
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < a.N * 16; i += blockDim.x) {
+    const int r = i >> 4, cc = i & 15;
+    if (live && !live[r]) continue;  // a resolved row keeps the caller's cached output
+    float o = a.Is > 0 ? y_s[NK + r][cc] : 0.0f;
+    for (int j = 0; j < a.K; ++j) {
+      const int pos = pair_pos[r * a.K + j];
+      if (pos >= 0) o = __builtin_fmaf(gates[r * a.K + j], y_s[pos][cc], o);
+    }
+    const size_t at = (size_t)r * a.H + c0 + cc;
+    if (out_bf16) static_cast<uint16_t*>(out)[at] = f32_to_bf16(o);
+    else static_cast<float*>(out)[at] = o;
+  }
 }
 
 // these kernels serve single-row-tile calls (MTMAX = 1); many-row tiles run in
@@ -430,6 +489,42 @@ hipError_t launch_expert_up(const Plan& p, const cmoe_weights& w, const void* x,
     case WFmt::F32: launch_up<WFmt::F32>(grid, s, a); break;
     case WFmt::FP8: launch_up<WFmt::FP8>(grid, s, a); break;
     case WFmt::FP4: launch_up<WFmt::FP4>(grid, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+bool down_combine_fits(const Plan& p) {
+  // (fp32 weights keep the two kernels: their fragments need more registers
+  // than 16 waves per workgroup leave)
+  return p.mt_max == 1 && !p.y_act && p.wt != CMOE_F32 && p.max_tiles <= kFusedMaxTiles &&
+         p.N * p.K + p.N <= kFusedMaxPairs;
+}
+
+hipError_t launch_expert_down_combine(const Plan& p, const cmoe_weights& w, void* out, hipStream_t s) {
+  DownArgs a;
+  a.w2 = w.w2;
+  a.w2_scale = w.w2_scale;
+  a.sw2 = w.shared_w2;
+  a.sw2_scale = w.shared_w2_scale;
+  a.tiles = p.tiles;
+  a.tile_count = p.tile_count;
+  a.h = p.h;
+  a.y = nullptr;  // y stays in LDS
+  a.N = p.N;
+  a.H = p.H;
+  a.E = p.E;
+  a.I = p.I;
+  a.Is = p.Is;
+  a.K = p.K;
+  a.n_slices = 0;
+  const int waves = p.max_tiles;  // one per tile (at most kFusedMaxTiles)
+  const unsigned grid = (unsigned)(p.H / 16), block = 64u * (unsigned)waves;
+  const int bf16 = p.act == CMOE_BF16;
+  switch (fmt_of(p)) {
+    case WFmt::BF16: expert_down_combine_kernel<WFmt::BF16><<<grid, block, 0, s>>>(a, p.pair_pos, p.gates, out, bf16, p.live); break;
+    case WFmt::F32: return hipErrorInvalidValue;  // excluded by down_combine_fits
+    case WFmt::FP8: expert_down_combine_kernel<WFmt::FP8><<<grid, block, 0, s>>>(a, p.pair_pos, p.gates, out, bf16, p.live); break;
+    case WFmt::FP4: expert_down_combine_kernel<WFmt::FP4><<<grid, block, 0, s>>>(a, p.pair_pos, p.gates, out, bf16, p.live); break;
   }
   return hipGetLastError();
 }
