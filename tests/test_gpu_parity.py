@@ -289,3 +289,20 @@ def test_blocks_independent_on_gpu():
         # an intermediate bf16 h can round the other way): same bar as parity
         d = np.abs(out_all[sl] - o1)
         assert d.max() <= 2e-2 * np.abs(o1).max() and d.sum() <= 5e-3 * np.abs(o1).sum()
+
+
+@pytest.mark.parametrize("wt", [W.BF16, W.FP8, W.FP4])
+def test_fused_decode_down_combine_is_bitwise_the_two_kernels(wt):
+    """A one-row call (at most 10 work tiles) runs the down GEMM and the
+    combine as one kernel; a two-block call of one row each (19 tiles) runs
+    them as two.  Both use one-row-tile GEMMs with fp32 y, so every row's
+    output must agree bit for bit."""
+    wl = W.WORKLOADS["decode1_bf16"].with_(name=f"decode2_{wt}", num_blocks=2, weight_dtype=wt,
+                                           seed=151)
+    inp = W.generate(wl)
+    out_two, r_two = run_gpu(inp, 1.0, wl.top_k)
+    for b in range(2):
+        one = W.with_arrays(inp, wl=wl.with_(num_blocks=1), x=np.ascontiguousarray(inp.x[b:b + 1]))
+        o1, r1 = run_gpu(one, 1.0, wl.top_k)
+        np.testing.assert_array_equal(r_two["topk_idx"][b:b + 1], r1["topk_idx"])
+        np.testing.assert_array_equal(o1.view(np.uint64), out_two[b:b + 1].view(np.uint64))
