@@ -47,21 +47,40 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
   const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (c >= H) return;
   if (live && !live[r]) return;  // a resolved row keeps the caller's cached output
-  // every load is issued before the first add: positions and gates, then the
-  // shared row and the routed rows (K <= 8)
+  // Every load is unconditional, so that all of them are in flight at once
+  // (a conditional load makes the compiler wait for everything issued before
+  // it): slots past K read a clamped index and are masked, empty slots read
+  // pair row 0 and add nothing, and the shared row is row 0 when there is no
+  // shared expert.  Then the sum, in the order above.
+  // The row's positions and gates come in one vector load (lane j of the
+  // wave reads slot j) and are handed to every lane by readlane; as eight
+  // uniform loads the compiler issued them one after another.
+  const int NK = N * K;
+  const int slot_i = min(r * K + (int)(threadIdx.x & 7), NK - 1);
+  const int pv = pair_pos[slot_i];
+  const float gv = gates[slot_i];
   int pos[8];
   float g[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    pos[j] = j < K ? pair_pos[(size_t)r * K + j] : -1;
-    g[j] = j < K ? gates[(size_t)r * K + j] : 0.0f;
+    const int pj = __builtin_amdgcn_readlane(pv, j);
+    pos[j] = j < K ? pj : -1;
+    g[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gv), j));
   }
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (has_shared) acc = load4(y + ((size_t)N * K + r) * H + c);
+  // (the flag passes through a vector register so that the shared row is a
+  // plain load and a select, not a branch that waits for the loads above)
+  int hs = has_shared;
+  asm volatile("" : "+v"(hs));
+  const f32x4 ysh = load4(y + (hs ? (size_t)NK + r : (size_t)0) * H + c);
   f32x4 v[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    v[j] = pos[j] >= 0 ? load4(y + (size_t)pos[j] * H + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 8; ++j) v[j] = load4(y + (size_t)max(pos[j], 0) * H + c);
+  // keep every load here: sunk into the conditional sums below, a load
+  // issues only after the ones before it have been waited for
+#pragma unroll
+  for (int j = 0; j < 8; ++j) asm volatile("" ::"v"(v[j]));
+  asm volatile("" ::"v"(ysh));
+  f32x4 acc = hs ? ysh : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     if (pos[j] < 0) continue;
