@@ -44,11 +44,17 @@ __global__ __launch_bounds__(256) void permute_rows_kernel(Plan p) {
   __shared__ PermuteLds L;
   const int tid = threadIdx.x, b = blockIdx.x;
   if (tid < 64) {
+    // unconditional loads (experts past E read expert 0), so the four are in
+    // flight together
+    int c[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * tid + i;
-      if (e < p.E) L.cnt[e] = p.counts[e];
+      c[i] = p.counts[e < p.E ? e : 0];
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * tid + i < p.E) L.cnt[4 * tid + i] = c[i];
     offsets_and_tiles(p, L, b == 0);
   }
   __syncthreads();

@@ -300,6 +300,17 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
   // first row exists).  Rows past R and experts past E hold -inf logits; the
   // u of rows past R is not computed and never read.
   {
+    // the 8 logit loads are unconditional (absent rows and experts read row 0,
+    // expert 0 and are replaced by -inf), so they are in flight together: a
+    // conditional load made each wait for the one before
+    float raw[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int r = wave + 16 * h, e = lane + 64 * s;
+        raw[h][s] = lb[(r < R ? r : 0) * E + (e < E ? e : 0)];
+      }
     float lv[2][4], mx[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -308,8 +319,7 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int e = lane + 64 * s;
-        const bool ok = r < R && e < E;
-        const float v = ok ? lb[r * E + e] : -INFINITY;
+        const float v = r < R && e < E ? raw[h][s] : -INFINITY;
         l_s[r][e] = v;
         lv[h][s] = v;
         mm = fmaxf(mm, v);
