@@ -7,6 +7,10 @@ in HBM.  The default workload is one 32-row bf16 block at the model's routing
 shape (H 2048, 256 experts, top-8, I 512, shared expert I 512, mass threshold
 0.9) -- the weight-streaming bound case.
 
+The expert weights are stored as MFMA panels (clover_moe_pack_weights, run
+once at load, before any timing), the library's fast layout; `--layout rows`
+times the row-major layout instead.
+
 Successive steps cycle through `--layers` copies of the weights placed at
 different addresses (the experts of copy j are rotated by j*E/L, router
 included, so every copy routes to the same number of experts): like the
@@ -48,8 +52,10 @@ def hip():
     return L
 
 
-def layer_copies(dp, n_layers, E):
-    """Weight copies at new addresses with experts rotated by j*E/n_layers."""
+def layer_copies(dp, n_layers, E, layout):
+    """Weight copies at new addresses with experts rotated by j*E/n_layers
+    (an expert's panels are its own contiguous bytes, so rotating packed
+    weights by experts is packing the rotated ones)."""
     import torch
     import sparse_moe_ffn_softmax_amd as cm
     layers = [dp.weights]
@@ -73,7 +79,7 @@ def layer_copies(dp, n_layers, E):
                  shared_w13=cp(t["shared_w13"]), shared_w13_scale=cp(t["shared_w13_scale"]),
                  shared_w2=cp(t["shared_w2"]), shared_w2_scale=cp(t["shared_w2_scale"]))
         keep.append(c)
-        layers.append(cm.make_weights(**c))
+        layers.append(cm.make_weights(**c, layout=layout))
     return layers, keep
 
 
@@ -90,9 +96,9 @@ def source_digest(name: str) -> str:
     return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str, src: str):
+def measured_traffic(kernel: str, workload: str, src: str, layout: str):
     """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was
-    taken on the current kernel source; else None."""
+    taken on the current kernel source and weight layout; else None."""
     p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.json")
     if not os.path.exists(p):
         return None
@@ -100,7 +106,7 @@ def measured_traffic(kernel: str, workload: str, src: str):
         d = json.load(open(p))
     except ValueError:
         return None
-    if d.get("code_sha256_16") != source_digest(src):
+    if d.get("code_sha256_16") != source_digest(src) or d.get("weight_layout", "rows") != layout:
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -111,6 +117,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="block32_bf16")
+    ap.add_argument("--layout", default="panels", choices=["panels", "rows"],
+                    help="expert weight storage: MFMA panels (packed once at load) or row-major")
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="rough budget of the oracle CPU-baseline leg (0 disables it)")
@@ -143,8 +151,8 @@ def main():
     t0 = time.time()
     inp = W.generate(wl)
     print(f"[bench] generated {wl.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
-    dp = cm.upload(inp)
-    layers, _keep = layer_copies(dp, args.layers, E)
+    dp = cm.upload(inp, layout=args.layout)
+    layers, _keep = layer_copies(dp, args.layers, E, args.layout)
     ws = cm.alloc_workspace(dp.problem, K)
     odt = torch.bfloat16 if wl.act_dtype == W.BF16 else torch.float32
     out = torch.empty((N, H), dtype=odt, device="cuda")
@@ -249,7 +257,8 @@ def main():
         want = -(-(N * K * 3 // 2) // E)
         tiled = want > 16
         kname = f"expert_{'up' if dom == 2 else 'down'}{'_tiled' if tiled else ''}_kernel"
-        traffic = measured_traffic(kname, wl.name, "expert_tiled.hip" if tiled else "expert_gemm.hip")
+        traffic = measured_traffic(kname, wl.name, "expert_tiled.hip" if tiled else "expert_gemm.hip",
+                                   args.layout)
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                     "traffic": traffic, "kernel": kname,
@@ -276,7 +285,8 @@ def main():
         "data": "synthetic (seeded normal inputs and random-init weights of the stated shapes)",
         "config": {"workload": wl.name, "num_blocks": B, "block_rows": wl.block_rows, "hidden": H,
                    "experts": E, "top_k": K, "inter": I, "shared_inter": Is,
-                   "mass_threshold": tau, "weight_copies_rotated": args.layers},
+                   "mass_threshold": tau, "weight_copies_rotated": args.layers,
+                   "weight_layout": args.layout},
         "roofline": roofline,
         "call": {
             "device_us_staged": round(float(device_ms.mean() * 1e3), 2),

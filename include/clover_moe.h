@@ -114,11 +114,29 @@ typedef struct {
                              (BF16, FP4_E2M1) */
 } cmoe_problem;
 
+/* Storage of the expert weight matrices w13, w2, shared_w13 and shared_w2
+ * (cmoe_weights.layout; one layout for all four).
+ *
+ *  CMOE_LAYOUT_ROWS:   [rows, cols] row-major, as described in cmoe_weights.
+ *  CMOE_LAYOUT_PANELS: MFMA panels, the order in which the expert GEMMs read
+ *                      the weights (16 rows at a time, 16 bytes per lane, 64
+ *                      lanes per load), so that every load a wave issues is
+ *                      1 KiB of whole, consecutive cache lines.  Made from the
+ *                      row-major matrices by clover_moe_pack_weights, which
+ *                      defines the byte order.  Same bytes, same results
+ *                      (up to the order of the fp32 sums inside an MFMA).
+ * Scale arrays are row-major in both layouts. */
+typedef enum {
+    CMOE_LAYOUT_ROWS = 0,
+    CMOE_LAYOUT_PANELS = 1
+} cmoe_layout;
+
 /* Weights (host struct of device pointers). */
-/* Weight matrices are [rows, cols] row-major in weight_dtype; for FP4_E2M1
- * that is rows*cols/2 bytes.  Scale arrays: FP8_E4M3: fp32, one per 128x128
- * block, [rows/128, cols/128] per matrix; FP4_E2M1: uint8 E8M0, one per 32
- * elements of a row, [rows, cols/32] per matrix; other dtypes: ignored. */
+/* Weight matrices are [rows, cols] row-major in weight_dtype (or MFMA panels
+ * of those, see cmoe_layout); for FP4_E2M1 that is rows*cols/2 bytes.  Scale
+ * arrays: FP8_E4M3: fp32, one per 128x128 block, [rows/128, cols/128] per
+ * matrix; FP4_E2M1: uint8 E8M0, one per 32 elements of a row, [rows, cols/32]
+ * per matrix; other dtypes: ignored. */
 typedef struct {
     const float* router_w;        /* [E,H] fp32, required */
     const float* router_b;        /* [E] fp32 per-expert logit bias, or NULL */
@@ -130,6 +148,7 @@ typedef struct {
     const void* shared_w13_scale; /* fp8: [2Is/128,H/128]; fp4: [2Is,H/32] */
     const void* shared_w2;        /* [H,Is] weight_dtype; required when Is > 0 */
     const void* shared_w2_scale;  /* fp8: [H/128,Is/128]; fp4: [H,Is/32] */
+    int32_t layout;               /* cmoe_layout of w13, w2, shared_w13, shared_w2 */
 } cmoe_weights;
 
 /* Optional routing outputs (host struct of device pointers; each may be NULL). */
@@ -218,6 +237,33 @@ cmoe_status clover_moe_block_forward_staged(const cmoe_problem* problem, const c
                                             const cmoe_routing* routing,
                                             void* workspace, size_t workspace_bytes, void* stream,
                                             void* const* stage_events, int32_t n_events);
+
+/* Rearranges row-major expert weight matrices into MFMA panels
+ * (CMOE_LAYOUT_PANELS).  Queued on `stream`; one pass over the bytes, nothing
+ * converted or rounded, so packing is done once when the weights are loaded.
+ *
+ * Layout: a matrix of `rows` rows of `row_bytes` bytes becomes rows/16 panels
+ * of 16 rows, stored one after another; panel p is row_bytes/64 units of
+ * 1 KiB, and byte 16*l + b (l = 0..63, b = 0..15) of unit q of panel p is byte
+ * 64*q + 16*(l/16) + b of panel row l%16.  Panel row i is matrix row 16p + i
+ * when gate_up = 0 (w2, shared_w2).  When gate_up = 1 (w13, shared_w13:
+ * rows = 2*inter, gate rows then up rows) panel p pairs gate and up: panel
+ * row i is gate row 8p + i for i < 8 and up row inter + 8p + i - 8 for i >= 8.
+ *
+ *  src:       [count, rows, row_bytes] bytes, device, 16-byte aligned:
+ *             count row-major matrices (w13 [E,2I,H] with count = E, w2 [E,H,I],
+ *             or a shared matrix with count = 1)
+ *  dst:       the same number of bytes, device, 16-byte aligned, not
+ *             overlapping src; written
+ *  count:     number of matrices, >= 1
+ *  rows:      a multiple of 16
+ *  row_bytes: a multiple of 64 (cols * bits per element / 8)
+ *  gate_up:   1 for w13 and shared_w13, 0 for w2 and shared_w2
+ *  stream:    hipStream_t (NULL = the default stream)
+ * Errors: CMOE_ERR_NULL, CMOE_ERR_VALUE (a size outside its domain),
+ * CMOE_ERR_ALIGN, CMOE_ERR_ALIAS (src and dst overlap), CMOE_ERR_HIP. */
+cmoe_status clover_moe_pack_weights(const void* src, void* dst, int64_t count, int32_t rows,
+                                    int32_t row_bytes, int32_t gate_up, void* stream);
 
 /* Static text of a status code. */
 const char* clover_moe_status_string(cmoe_status status);

@@ -20,9 +20,12 @@ CMOE_OK, CMOE_ERR_NULL, CMOE_ERR_VALUE, CMOE_ERR_UNSUPPORTED = 0, 1, 2, 3
 CMOE_ERR_ALIGN, CMOE_ERR_ALIAS, CMOE_ERR_WORKSPACE, CMOE_ERR_HIP = 4, 5, 6, 7
 CMOE_F32, CMOE_BF16, CMOE_FP8_E4M3, CMOE_FP4_E2M1 = 0, 1, 2, 3
 DTYPE_CODES = {"f32": CMOE_F32, "bf16": CMOE_BF16, "fp8_e4m3": CMOE_FP8_E4M3, "fp4_e2m1": CMOE_FP4_E2M1}
+CMOE_LAYOUT_ROWS, CMOE_LAYOUT_PANELS = 0, 1
+LAYOUT_CODES = {"rows": CMOE_LAYOUT_ROWS, "panels": CMOE_LAYOUT_PANELS}
 
 EXPORTED = ("clover_moe_workspace_size", "clover_moe_block_forward", "clover_moe_block_forward_ex",
-            "clover_moe_block_forward_staged", "clover_moe_status_string", "clover_moe_last_error")
+            "clover_moe_block_forward_staged", "clover_moe_pack_weights", "clover_moe_status_string",
+            "clover_moe_last_error")
 NUM_STAGES = 5
 STAGE_NAMES = ("router", "route_blocks", "expert_up", "expert_down", "combine")
 
@@ -36,7 +39,8 @@ class cmoe_problem(ctypes.Structure):
 class cmoe_weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("router_w", "router_b", "w13", "w13_scale", "w2", "w2_scale",
-                 "shared_w13", "shared_w13_scale", "shared_w2", "shared_w2_scale")]
+                 "shared_w13", "shared_w13_scale", "shared_w2", "shared_w2_scale")] + [
+        ("layout", ctypes.c_int32)]
 
 
 class cmoe_routing(ctypes.Structure):
@@ -81,6 +85,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.clover_moe_block_forward_ex.argtypes = ex_args
     L.clover_moe_block_forward_staged.restype = ctypes.c_int
     L.clover_moe_block_forward_staged.argtypes = ex_args + [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]
+    L.clover_moe_pack_weights.restype = ctypes.c_int
+    L.clover_moe_pack_weights.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
     L.clover_moe_status_string.restype = ctypes.c_char_p
     L.clover_moe_status_string.argtypes = [ctypes.c_int]
     L.clover_moe_last_error.restype = ctypes.c_char_p
@@ -142,6 +149,30 @@ def clover_moe_block_forward(problem: cmoe_problem, weights: cmoe_weights, x, ma
             top_k, ctypes.byref(options), _ptr(out), rt, _ptr(workspace), workspace_bytes, stream))
 
 
+def clover_moe_pack_weights(src, dst, count: int, rows: int, row_bytes: int, gate_up: int,
+                            stream=None) -> None:
+    """Queue the row-major -> MFMA-panel rearrangement of `count` matrices of
+    `rows` x `row_bytes` bytes (src, dst: torch tensors or raw device pointers)."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    _check(load_library().clover_moe_pack_weights(_ptr(src), _ptr(dst), count, rows, row_bytes, gate_up, stream))
+
+
+def pack_matrix_stack(t, gate_up: bool, stream=None):
+    """A new device tensor holding the MFMA panels of `t`, a [..., rows, cols]
+    stack of row-major matrices in any storage dtype (the last dimension is
+    the row's storage elements, e.g. two fp4 codes per byte)."""
+    import torch
+    rows = t.shape[-2]
+    row_bytes = t.shape[-1] * t.element_size()
+    dst = torch.empty_like(t)
+    clover_moe_pack_weights(t, dst, t.numel() // (t.shape[-1] * rows), rows, row_bytes, int(gate_up), stream)
+    return dst
+
+
 def clover_moe_block_forward_staged(problem: cmoe_problem, weights: cmoe_weights, x,
                                     mass_threshold: float, top_k: int, out,
                                     routing: Optional[cmoe_routing], workspace, stage_events,
@@ -176,10 +207,10 @@ def make_problem(hidden, num_experts, inter, shared_inter, block_rows, num_block
 
 def make_weights(router_w, w13, w2, router_b=None, w13_scale=None, w2_scale=None,
                  shared_w13=None, shared_w13_scale=None, shared_w2=None,
-                 shared_w2_scale=None) -> cmoe_weights:
+                 shared_w2_scale=None, layout="rows") -> cmoe_weights:
     return cmoe_weights(_ptr(router_w), _ptr(router_b), _ptr(w13), _ptr(w13_scale), _ptr(w2),
                         _ptr(w2_scale), _ptr(shared_w13), _ptr(shared_w13_scale), _ptr(shared_w2),
-                        _ptr(shared_w2_scale))
+                        _ptr(shared_w2_scale), LAYOUT_CODES[layout])
 
 
 def make_options(expert_budget: int = 0, live_rows=None) -> cmoe_options:
@@ -201,9 +232,11 @@ class DeviceProblem:
     hidden: int
 
 
-def upload(inp, device="cuda") -> DeviceProblem:
+def upload(inp, device="cuda", layout="rows") -> DeviceProblem:
     """Copy a host ``workloads.MoEInputs`` (storage-format numpy arrays) to the
-    device, keeping the raw bytes, and describe it with the C structs."""
+    device, keeping the raw bytes, and describe it with the C structs.  With
+    layout="panels" the four expert matrices are packed on the device
+    (clover_moe_pack_weights) and only the panels are kept."""
     import numpy as np
     import torch
 
@@ -224,13 +257,19 @@ def upload(inp, device="cuda") -> DeviceProblem:
     names = ("x", "router_w", "router_b", "w13", "w13_scale", "w2", "w2_scale", "shared_w13",
              "shared_w13_scale", "shared_w2", "shared_w2_scale")
     ts = {n: dev(getattr(inp, n)) for n in names}
+    if layout == "panels":
+        for n, gate_up in (("w13", True), ("w2", False), ("shared_w13", True), ("shared_w2", False)):
+            if ts[n] is not None:
+                ts[n] = pack_matrix_stack(ts[n], gate_up)
+    elif layout != "rows":
+        raise ValueError(f"layout={layout!r}")
     live = getattr(inp, "live_rows", None)
     ts["live_rows"] = None if live is None else torch.from_numpy(np.ascontiguousarray(live, np.uint8)).to(device)
     prob = make_problem(wl.hidden, wl.num_experts, wl.inter, wl.shared_inter, wl.block_rows,
                         wl.num_blocks, wl.act_dtype, wl.weight_dtype)
     w = make_weights(ts["router_w"], ts["w13"], ts["w2"], ts["router_b"], ts["w13_scale"],
                      ts["w2_scale"], ts["shared_w13"], ts["shared_w13_scale"], ts["shared_w2"],
-                     ts["shared_w2_scale"])
+                     ts["shared_w2_scale"], layout)
     return DeviceProblem(prob, w, ts, wl.rows, wl.hidden)
 
 

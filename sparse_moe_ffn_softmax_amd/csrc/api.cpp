@@ -218,6 +218,8 @@ static cmoe_status forward_impl(const cmoe_problem* problem, const cmoe_weights*
                        (p.shared_inter > 0 && (!w->shared_w13_scale || !w->shared_w2_scale))))
     return fail(CMOE_ERR_NULL, "%s weights need every scale array",
                 fp8 ? "fp8" : "fp4");
+  if (w->layout != CMOE_LAYOUT_ROWS && w->layout != CMOE_LAYOUT_PANELS)
+    return fail(CMOE_ERR_VALUE, "weights->layout=%d is not a cmoe_layout", w->layout);
   if (!(mass_threshold > 0.0f && mass_threshold <= 1.0f))
     return fail(CMOE_ERR_VALUE, "mass_threshold=%g must be in (0, 1]", (double)mass_threshold);
   const int budget = options ? options->expert_budget : 0;
@@ -297,6 +299,7 @@ static cmoe_status forward_impl(const cmoe_problem* problem, const cmoe_weights*
   cmoe::carve(plan, p, top_k, workspace, routing);
   plan.live = live;
   plan.budget = budget;
+  plan.panels = w->layout == CMOE_LAYOUT_PANELS;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   // few routed pairs: the down GEMM writes `out` itself (stage 4 is empty)
@@ -357,6 +360,26 @@ cmoe_status clover_moe_block_forward_staged(const cmoe_problem* problem, const c
   if (!stage_events) return fail(CMOE_ERR_NULL, "stage_events is NULL");
   return forward_impl(problem, w, x, mass_threshold, top_k, options, out, routing, workspace,
                       workspace_bytes, stream, stage_events, n_events);
+}
+
+cmoe_status clover_moe_pack_weights(const void* src, void* dst, int64_t count, int32_t rows,
+                                    int32_t row_bytes, int32_t gate_up, void* stream) {
+  if (!src) return fail(CMOE_ERR_NULL, "src is NULL");
+  if (!dst) return fail(CMOE_ERR_NULL, "dst is NULL");
+  if (count < 1) return fail(CMOE_ERR_VALUE, "count=%lld must be >= 1", (long long)count);
+  if (rows < 16 || rows % 16) return fail(CMOE_ERR_VALUE, "rows=%d must be a positive multiple of 16", rows);
+  if (row_bytes < 64 || row_bytes % 64)
+    return fail(CMOE_ERR_VALUE, "row_bytes=%d must be a positive multiple of 64", row_bytes);
+  if (gate_up != 0 && gate_up != 1) return fail(CMOE_ERR_VALUE, "gate_up=%d must be 0 or 1", gate_up);
+  if ((uintptr_t)src % 16 || (uintptr_t)dst % 16)
+    return fail(CMOE_ERR_ALIGN, "src %p / dst %p not 16-byte aligned", src, dst);
+  const size_t bytes = (size_t)count * (size_t)rows * (size_t)row_bytes;
+  if (overlap({"src", (uintptr_t)src, bytes, false}, {"dst", (uintptr_t)dst, bytes, true}))
+    return fail(CMOE_ERR_ALIAS, "src and dst overlap");
+  const hipError_t e = cmoe::launch_pack_panels(src, dst, count, rows, row_bytes, gate_up,
+                                                static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(CMOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return CMOE_OK;
 }
 
 const char* clover_moe_status_string(cmoe_status s) {

@@ -34,6 +34,7 @@ struct Tile {
 struct Plan {
   int N, H, E, I, Is, R, B, K;
   int act, wt;           // cmoe_dtype codes
+  bool panels;           // expert weights in MFMA panels (CMOE_LAYOUT_PANELS), else row-major
   int max_tiles;         // grid bound for the grouped GEMMs
   int mt_max;            // MFMA row tiles per work tile: 1, 2, 4, 6 or 8
   int tile_rows;         // 16 * mt_max
@@ -102,5 +103,8 @@ hipError_t launch_expert_down_combine(const Plan& p, const cmoe_weights& w, void
 hipError_t launch_expert_tiled(const Plan& p, const cmoe_weights& w, const void* x, bool up,
                                hipStream_t s);
 hipError_t launch_combine(const Plan& p, void* out, hipStream_t s);
+// count row-major matrices of rows x row_bytes bytes -> MFMA panels (clover_moe.h)
+hipError_t launch_pack_panels(const void* src, void* dst, int64_t count, int rows, int row_bytes, int gate_up,
+                              hipStream_t s);
 
 }  // namespace cmoe

@@ -46,12 +46,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
   const int r = blockIdx.y;
   const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (c >= H) return;
-  if (live && !live[r]) return;  // a resolved row keeps the caller's cached output
   // Every load is unconditional, so that all of them are in flight at once
   // (a conditional load makes the compiler wait for everything issued before
   // it): slots past K read a clamped index and are masked, empty slots read
-  // pair row 0 and add nothing, and the shared row is row 0 when there is no
-  // shared expert.  Then the sum, in the order above.
+  // pair row 0 and add nothing, the shared row is row 0 when there is no
+  // shared expert, and the row's live flag is a byte of pair_pos when there
+  // is no mask.  Then the sum, in the order above.
+  const uint8_t* lp = live ? live + r : reinterpret_cast<const uint8_t*>(pair_pos);
+  const uint8_t lv = *lp;
   // The row's positions and gates come in one vector load (lane j of the
   // wave reads slot j) and are handed to every lane by readlane; as eight
   // uniform loads the compiler issued them one after another.
@@ -80,6 +82,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
 #pragma unroll
   for (int j = 0; j < 8; ++j) asm volatile("" ::"v"(v[j]));
   asm volatile("" ::"v"(ysh));
+  if (live && !lv) return;  // a resolved row keeps the caller's cached output
   f32x4 acc = hs ? ysh : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < 8; ++j) {

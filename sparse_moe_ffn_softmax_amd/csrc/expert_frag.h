@@ -131,6 +131,24 @@ struct Frag<WFmt::FP4> {
   }
 };
 
+// Weights arrive in 16-byte chunks: chunk q of a lane is the 16 bytes its
+// lane group needs from bytes [64q, 64q+64) of its weight row, counted from
+// the lane's first k.  Chunk q is kChunk<PK> bytes after chunk 0: the next 64
+// bytes of the row in row-major storage, the next 1 KiB unit of the panel in
+// MFMA-panel storage (CMOE_LAYOUT_PANELS in clover_moe.h).
+template <bool PK>
+constexpr int kChunk = PK ? 1024 : 64;
+
+// One weight chunk.  Panel chunks are read non-temporally: a wave's load
+// there covers 1 KiB of contiguous whole cache lines, which the hint streams
+// past the caches (row-major chunks are half cache lines, and the hint would
+// evict each line before its other half is read).
+template <bool PK>
+__device__ __forceinline__ u32x4 load_chunk(const uint8_t* p) {
+  if constexpr (PK) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  else return *reinterpret_cast<const u32x4*>(p);
+}
+
 template <typename T>
 __device__ __forceinline__ void store_act(T* p, float v);
 template <>

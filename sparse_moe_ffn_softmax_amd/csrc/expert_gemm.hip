@@ -61,6 +61,18 @@ namespace cmoe {
 // (two register buffers, alternating), or, on the fixed four-stage path, all
 // four stages at once.
 // ---------------------------------------------------------------------------
+// k order inside a 128-deep stage (MFMA only needs A and B to agree on it):
+// the element offset of the fragment lane group kg uses at step u.  fp8 pairs
+// steps: lane group kg takes k [16kg, 16kg+16) of each 64-deep pair of steps,
+// so its weights come as one 16-byte chunk per two steps instead of two
+// 8-byte loads.  Every format's lane group then reads 16 weight bytes at
+// byte 16kg of each 64 bytes of its row.
+template <WFmt F>
+__device__ __forceinline__ constexpr int a_koff(int u, int kg) {
+  if constexpr (F == WFmt::FP8) return 64 * (u / 2) + 16 * kg + 8 * (u % 2);
+  else return u * Frag<F>::kStepK + kg * Frag<F>::kGroupK;
+}
+
 template <WFmt F, int MT, int NCT>
 struct Stage {
   static constexpr int U = 128 / Frag<F>::kStep;  // MFMA steps per stage
@@ -71,34 +83,45 @@ struct Stage {
 
 // A wave computes NCT column tiles (16 weight rows each) over the same MT row
 // tiles, so each activation fragment feeds NCT MFMAs.  wrow[c]: this lane's
-// row of column tile c at its first k of the wave's range (WT units);
-// wscale[c]: fp8: that row's 128x128 block scales at that k (fp32); fp4: its
-// E8M0 bytes at that k.
-template <WFmt F, int MT, int NCT>
-__device__ __forceinline__ void load_stage(Stage<F, MT, NCT>& st,
-                                           const typename Frag<F>::WT* const (&wrow)[NCT],
+// weight chunk 0 (at the wave's first k) of column tile c; wscale[c]: fp8:
+// the row's 128x128 block scales at that k (fp32); fp4: its E8M0 bytes there.
+
+template <WFmt F, int MT, int NCT, bool PK>
+__device__ __forceinline__ void load_stage(Stage<F, MT, NCT>& st, const uint8_t* const (&wrow)[NCT],
                                            const void* const (&wscale)[NCT],
                                            const typename Frag<F>::AT* const (&arow)[MT], int k0) {
   using Fr = Frag<F>;
+  using WT = typename Fr::WT;
   constexpr int U = Stage<F, MT, NCT>::U;
+  constexpr int QB = kChunk<PK>;
 #pragma unroll
   for (int c = 0; c < NCT; ++c) {
     if constexpr (F == WFmt::FP4) {
-      // 32 codes (k 32kg .. +32 of the stage) in one load, and the stage's scales
-      const u32x4 v = *reinterpret_cast<const u32x4*>(wrow[c] + k0 / 2);
+      // 32 codes (k 32kg .. +32 of the stage) in one chunk, and the stage's scales
+      const u32x4 v = load_chunk<PK>(wrow[c] + (k0 / 128) * QB);
 #pragma unroll
       for (int u = 0; u < U; ++u) st.b[c][u] = v[u];
       st.sc[c] = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(wscale[c]) + k0 / 32);
+    } else if constexpr (F == WFmt::FP8) {
+      // one chunk (16 codes) per pair of steps, see a_koff
+#pragma unroll
+      for (int j = 0; j < U / 2; ++j) {
+        const u32x4 v = load_chunk<PK>(wrow[c] + (k0 / 64 + j) * QB);
+        st.b[c][2 * j] = typename Fr::B{v[0], v[1]};
+        st.b[c][2 * j + 1] = typename Fr::B{v[2], v[3]};
+      }
     } else {
 #pragma unroll
-      for (int u = 0; u < U; ++u) st.b[c][u] = Fr::load_b(wrow[c] + k0 + u * Fr::kStep);
+      for (int u = 0; u < U; ++u)
+        st.b[c][u] = __builtin_bit_cast(typename Fr::B,
+                                        load_chunk<PK>(wrow[c] + ((k0 + u * Fr::kStep) * (int)sizeof(WT) / 64) * QB));
     }
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      st.a[mt][u] = Fr::load_a(arow[mt] + k0 + u * Fr::kStepK);
+      st.a[mt][u] = Fr::load_a(arow[mt] + k0 + a_koff<F>(u, 0));
 }
 
 template <WFmt F, int MT, int NCT>
@@ -146,8 +169,8 @@ constexpr int kDeepStages = 4;
 template <WFmt F, int MT, int NCT>
 constexpr int stage_words() { return (int)(sizeof(Stage<F, MT, NCT>) / 4); }
 
-template <WFmt F, int MT, int NCT, bool DEEP = (F == WFmt::FP4)>
-__device__ __forceinline__ void wave_gemm(const typename Frag<F>::WT* const (&wrow)[NCT],
+template <WFmt F, int MT, int NCT, bool PK, bool DEEP = (F == WFmt::FP4)>
+__device__ __forceinline__ void wave_gemm(const uint8_t* const (&wrow)[NCT],
                                           const typename Frag<F>::AT* const (&arow)[MT], int K,
                                           const void* const (&wscale)[NCT], f32x4 (&acc)[NCT][MT]) {
 #pragma unroll
@@ -163,10 +186,10 @@ __device__ __forceinline__ void wave_gemm(const typename Frag<F>::WT* const (&wr
   if constexpr (DEEP && kDeepStages * stage_words<F, MT, NCT>() <= 160) {
     if (K == 512) {
       Stage<F, MT, NCT> st[4];
-      static_for<0, kDeepStages>([&](auto S) { load_stage<F, MT, NCT>(st[S], wrow, wscale, arow, S * 128); });
+      static_for<0, kDeepStages>([&](auto S) { load_stage<F, MT, NCT, PK>(st[S], wrow, wscale, arow, S * 128); });
       static_for<0, 4>([&](auto S) {
         constexpr int next = S + kDeepStages;
-        if constexpr (next < 4) load_stage<F, MT, NCT>(st[next], wrow, wscale, arow, next * 128);
+        if constexpr (next < 4) load_stage<F, MT, NCT, PK>(st[next], wrow, wscale, arow, next * 128);
         __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of this stage's MFMAs
         mma_stage<F, MT, NCT>(st[S], wscale, S * 128, acc);
       });
@@ -174,13 +197,13 @@ __device__ __forceinline__ void wave_gemm(const typename Frag<F>::WT* const (&wr
     }
   }
   Stage<F, MT, NCT> s0, s1;
-  load_stage<F, MT, NCT>(s0, wrow, wscale, arow, 0);
+  load_stage<F, MT, NCT, PK>(s0, wrow, wscale, arow, 0);
   for (int k0 = 0; k0 < K; k0 += 256) {
     const bool two = k0 + 128 < K;
-    if (two) load_stage<F, MT, NCT>(s1, wrow, wscale, arow, k0 + 128);
+    if (two) load_stage<F, MT, NCT, PK>(s1, wrow, wscale, arow, k0 + 128);
     mma_stage<F, MT, NCT>(s0, wscale, k0, acc);
     if (!two) break;
-    if (k0 + 256 < K) load_stage<F, MT, NCT>(s0, wrow, wscale, arow, k0 + 256);
+    if (k0 + 256 < K) load_stage<F, MT, NCT, PK>(s0, wrow, wscale, arow, k0 + 256);
     mma_stage<F, MT, NCT>(s1, wscale, k0 + 128, acc);
   }
 }
@@ -204,7 +227,7 @@ struct UpArgs {
   int N, H, E, I, Is, K, n_slices;
 };
 
-template <WFmt F, int MT, int NCT>
+template <WFmt F, int MT, int NCT, bool PK>
 __device__ __forceinline__ void up_tile(const UpArgs& a, const Tile& t, int slice) {
   using Fr = Frag<F>;
   using AT = typename Fr::AT;
@@ -218,15 +241,19 @@ __device__ __forceinline__ void up_tile(const UpArgs& a, const Tile& t, int slic
   // the waves split the hidden dimension into ks equal parts (multiples of 128)
   const int ks = (a.H % 512 == 0) ? 4 : (a.H % 256 == 0) ? 2 : 1;
   const int klen = a.H / ks, kbeg = wave * klen;
-  const WT* W = shared ? static_cast<const WT*>(a.sw13)
-                       : static_cast<const WT*>(a.w13) + (size_t)t.expert * 2 * a.I * a.H / Fr::kPack;
-  const WT* wrow[NCT];
+  const size_t rowb = (size_t)a.H * sizeof(WT) / Fr::kPack;  // bytes per weight row
+  const uint8_t* W = shared ? static_cast<const uint8_t*>(a.sw13)
+                            : static_cast<const uint8_t*>(a.w13) + (size_t)t.expert * 2 * a.I * rowb;
+  const size_t kbegb = (size_t)kbeg * sizeof(WT) / Fr::kPack;
+  const uint8_t* wrow[NCT];
   const void* wscale[NCT];
 #pragma unroll
   for (int c = 0; c < NCT; ++c) {
     const int ic = i0 + 8 * c;
     const int wr = col < 8 ? ic + col : inter + ic + col - 8;  // gate row / up row
-    wrow[c] = W + ((size_t)wr * a.H + kbeg + kg * Fr::kGroupK) / Fr::kPack;
+    // panels: column tile c is panel ic/8 (its gate rows, then its up rows)
+    wrow[c] = PK ? W + (size_t)(ic / 8) * 16 * rowb + (kbegb / 64) * kChunk<PK> + 16 * lane
+                 : W + (size_t)wr * rowb + kbegb + 16 * kg;
     wscale[c] = nullptr;
     if constexpr (F == WFmt::FP8) {
       const float* S = static_cast<const float*>(shared ? a.sw13_scale : a.w13_scale);
@@ -247,11 +274,11 @@ __device__ __forceinline__ void up_tile(const UpArgs& a, const Tile& t, int slic
   for (int mt = 0; mt < MT; ++mt) {
     const int m = mt * 16 + col < t.rows ? mt * 16 + col : 0;
     const int src = shared ? t.start + m : a.pair_row[t.start + m];
-    arow[mt] = static_cast<const AT*>(a.x) + (size_t)src * a.H + kbeg + kg * Fr::kGroupK;
+    arow[mt] = static_cast<const AT*>(a.x) + (size_t)src * a.H + kbeg + a_koff<F>(0, kg);
   }
   f32x4 acc[NCT][MT];
   if (wave < ks) {
-    wave_gemm<F, MT, NCT>(wrow, arow, klen, wscale, acc);
+    wave_gemm<F, MT, NCT, PK>(wrow, arow, klen, wscale, acc);
   } else {
 #pragma unroll
     for (int c = 0; c < NCT; ++c)
@@ -291,7 +318,7 @@ __device__ __forceinline__ void up_tile(const UpArgs& a, const Tile& t, int slic
 // down 25.6 -> 23.8 us; bf16 unchanged).  Four waves (128 VGPRs) spill.
 constexpr int kMinWavesPerSimd = 3;
 
-template <WFmt F, int MTMAX, int NCT>
+template <WFmt F, int MTMAX, int NCT, bool PK>
 __global__ __launch_bounds__(256, kMinWavesPerSimd) void expert_up_kernel(UpArgs a) {
   const int slot = blockIdx.x / a.n_slices, slice = blockIdx.x % a.n_slices;
   if (slot >= *a.tile_count) return;
@@ -299,10 +326,10 @@ __global__ __launch_bounds__(256, kMinWavesPerSimd) void expert_up_kernel(UpArgs
   const int inter = t.expert == a.E ? a.Is : a.I;
   if (slice * kUpCols * NCT >= inter) return;
   const int mt = (t.rows + 15) >> 4;  // 1..MTMAX
-  if constexpr (MTMAX >= 4) if (mt == 4) { up_tile<F, 4, NCT>(a, t, slice); return; }
-  if constexpr (MTMAX >= 3) if (mt == 3) { up_tile<F, 3, NCT>(a, t, slice); return; }
-  if constexpr (MTMAX >= 2) if (mt == 2) { up_tile<F, 2, NCT>(a, t, slice); return; }
-  up_tile<F, 1, NCT>(a, t, slice);
+  if constexpr (MTMAX >= 4) if (mt == 4) { up_tile<F, 4, NCT, PK>(a, t, slice); return; }
+  if constexpr (MTMAX >= 3) if (mt == 3) { up_tile<F, 3, NCT, PK>(a, t, slice); return; }
+  if constexpr (MTMAX >= 2) if (mt == 2) { up_tile<F, 2, NCT, PK>(a, t, slice); return; }
+  up_tile<F, 1, NCT, PK>(a, t, slice);
 }
 
 struct DownArgs {
@@ -319,7 +346,7 @@ struct DownArgs {
 
 // acc[c][mt]: the tile's y for its MT row tiles and the NCT 16-column tiles
 // of output columns starting at c0
-template <WFmt F, int MT, int NCT, bool DEEP = (F == WFmt::FP4)>
+template <WFmt F, int MT, int NCT, bool PK, bool DEEP = (F == WFmt::FP4)>
 __device__ __forceinline__ void down_acc(const DownArgs& a, const Tile& t, int c0, f32x4 (&acc)[NCT][MT]) {
   using Fr = Frag<F>;
   using AT = typename Fr::AT;
@@ -328,14 +355,16 @@ __device__ __forceinline__ void down_acc(const DownArgs& a, const Tile& t, int c
   const int col = lane & 15, kg = lane >> 4;
   const bool shared = t.expert == a.E;
   const int inter = shared ? a.Is : a.I;
-  const WT* W = shared ? static_cast<const WT*>(a.sw2)
-                       : static_cast<const WT*>(a.w2) + (size_t)t.expert * a.H * a.I / Fr::kPack;
-  const WT* wrow[NCT];
+  const size_t rowb = (size_t)inter * sizeof(WT) / Fr::kPack;  // bytes per weight row
+  const uint8_t* W = shared ? static_cast<const uint8_t*>(a.sw2)
+                            : static_cast<const uint8_t*>(a.w2) + (size_t)t.expert * a.H * rowb;
+  const uint8_t* wrow[NCT];
   const void* wscale[NCT];
 #pragma unroll
   for (int c = 0; c < NCT; ++c) {
     const int orow = c0 + 16 * c + col;  // W2 row = output column
-    wrow[c] = W + ((size_t)orow * inter + kg * Fr::kGroupK) / Fr::kPack;
+    // panels: column tile c is panel (c0 + 16c) / 16
+    wrow[c] = PK ? W + (size_t)((c0 + 16 * c) / 16) * 16 * rowb + 16 * lane : W + (size_t)orow * rowb + 16 * kg;
     wscale[c] = nullptr;
     if constexpr (F == WFmt::FP8) {
       const float* S = static_cast<const float*>(shared ? a.sw2_scale : a.w2_scale);
@@ -353,19 +382,19 @@ __device__ __forceinline__ void down_acc(const DownArgs& a, const Tile& t, int c
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = mt * 16 + col < t.rows ? mt * 16 + col : 0;
-    arow[mt] = hbase + (size_t)m * inter + kg * Fr::kGroupK;
+    arow[mt] = hbase + (size_t)m * inter + a_koff<F>(0, kg);
   }
-  wave_gemm<F, MT, NCT, DEEP>(wrow, arow, inter, wscale, acc);
+  wave_gemm<F, MT, NCT, PK, DEEP>(wrow, arow, inter, wscale, acc);
 }
 
-template <WFmt F, int MT, int NCT>
+template <WFmt F, int MT, int NCT, bool PK>
 __device__ __forceinline__ void down_tile(const DownArgs& a, const Tile& t, int slice) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kg = lane >> 4;
   // this wave's output columns: c0 + 16c .. +16 for its NCT column tiles
   const int c0 = (slice * 4 + wave) * 16 * NCT;
   f32x4 acc[NCT][MT];
-  down_acc<F, MT, NCT>(a, t, c0, acc);
+  down_acc<F, MT, NCT, PK>(a, t, c0, acc);
 
   const bool shared = t.expert == a.E;
   float* y = a.y + ((shared ? (size_t)a.N * a.K : 0) + (size_t)t.start) * a.H;
@@ -380,16 +409,16 @@ __device__ __forceinline__ void down_tile(const DownArgs& a, const Tile& t, int 
       }
 }
 
-template <WFmt F, int MTMAX, int NCT>
+template <WFmt F, int MTMAX, int NCT, bool PK>
 __global__ __launch_bounds__(256, kMinWavesPerSimd) void expert_down_kernel(DownArgs a) {
   const int slot = blockIdx.x / a.n_slices, slice = blockIdx.x % a.n_slices;
   if (slot >= *a.tile_count) return;
   const Tile t = a.tiles[slot];
   const int mt = (t.rows + 15) >> 4;  // 1..MTMAX
-  if constexpr (MTMAX >= 4) if (mt == 4) { down_tile<F, 4, NCT>(a, t, slice); return; }
-  if constexpr (MTMAX >= 3) if (mt == 3) { down_tile<F, 3, NCT>(a, t, slice); return; }
-  if constexpr (MTMAX >= 2) if (mt == 2) { down_tile<F, 2, NCT>(a, t, slice); return; }
-  down_tile<F, 1, NCT>(a, t, slice);
+  if constexpr (MTMAX >= 4) if (mt == 4) { down_tile<F, 4, NCT, PK>(a, t, slice); return; }
+  if constexpr (MTMAX >= 3) if (mt == 3) { down_tile<F, 3, NCT, PK>(a, t, slice); return; }
+  if constexpr (MTMAX >= 2) if (mt == 2) { down_tile<F, 2, NCT, PK>(a, t, slice); return; }
+  down_tile<F, 1, NCT, PK>(a, t, slice);
 }
 
 // Calls with at most kFusedMaxTiles work tiles (one-row decode: 8 experts
@@ -404,20 +433,34 @@ __global__ __launch_bounds__(256, kMinWavesPerSimd) void expert_down_kernel(Down
 constexpr int kFusedMaxTiles = 10;
 constexpr int kFusedMaxPairs = 64;  // N*K + N
 
-template <WFmt F>
+template <WFmt F, bool PK>
 __global__ __launch_bounds__(64 * kFusedMaxTiles) void expert_down_combine_kernel(DownArgs a, const int32_t* pair_pos,
                                                                    const float* gates, void* out,
                                                                    int out_bf16, const uint8_t* live) {
   __shared__ float y_s[kFusedMaxPairs][16];
+  __shared__ int pos_s[kFusedMaxPairs];
+  __shared__ float g_s[kFusedMaxPairs];
+  __shared__ uint8_t live_s[kFusedMaxPairs];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int col = lane & 15, kg = lane >> 4;
   const int c0 = blockIdx.x * 16;
-  const int NK = a.N * a.K;
+  const int N = a.N, K = a.K, NK = N * K;  // NK + N <= 64 <= blockDim.x
+  // The combine's slot positions, gates and live flags are loaded here, before
+  // the GEMM, and parked in LDS after it, so their latency hides under the
+  // GEMM's (read after the barrier, each slot's loads waited for the one
+  // before).  The loads are unconditional: thread t reads slot min(t, NK-1),
+  // and row flags come from the first bytes of pair_pos when there is no mask
+  // (read, then ignored).
+  const int tid = threadIdx.x;
+  const int pv = pair_pos[min(tid, NK - 1)];
+  const float gv = gates[min(tid, NK - 1)];
+  const uint8_t* lp = live ? live : reinterpret_cast<const uint8_t*>(pair_pos);
+  const uint8_t lv = lp[min(tid, N - 1)];
   const int nt = *a.tile_count;
   for (int slot = wave; slot < nt; slot += nw) {
     const Tile t = a.tiles[slot];
     f32x4 acc[1][1];
-    down_acc<F, 1, 1, true>(a, t, c0, acc);
+    down_acc<F, 1, 1, PK, true>(a, t, c0, acc);
     const int base = (t.expert == a.E ? NK : 0) + t.start;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -425,14 +468,21 @@ __global__ __launch_bounds__(64 * kFusedMaxTiles) void expert_down_combine_kerne
       if (m < t.rows) y_s[base + m][col] = acc[0][0][v];
     }
   }
+  if (tid < NK) {
+    pos_s[tid] = pv;
+    g_s[tid] = gv;
+  }
+  if (tid < N) live_s[tid] = live == nullptr || lv != 0;
   __syncthreads();
-  for (int i = threadIdx.x; i < a.N * 16; i += blockDim.x) {
+  for (int i = tid; i < N * 16; i += blockDim.x) {
     const int r = i >> 4, cc = i & 15;
-    if (live && !live[r]) continue;  // a resolved row keeps the caller's cached output
+    if (!live_s[r]) continue;  // a resolved row keeps the caller's cached output
     float o = a.Is > 0 ? y_s[NK + r][cc] : 0.0f;
-    for (int j = 0; j < a.K; ++j) {
-      const int pos = pair_pos[r * a.K + j];
-      if (pos >= 0) o = __builtin_fmaf(gates[r * a.K + j], y_s[pos][cc], o);
+    for (int j = 0; j < K; ++j) {
+      // an empty slot (pos < 0) reads row 0 and keeps o unchanged
+      const int pos = pos_s[r * K + j];
+      const float t = __builtin_fmaf(g_s[r * K + j], y_s[max(pos, 0)][cc], o);
+      o = pos >= 0 ? t : o;
     }
     const size_t at = (size_t)r * a.H + c0 + cc;
     if (out_bf16) static_cast<uint16_t*>(out)[at] = f32_to_bf16(o);
@@ -442,18 +492,37 @@ __global__ __launch_bounds__(64 * kFusedMaxTiles) void expert_down_combine_kerne
 
 // these kernels serve single-row-tile calls (MTMAX = 1); many-row tiles run in
 // expert_tiled.hip
-template <WFmt F>
+template <WFmt F, bool PK>
 static void launch_up(unsigned grid, hipStream_t s, const UpArgs& a) {
-  expert_up_kernel<F, 1, up_nct<F>()><<<grid, 256, 0, s>>>(a);
+  expert_up_kernel<F, 1, up_nct<F>(), PK><<<grid, 256, 0, s>>>(a);
 }
-template <WFmt F>
+template <WFmt F, bool PK>
 static void launch_down(int nct, unsigned grid, hipStream_t s, const DownArgs& a) {
   if constexpr (F == WFmt::FP4) {
-    if (nct == 4) expert_down_kernel<F, 1, 4><<<grid, 256, 0, s>>>(a);
-    else expert_down_kernel<F, 1, 2><<<grid, 256, 0, s>>>(a);
+    if (nct == 4) expert_down_kernel<F, 1, 4, PK><<<grid, 256, 0, s>>>(a);
+    else expert_down_kernel<F, 1, 2, PK><<<grid, 256, 0, s>>>(a);
   } else {
-    expert_down_kernel<F, 1, 1><<<grid, 256, 0, s>>>(a);
+    expert_down_kernel<F, 1, 1, PK><<<grid, 256, 0, s>>>(a);
   }
+}
+template <WFmt F>
+static void launch_up(bool panels, unsigned grid, hipStream_t s, const UpArgs& a) {
+  if (panels) launch_up<F, true>(grid, s, a);
+  else launch_up<F, false>(grid, s, a);
+}
+template <WFmt F>
+static void launch_down(bool panels, int nct, unsigned grid, hipStream_t s, const DownArgs& a) {
+  if (panels) launch_down<F, true>(nct, grid, s, a);
+  else launch_down<F, false>(nct, grid, s, a);
+}
+template <WFmt F>
+static void launch_down_combine(bool panels, unsigned grid, unsigned block, hipStream_t s, const DownArgs& a,
+                                const Plan& p, void* out) {
+  const int bf16 = p.act == CMOE_BF16;
+  if (panels)
+    expert_down_combine_kernel<F, true><<<grid, block, 0, s>>>(a, p.pair_pos, p.gates, out, bf16, p.live);
+  else
+    expert_down_combine_kernel<F, false><<<grid, block, 0, s>>>(a, p.pair_pos, p.gates, out, bf16, p.live);
 }
 
 static WFmt fmt_of(const Plan& p) {
@@ -485,10 +554,10 @@ hipError_t launch_expert_up(const Plan& p, const cmoe_weights& w, const void* x,
   a.n_slices = (p.I > p.Is ? p.I : p.Is) / (kUpCols * nct);
   const unsigned grid = (unsigned)p.max_tiles * (unsigned)a.n_slices;
   switch (f) {
-    case WFmt::BF16: launch_up<WFmt::BF16>(grid, s, a); break;
-    case WFmt::F32: launch_up<WFmt::F32>(grid, s, a); break;
-    case WFmt::FP8: launch_up<WFmt::FP8>(grid, s, a); break;
-    case WFmt::FP4: launch_up<WFmt::FP4>(grid, s, a); break;
+    case WFmt::BF16: launch_up<WFmt::BF16>(p.panels, grid, s, a); break;
+    case WFmt::F32: launch_up<WFmt::F32>(p.panels, grid, s, a); break;
+    case WFmt::FP8: launch_up<WFmt::FP8>(p.panels, grid, s, a); break;
+    case WFmt::FP4: launch_up<WFmt::FP4>(p.panels, grid, s, a); break;
   }
   return hipGetLastError();
 }
@@ -519,12 +588,11 @@ hipError_t launch_expert_down_combine(const Plan& p, const cmoe_weights& w, void
   a.n_slices = 0;
   const int waves = p.max_tiles;  // one per tile (at most kFusedMaxTiles)
   const unsigned grid = (unsigned)(p.H / 16), block = 64u * (unsigned)waves;
-  const int bf16 = p.act == CMOE_BF16;
   switch (fmt_of(p)) {
-    case WFmt::BF16: expert_down_combine_kernel<WFmt::BF16><<<grid, block, 0, s>>>(a, p.pair_pos, p.gates, out, bf16, p.live); break;
+    case WFmt::BF16: launch_down_combine<WFmt::BF16>(p.panels, grid, block, s, a, p, out); break;
     case WFmt::F32: return hipErrorInvalidValue;  // excluded by down_combine_fits
-    case WFmt::FP8: expert_down_combine_kernel<WFmt::FP8><<<grid, block, 0, s>>>(a, p.pair_pos, p.gates, out, bf16, p.live); break;
-    case WFmt::FP4: expert_down_combine_kernel<WFmt::FP4><<<grid, block, 0, s>>>(a, p.pair_pos, p.gates, out, bf16, p.live); break;
+    case WFmt::FP8: launch_down_combine<WFmt::FP8>(p.panels, grid, block, s, a, p, out); break;
+    case WFmt::FP4: launch_down_combine<WFmt::FP4>(p.panels, grid, block, s, a, p, out); break;
   }
   return hipGetLastError();
 }
@@ -550,10 +618,10 @@ hipError_t launch_expert_down(const Plan& p, const cmoe_weights& w, hipStream_t 
   a.n_slices = p.H / (kDownCols * nct);
   const unsigned grid = (unsigned)p.max_tiles * (unsigned)a.n_slices;
   switch (f) {
-    case WFmt::BF16: launch_down<WFmt::BF16>(nct, grid, s, a); break;
-    case WFmt::F32: launch_down<WFmt::F32>(nct, grid, s, a); break;
-    case WFmt::FP8: launch_down<WFmt::FP8>(nct, grid, s, a); break;
-    case WFmt::FP4: launch_down<WFmt::FP4>(nct, grid, s, a); break;
+    case WFmt::BF16: launch_down<WFmt::BF16>(p.panels, nct, grid, s, a); break;
+    case WFmt::F32: launch_down<WFmt::F32>(p.panels, nct, grid, s, a); break;
+    case WFmt::FP8: launch_down<WFmt::FP8>(p.panels, nct, grid, s, a); break;
+    case WFmt::FP4: launch_down<WFmt::FP4>(p.panels, nct, grid, s, a); break;
   }
   return hipGetLastError();
 }

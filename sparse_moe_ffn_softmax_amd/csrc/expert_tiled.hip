@@ -56,8 +56,9 @@ constexpr int kTiledMaxStages = 128;  // fp8 block scales held per weight row (h
 // over k in [0, Kdim).  asrc[i]: source row pointer (stage 0) of the i-th
 // activation vector this thread stages (rows past the tile repeat the tile's
 // first row, so that every load is unconditional); brow: this lane's weight
-// row at its first k (blane); bsc: its fp8 block scales, one per 128 k, in LDS.
-template <WFmt F, int MT>
+// chunk 0 (bchunk0); bsc: its fp8 block scales, one per 128 k, in LDS.  PK:
+// the weights are stored in MFMA panels.
+template <WFmt F, int MT, bool PK>
 struct TiledGemm {
   using Fr = Frag<F>;
   using AT = typename Fr::AT;
@@ -95,8 +96,17 @@ struct TiledGemm {
     else return c;                                                          // c = 4u + kg
   }
   static __device__ __forceinline__ int aread(int u, int kg) { return (4 * u + kg) * (16 / (int)sizeof(AT)); }
-  // this lane's first weight byte of a stage, relative to its weight row
-  static __device__ __forceinline__ int blane(int kg) { return kPair ? 16 * kg : kg * Fr::kGroupK / Fr::kPack; }
+  // Each lane group kg reads the 16 weight bytes at byte 16kg of every 64
+  // bytes of its row (fp8 through the paired order above), i.e. one chunk
+  // (expert_frag.h) per 64 row bytes.
+  // This lane's chunk 0 of a weight matrix W (rows of rowb bytes) whose
+  // panel (16 rows, see clover_moe.h) `panel` holds, at panel row `prow`, this
+  // lane's weight row; that row is row `row` of W in row-major storage.
+  static __device__ __forceinline__ const uint8_t* bchunk0(const uint8_t* W, size_t rowb, int row, int panel,
+                                                           int lane) {
+    if constexpr (PK) return W + (size_t)panel * 16 * rowb + 16 * lane;
+    else return W + (size_t)row * rowb + 16 * (lane >> 4);
+  }
   // one stage of this lane's weights; fp4 adds the stage's four E8M0 bytes of its row
   struct BSet {
     typename Fr::B b[U];
@@ -104,8 +114,9 @@ struct TiledGemm {
   };
 
   static __device__ __forceinline__ void run(Lds& As, const AT* const (&asrc)[AV],
-                                             const WT* brow, const void* bsc, int Kdim,
+                                             const uint8_t* brow, const void* bsc, int Kdim,
                                              f32x4 (&acc)[MT]) {
+    constexpr int QB = kChunk<PK>;
     const int tid = threadIdx.x, lane = tid & 63;
     const int col = lane & 15, kg = lane >> 4;
     const int seg = tid % VPR, r0 = tid / VPR;
@@ -127,7 +138,7 @@ struct TiledGemm {
     auto load_b = [&](BSet& bs, int k0) {
       auto& b = bs.b;
       if constexpr (F == WFmt::FP4) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(brow + k0 / 2);
+        const u32x4 v = load_chunk<PK>(brow + (k0 / 128) * QB);
 #pragma unroll
         for (int u = 0; u < U; ++u) b[u] = v[u];
         bs.sc = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(bsc) + k0 / 32);
@@ -137,13 +148,15 @@ struct TiledGemm {
       } else if constexpr (kPair) {
 #pragma unroll
         for (int j = 0; j < U / 2; ++j) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(brow + k0 + 64 * j);
+          const u32x4 v = load_chunk<PK>(brow + (k0 / 64 + j) * QB);
           b[2 * j] = typename Fr::B{v[0], v[1]};
           b[2 * j + 1] = typename Fr::B{v[2], v[3]};
         }
       } else {
 #pragma unroll
-        for (int u = 0; u < U; ++u) b[u] = Fr::load_b(brow + k0 + u * Fr::kStep);
+        for (int u = 0; u < U; ++u)
+          b[u] = __builtin_bit_cast(typename Fr::B,
+                                    load_chunk<PK>(brow + ((k0 + u * Fr::kStep) * (int)sizeof(WT) / 64) * QB));
       }
     };
     // Every row tile runs (rows past the tile are zeros in LDS): a guard per
@@ -266,9 +279,9 @@ struct TiledGemm {
   }
 };
 
-template <WFmt F, int MT>
+template <WFmt F, int MT, bool PK>
 __global__ __launch_bounds__(kTiledThreads) void expert_up_tiled_kernel(TiledArgs a) {
-  using G = TiledGemm<F, MT>;
+  using G = TiledGemm<F, MT, PK>;
   using AT = typename G::AT;
   using WT = typename G::WT;
   __shared__ typename G::Lds As;
@@ -292,11 +305,12 @@ __global__ __launch_bounds__(kTiledThreads) void expert_up_tiled_kernel(TiledArg
     const int src = shared ? t.start + rr : a.pair_row[t.start + rr];
     asrc[i] = static_cast<const AT*>(a.x) + (size_t)src * H + (tid % G::VPR) * (16 / (int)sizeof(AT));
   }
-  const WT* W = shared ? static_cast<const WT*>(a.sw)
-                       : static_cast<const WT*>(a.w) + (size_t)t.expert * 2 * a.I * H / Frag<F>::kPack;
+  const size_t rowb = (size_t)H * sizeof(WT) / Frag<F>::kPack;  // bytes per weight row
+  const uint8_t* W = shared ? static_cast<const uint8_t*>(a.sw)
+                            : static_cast<const uint8_t*>(a.w) + (size_t)t.expert * 2 * a.I * rowb;
   const int i0 = slice * kTiledUpCols + wave * 8;
   const int wr = col < 8 ? i0 + col : inter + i0 + col - 8;  // gate row / up row
-  const WT* brow = W + (size_t)wr * H / Frag<F>::kPack + G::blane(kg);
+  const uint8_t* brow = G::bchunk0(W, rowb, wr, i0 / 8, lane);
   const void* bsc = sc_s[col < 8 ? 0 : 1];
   if constexpr (F == WFmt::FP4) {
     // this lane's row of E8M0 bytes, read stage by stage
@@ -329,9 +343,9 @@ __global__ __launch_bounds__(kTiledThreads) void expert_up_tiled_kernel(TiledArg
     }
 }
 
-template <WFmt F, int MT>
+template <WFmt F, int MT, bool PK>
 __global__ __launch_bounds__(kTiledThreads) void expert_down_tiled_kernel(TiledArgs a) {
-  using G = TiledGemm<F, MT>;
+  using G = TiledGemm<F, MT, PK>;
   using AT = typename G::AT;
   using WT = typename G::WT;
   __shared__ typename G::Lds As;
@@ -354,11 +368,12 @@ __global__ __launch_bounds__(kTiledThreads) void expert_down_tiled_kernel(TiledA
     const int r = tid / G::VPR + i * G::RPP;
     asrc[i] = hb + (size_t)(r < t.rows ? r : 0) * inter + (tid % G::VPR) * (16 / (int)sizeof(AT));
   }
-  const WT* W = shared ? static_cast<const WT*>(a.sw)
-                       : static_cast<const WT*>(a.w) + (size_t)t.expert * H * a.I / Frag<F>::kPack;
+  const size_t rowb = (size_t)inter * sizeof(WT) / Frag<F>::kPack;  // bytes per weight row
+  const uint8_t* W = shared ? static_cast<const uint8_t*>(a.sw)
+                            : static_cast<const uint8_t*>(a.w) + (size_t)t.expert * H * rowb;
   const int c0 = slice * kTiledDownCols + wave * 16;
   const int orow = c0 + col;  // W2 row = output column
-  const WT* brow = W + (size_t)orow * inter / Frag<F>::kPack + G::blane(kg);
+  const uint8_t* brow = G::bchunk0(W, rowb, orow, c0 / 16, lane);
   const void* bsc = sc_s[0];
   if constexpr (F == WFmt::FP4) {
     const uint8_t* S = static_cast<const uint8_t*>(shared ? a.sws : a.ws);
@@ -389,22 +404,28 @@ __global__ __launch_bounds__(kTiledThreads) void expert_down_tiled_kernel(TiledA
     }
 }
 
-template <bool kUp, WFmt F, int MT>
+template <bool kUp, WFmt F, int MT, bool PK>
 static void launch_tiled(const TiledArgs& a, unsigned grid, hipStream_t s) {
   if constexpr (kUp)
-    expert_up_tiled_kernel<F, MT><<<grid, kTiledThreads, 0, s>>>(a);
+    expert_up_tiled_kernel<F, MT, PK><<<grid, kTiledThreads, 0, s>>>(a);
   else
-    expert_down_tiled_kernel<F, MT><<<grid, kTiledThreads, 0, s>>>(a);
+    expert_down_tiled_kernel<F, MT, PK><<<grid, kTiledThreads, 0, s>>>(a);
+}
+
+template <bool kUp, WFmt F, bool PK>
+static void launch_tiled_mt(const TiledArgs& a, int mt_max, unsigned grid, hipStream_t s) {
+  switch (mt_max) {
+    case 2: launch_tiled<kUp, F, 2, PK>(a, grid, s); break;
+    case 4: launch_tiled<kUp, F, 4, PK>(a, grid, s); break;
+    case 6: launch_tiled<kUp, F, 6, PK>(a, grid, s); break;
+    default: launch_tiled<kUp, F, 8, PK>(a, grid, s); break;
+  }
 }
 
 template <bool kUp, WFmt F>
-static void launch_tiled_mt(const TiledArgs& a, int mt_max, unsigned grid, hipStream_t s) {
-  switch (mt_max) {
-    case 2: launch_tiled<kUp, F, 2>(a, grid, s); break;
-    case 4: launch_tiled<kUp, F, 4>(a, grid, s); break;
-    case 6: launch_tiled<kUp, F, 6>(a, grid, s); break;
-    default: launch_tiled<kUp, F, 8>(a, grid, s); break;
-  }
+static void launch_tiled_mt(const TiledArgs& a, bool panels, int mt_max, unsigned grid, hipStream_t s) {
+  if (panels) launch_tiled_mt<kUp, F, true>(a, mt_max, grid, s);
+  else launch_tiled_mt<kUp, F, false>(a, mt_max, grid, s);
 }
 
 hipError_t launch_expert_tiled(const Plan& p, const cmoe_weights& w, const void* x, bool up,
@@ -434,15 +455,15 @@ hipError_t launch_expert_tiled(const Plan& p, const cmoe_weights& w, const void*
                  : p.wt == CMOE_F32      ? WFmt::F32
                                          : WFmt::BF16;
   if (up) {
-    if (f == WFmt::FP4) launch_tiled_mt<true, WFmt::FP4>(a, p.mt_max, grid, s);
-    else if (f == WFmt::FP8) launch_tiled_mt<true, WFmt::FP8>(a, p.mt_max, grid, s);
-    else if (f == WFmt::F32) launch_tiled_mt<true, WFmt::F32>(a, p.mt_max, grid, s);
-    else launch_tiled_mt<true, WFmt::BF16>(a, p.mt_max, grid, s);
+    if (f == WFmt::FP4) launch_tiled_mt<true, WFmt::FP4>(a, p.panels, p.mt_max, grid, s);
+    else if (f == WFmt::FP8) launch_tiled_mt<true, WFmt::FP8>(a, p.panels, p.mt_max, grid, s);
+    else if (f == WFmt::F32) launch_tiled_mt<true, WFmt::F32>(a, p.panels, p.mt_max, grid, s);
+    else launch_tiled_mt<true, WFmt::BF16>(a, p.panels, p.mt_max, grid, s);
   } else {
-    if (f == WFmt::FP4) launch_tiled_mt<false, WFmt::FP4>(a, p.mt_max, grid, s);
-    else if (f == WFmt::FP8) launch_tiled_mt<false, WFmt::FP8>(a, p.mt_max, grid, s);
-    else if (f == WFmt::F32) launch_tiled_mt<false, WFmt::F32>(a, p.mt_max, grid, s);
-    else launch_tiled_mt<false, WFmt::BF16>(a, p.mt_max, grid, s);
+    if (f == WFmt::FP4) launch_tiled_mt<false, WFmt::FP4>(a, p.panels, p.mt_max, grid, s);
+    else if (f == WFmt::FP8) launch_tiled_mt<false, WFmt::FP8>(a, p.panels, p.mt_max, grid, s);
+    else if (f == WFmt::F32) launch_tiled_mt<false, WFmt::F32>(a, p.panels, p.mt_max, grid, s);
+    else launch_tiled_mt<false, WFmt::BF16>(a, p.panels, p.mt_max, grid, s);
   }
   return hipGetLastError();
 }

@@ -193,3 +193,32 @@ def test_binding_raises_with_message():
         cm.clover_moe_workspace_size(problem(block_rows=12), 8)
     assert ei.value.status == cm.CMOE_ERR_UNSUPPORTED
     assert "block_rows" in str(ei.value)
+
+
+def test_invalid_weight_layout_rejected():
+    w = weights()
+    w.layout = 2
+    assert call(w=w) == cm.CMOE_ERR_VALUE
+    assert "layout" in cm.clover_moe_last_error()
+
+
+@pytest.mark.parametrize("args,expect", [
+    (dict(src=None), cm.CMOE_ERR_NULL),
+    (dict(dst=None), cm.CMOE_ERR_NULL),
+    (dict(count=0), cm.CMOE_ERR_VALUE),
+    (dict(rows=8), cm.CMOE_ERR_VALUE),
+    (dict(rows=40), cm.CMOE_ERR_VALUE),
+    (dict(row_bytes=32), cm.CMOE_ERR_VALUE),
+    (dict(row_bytes=100), cm.CMOE_ERR_VALUE),
+    (dict(gate_up=2), cm.CMOE_ERR_VALUE),
+    (dict(src=fake(2, 8)), cm.CMOE_ERR_ALIGN),
+    (dict(dst=fake(3, 4)), cm.CMOE_ERR_ALIGN),
+    (dict(dst=fake(2) + 4096), cm.CMOE_ERR_ALIAS),        # dst inside src
+])
+def test_invalid_pack_calls_rejected(args, expect):
+    a = dict(src=fake(2), dst=fake(3), count=4, rows=64, row_bytes=256, gate_up=1)
+    a.update(args)
+    lib = cm.load_library()
+    assert lib.clover_moe_pack_weights(a["src"], a["dst"], a["count"], a["rows"], a["row_bytes"],
+                                       a["gate_up"], None) == expect
+    assert cm.clover_moe_last_error()
