@@ -16,8 +16,10 @@ constexpr int kMaxTileRows = 128;
 // h columns produced by one expert_up workgroup (one 16-column MFMA tile of 8
 // gate + 8 up columns; the 4 waves split the hidden dimension).
 constexpr int kUpCols = 8;
-// output columns produced by one expert_down workgroup (4 waves x 16).
-constexpr int kDownCols = 64;
+// waves of one expert_down workgroup, and the output columns it produces
+// (16 per wave; 4-bit weights: 16 per column tile, see expert_gemm.hip)
+constexpr int kDownWaves = 2;
+constexpr int kDownCols = 16 * kDownWaves;
 
 // One unit of grouped-GEMM work: `rows` consecutive pairs of one expert,
 // starting at pair position `start` (expert == E means the shared expert,

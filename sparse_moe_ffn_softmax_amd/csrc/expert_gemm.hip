@@ -14,13 +14,16 @@
 // pair, row count).  These kernels run the calls whose tiles hold at most 16
 // rows (one MFMA row tile: one block, decode, verification); calls with more
 // rows per expert run the LDS-tiled kernels of expert_tiled.hip.  A
-// workgroup of 4 waves takes one tile and one slice of output columns, 64 KiB
-// of bf16 weights either way:
-//   expert_up   : 8 h columns = one 16-column MFMA tile of 8 gate and the
-//                 matching 8 up columns (SwiGLU pairs lanes l and l+8 of the
-//                 accumulator); the 4 waves split the hidden dimension and
-//                 their partial sums meet in LDS, added in wave order;
-//   expert_down : 64 y columns, 16 per wave.
+// workgroup takes one tile and one slice of output columns:
+//   expert_up   : 4 waves, 8 h columns = one 16-column MFMA tile of 8 gate
+//                 and the matching 8 up columns (SwiGLU pairs lanes l and l+8
+//                 of the accumulator), 64 KiB of bf16 weights; the waves split
+//                 the hidden dimension and their partial sums meet in LDS,
+//                 added in wave order;
+//   expert_down : kDownWaves = 2 waves, 32 y columns, 16 per wave (32 KiB of
+//                 bf16 weights at I = 512; with 4 waves and 64 columns the
+//                 last, partly filled round of workgroups cost about 1 us of
+//                 the one-block down kernel's 55).
 // 4-bit weights are four times smaller, so there a wave takes four (up) or
 // four or two (down, by H) such column tiles, and each activation fragment it
 // loads feeds one MFMA per column tile.
@@ -392,7 +395,7 @@ __device__ __forceinline__ void down_tile(const DownArgs& a, const Tile& t, int 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kg = lane >> 4;
   // this wave's output columns: c0 + 16c .. +16 for its NCT column tiles
-  const int c0 = (slice * 4 + wave) * 16 * NCT;
+  const int c0 = (slice * kDownWaves + wave) * 16 * NCT;
   f32x4 acc[NCT][MT];
   down_acc<F, MT, NCT, PK>(a, t, c0, acc);
 
@@ -410,7 +413,7 @@ __device__ __forceinline__ void down_tile(const DownArgs& a, const Tile& t, int 
 }
 
 template <WFmt F, int MTMAX, int NCT, bool PK>
-__global__ __launch_bounds__(256, kMinWavesPerSimd) void expert_down_kernel(DownArgs a) {
+__global__ __launch_bounds__(64 * kDownWaves, kMinWavesPerSimd) void expert_down_kernel(DownArgs a) {
   const int slot = blockIdx.x / a.n_slices, slice = blockIdx.x % a.n_slices;
   if (slot >= *a.tile_count) return;
   const Tile t = a.tiles[slot];
@@ -499,10 +502,10 @@ static void launch_up(unsigned grid, hipStream_t s, const UpArgs& a) {
 template <WFmt F, bool PK>
 static void launch_down(int nct, unsigned grid, hipStream_t s, const DownArgs& a) {
   if constexpr (F == WFmt::FP4) {
-    if (nct == 4) expert_down_kernel<F, 1, 4, PK><<<grid, 256, 0, s>>>(a);
-    else expert_down_kernel<F, 1, 2, PK><<<grid, 256, 0, s>>>(a);
+    if (nct == 4) expert_down_kernel<F, 1, 4, PK><<<grid, 64 * kDownWaves, 0, s>>>(a);
+    else expert_down_kernel<F, 1, 2, PK><<<grid, 64 * kDownWaves, 0, s>>>(a);
   } else {
-    expert_down_kernel<F, 1, 1, PK><<<grid, 256, 0, s>>>(a);
+    expert_down_kernel<F, 1, 1, PK><<<grid, 64 * kDownWaves, 0, s>>>(a);
   }
 }
 template <WFmt F>

@@ -11,9 +11,10 @@
 // exactly with their scale.
 //
 // With tens of rows per expert every weight byte feeds tens of MFMA rows, so
-// the activation tile must not be fetched once per wave.  A workgroup
-// (8 waves) owns one tile of up to T = 16*MT rows and a slice of output
-// columns (up: 64 h columns = 128 weight columns; down: 128 y columns).  The
+// the activation tile must not be fetched once per wave.  A workgroup of
+// NW waves (below) owns one tile of up to T = 16*MT rows and a slice of
+// output columns (up: 8 h columns = 16 weight columns per wave; down: 16 y
+// columns per wave).  The
 // hidden (or intermediate) dimension is consumed in stages of 256 bytes per
 // row: the gathered activation rows of the next stage are loaded into
 // registers and parked in the other half of a double-buffered LDS tile while
@@ -30,10 +31,16 @@
 
 namespace cmoe {
 
-constexpr int kTiledWaves = 8;                  // waves per workgroup, 16 MFMA columns each
-constexpr int kTiledThreads = 64 * kTiledWaves;
-constexpr int kTiledUpCols = 8 * kTiledWaves;     // h columns per workgroup (gate + up pairs)
-constexpr int kTiledDownCols = 16 * kTiledWaves;  // y columns per workgroup
+// Waves per workgroup, 16 MFMA columns each, by row-tile count: 4 for tiles
+// of at most 32 rows, 8 above.  Short tiles make long, few workgroups (16
+// blocks: 272 tiles x 8 column slices of 8 waves is under three rounds of
+// the chip), and halving the workgroup halves the last round's idle share
+// (16 blocks: gate/up 183 -> 177 us, down 105 -> 101 us); tall tiles need
+// the 8 waves to share their activation tile's LDS (64 blocks with 4 waves:
+// gate/up 134 -> 171 us).
+__host__ __device__ constexpr int tiled_waves(int mt) { return mt <= 2 ? 4 : 8; }
+__host__ __device__ constexpr int tiled_up_cols(int mt) { return 8 * tiled_waves(mt); }     // h columns per workgroup
+__host__ __device__ constexpr int tiled_down_cols(int mt) { return 16 * tiled_waves(mt); }  // y columns per workgroup
 
 struct TiledArgs {
   const void* x;     // up: activations [N,H]
@@ -67,7 +74,9 @@ struct TiledGemm {
   static constexpr int KS = 256 / (int)sizeof(AT);  // k per stage (256 bytes of a row)
   static constexpr int U = KS / Fr::kStep;          // MFMA steps per stage
   static constexpr int VPR = 16;                    // 16-byte vectors per row per stage
-  static constexpr int RPP = kTiledThreads / VPR;   // rows staged per pass of the workgroup
+  static constexpr int NW = tiled_waves(MT);        // waves per workgroup
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int RPP = THREADS / VPR;         // rows staged per pass of the workgroup
   static constexpr int AV = T / RPP;                // vectors per thread per stage
   // 288-byte rows: the MFMA fragment reads (16 rows at one offset, the four
   // lane groups 64 contiguous bytes) are free of bank conflicts (a 272-byte
@@ -280,7 +289,7 @@ struct TiledGemm {
 };
 
 template <WFmt F, int MT, bool PK>
-__global__ __launch_bounds__(kTiledThreads) void expert_up_tiled_kernel(TiledArgs a) {
+__global__ __launch_bounds__(64 * tiled_waves(MT)) void expert_up_tiled_kernel(TiledArgs a) {
   using G = TiledGemm<F, MT, PK>;
   using AT = typename G::AT;
   using WT = typename G::WT;
@@ -292,7 +301,8 @@ __global__ __launch_bounds__(kTiledThreads) void expert_up_tiled_kernel(TiledArg
   const Tile t = a.tiles[slot];
   const bool shared = t.expert == a.E;
   const int inter = shared ? a.Is : a.I;
-  if (slice * kTiledUpCols >= inter) return;
+  constexpr int UPC = tiled_up_cols(MT);
+  if (slice * UPC >= inter) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, kg = lane >> 4;
   const int H = a.H;
@@ -308,7 +318,7 @@ __global__ __launch_bounds__(kTiledThreads) void expert_up_tiled_kernel(TiledArg
   const size_t rowb = (size_t)H * sizeof(WT) / Frag<F>::kPack;  // bytes per weight row
   const uint8_t* W = shared ? static_cast<const uint8_t*>(a.sw)
                             : static_cast<const uint8_t*>(a.w) + (size_t)t.expert * 2 * a.I * rowb;
-  const int i0 = slice * kTiledUpCols + wave * 8;
+  const int i0 = slice * UPC + wave * 8;
   const int wr = col < 8 ? i0 + col : inter + i0 + col - 8;  // gate row / up row
   const uint8_t* brow = G::bchunk0(W, rowb, wr, i0 / 8, lane);
   const void* bsc = sc_s[col < 8 ? 0 : 1];
@@ -324,8 +334,8 @@ __global__ __launch_bounds__(kTiledThreads) void expert_up_tiled_kernel(TiledArg
     // the workgroup's gate rows share one 128-row scale block, its up rows
     // another; the first stage's barrier orders these writes before any read
     const int ns = H / 128;
-    const int srow[2] = {(slice * kTiledUpCols) / 128, (inter + slice * kTiledUpCols) / 128};
-    for (int i = tid; i < 2 * ns; i += kTiledThreads) sc_s[i / ns][i % ns] = S[(size_t)srow[i / ns] * ns + i % ns];
+    const int srow[2] = {(slice * UPC) / 128, (inter + slice * UPC) / 128};
+    for (int i = tid; i < 2 * ns; i += G::THREADS) sc_s[i / ns][i % ns] = S[(size_t)srow[i / ns] * ns + i % ns];
   }
   f32x4 acc[MT];
   G::run(As, asrc, brow, bsc, H, acc);
@@ -344,7 +354,7 @@ __global__ __launch_bounds__(kTiledThreads) void expert_up_tiled_kernel(TiledArg
 }
 
 template <WFmt F, int MT, bool PK>
-__global__ __launch_bounds__(kTiledThreads) void expert_down_tiled_kernel(TiledArgs a) {
+__global__ __launch_bounds__(64 * tiled_waves(MT)) void expert_down_tiled_kernel(TiledArgs a) {
   using G = TiledGemm<F, MT, PK>;
   using AT = typename G::AT;
   using WT = typename G::WT;
@@ -371,7 +381,7 @@ __global__ __launch_bounds__(kTiledThreads) void expert_down_tiled_kernel(TiledA
   const size_t rowb = (size_t)inter * sizeof(WT) / Frag<F>::kPack;  // bytes per weight row
   const uint8_t* W = shared ? static_cast<const uint8_t*>(a.sw)
                             : static_cast<const uint8_t*>(a.w) + (size_t)t.expert * H * rowb;
-  const int c0 = slice * kTiledDownCols + wave * 16;
+  const int c0 = slice * tiled_down_cols(MT) + wave * 16;
   const int orow = c0 + col;  // W2 row = output column
   const uint8_t* brow = G::bchunk0(W, rowb, orow, c0 / 16, lane);
   const void* bsc = sc_s[0];
@@ -381,11 +391,12 @@ __global__ __launch_bounds__(kTiledThreads) void expert_down_tiled_kernel(TiledA
     bsc = S + (size_t)orow * (inter / 32);
   }
   if constexpr (F == WFmt::FP8) {
-    // the workgroup's 128 output rows are one scale block row
+    // the workgroup's 64 or 128 output rows lie in one 128-row scale block row
     const float* S = static_cast<const float*>(shared ? a.sws : a.ws);
     if (!shared) S += (size_t)t.expert * (H / 128) * (a.I / 128);
     const int ns = inter / 128;
-    for (int i = tid; i < ns; i += kTiledThreads) sc_s[0][i] = S[(size_t)slice * ns + i];
+    const int srow = (slice * tiled_down_cols(MT)) / 128;
+    for (int i = tid; i < ns; i += G::THREADS) sc_s[0][i] = S[(size_t)srow * ns + i];
   }
   f32x4 acc[MT];
   G::run(As, asrc, brow, bsc, inter, acc);
@@ -407,9 +418,9 @@ __global__ __launch_bounds__(kTiledThreads) void expert_down_tiled_kernel(TiledA
 template <bool kUp, WFmt F, int MT, bool PK>
 static void launch_tiled(const TiledArgs& a, unsigned grid, hipStream_t s) {
   if constexpr (kUp)
-    expert_up_tiled_kernel<F, MT, PK><<<grid, kTiledThreads, 0, s>>>(a);
+    expert_up_tiled_kernel<F, MT, PK><<<grid, 64 * tiled_waves(MT), 0, s>>>(a);
   else
-    expert_down_tiled_kernel<F, MT, PK><<<grid, kTiledThreads, 0, s>>>(a);
+    expert_down_tiled_kernel<F, MT, PK><<<grid, 64 * tiled_waves(MT), 0, s>>>(a);
 }
 
 template <bool kUp, WFmt F, bool PK>
@@ -448,7 +459,7 @@ hipError_t launch_expert_tiled(const Plan& p, const cmoe_weights& w, const void*
   a.I = p.I;
   a.Is = p.Is;
   a.K = p.K;
-  a.n_slices = up ? (p.I > p.Is ? p.I : p.Is) / kTiledUpCols : p.H / kTiledDownCols;
+  a.n_slices = up ? (p.I > p.Is ? p.I : p.Is) / tiled_up_cols(p.mt_max) : p.H / tiled_down_cols(p.mt_max);
   const unsigned grid = tile_grid(p.max_tiles, a.n_slices);
   const WFmt f = p.wt == CMOE_FP4_E2M1   ? WFmt::FP4
                  : p.wt == CMOE_FP8_E4M3 ? WFmt::FP8
