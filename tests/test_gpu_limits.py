@@ -5,8 +5,9 @@ within the bars of tests/parity.py, as everywhere else."""
 import numpy as np
 import pytest
 
+import sparse_moe_ffn_softmax_amd as cm
 import workloads as W
-from parity import check
+from parity import bits, check, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -29,6 +30,24 @@ def test_max_hidden():
 def test_max_inter():
     # I = Is = 8192: the down GEMM runs 64 stages; gate/up 1024 column slices
     check(W.generate(_wl("max_inter", 2, 8, 128, 16, 4, 8192, 8192, seed=202)), threads=16)
+
+
+@pytest.mark.parametrize("name,shape", [
+    ("max_hidden_panels", (1, 8, 16384, 16, 4, 128, 128)),
+    ("max_inter_panels", (2, 8, 128, 16, 4, 8192, 8192)),
+    ("max_hidden_fp4_panels", (1, 8, 16384, 16, 4, 128, 128)),
+])
+def test_limits_on_panel_weights(name, shape):
+    """The largest panel shapes (rows of 16384 bf16 elements, 8192-row down
+    matrices, 4-bit rows of 8 KiB) give the row-major call's output bit for
+    bit."""
+    wt = W.FP4 if "fp4" in name else W.BF16
+    wl = _wl(name, *shape, wt=wt, seed=205)
+    inp = W.generate(wl)
+    out_r, rt_r = run_gpu(inp, wl.mass_threshold, wl.top_k)
+    out_p, rt_p = run_gpu(inp, wl.mass_threshold, wl.top_k, dp=cm.upload(inp, layout="panels"))
+    np.testing.assert_array_equal(bits(rt_p["topk_idx"]), bits(rt_r["topk_idx"]))
+    np.testing.assert_array_equal(bits(out_p), bits(out_r))
 
 
 def test_max_blocks_sampled():
