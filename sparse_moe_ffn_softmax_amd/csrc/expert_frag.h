@@ -8,10 +8,14 @@
 // same for A and B, so each lane loads 16 contiguous bytes of its row.
 //
 // Inside a 128-deep stage, lane group kg (= l/16) covers k kGroupK*kg + u*kStepK
-// .. +kLane at MFMA step u.  For bf16, fp32 and fp8 that is the natural
-// order (kGroupK = kLane, kStepK = kStep).  For fp4 each lane group takes a
+// .. +kLane at MFMA step u.  For bf16 and fp32 that is the natural order
+// (kGroupK = kLane, kStepK = kStep).  For fp4 each lane group takes a
 // contiguous 32 k (one MX scale block), so its 32 codes are one 16-byte load
-// and it needs one scale per stage.
+// and it needs one scale per stage.  fp8 departs from its kGroupK/kStepK in
+// both kernel families: lane group kg takes k [16kg, 16kg+16) of each 64-deep
+// pair of steps, so its 16 codes are one 16-byte load per two steps.  In
+// every format a lane group thus reads 16 weight bytes at byte 16kg of each
+// 64 bytes of its row (one weight chunk, below).
 #pragma once
 #include "cmoe_device.h"
 
@@ -36,7 +40,6 @@ struct Frag<WFmt::BF16> {
   using AT = uint16_t;
   using WT = uint16_t;
   static __device__ __forceinline__ A load_a(const AT* p) { return *reinterpret_cast<const u32x4*>(p); }
-  static __device__ __forceinline__ B load_b(const WT* p) { return *reinterpret_cast<const u32x4*>(p); }
   static __device__ __forceinline__ A zero_a() { return u32x4{0u, 0u, 0u, 0u}; }
   static __device__ __forceinline__ f32x4 mma(A a, B b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -55,7 +58,6 @@ struct Frag<WFmt::F32> {
   using AT = float;
   using WT = float;
   static __device__ __forceinline__ A load_a(const AT* p) { return *reinterpret_cast<const f32x4*>(p); }
-  static __device__ __forceinline__ B load_b(const WT* p) { return *reinterpret_cast<const f32x4*>(p); }
   static __device__ __forceinline__ A zero_a() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
   static __device__ __forceinline__ f32x4 mma(A a, B b, f32x4 c) {
     c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
@@ -77,7 +79,6 @@ struct Frag<WFmt::FP8> {
   using AT = uint16_t;
   using WT = uint8_t;
   static __device__ __forceinline__ A load_a(const AT* p) { return *reinterpret_cast<const u32x4*>(p); }
-  static __device__ __forceinline__ B load_b(const WT* p) { return *reinterpret_cast<const u32x2*>(p); }
   static __device__ __forceinline__ A zero_a() { return u32x4{0u, 0u, 0u, 0u}; }
   static __device__ __forceinline__ u32x4 widen(B b) {
     // exact e4m3 -> bf16 (scale 1.0), two codes per instruction

@@ -88,7 +88,6 @@ struct Stage {
 // tiles, so each activation fragment feeds NCT MFMAs.  wrow[c]: this lane's
 // weight chunk 0 (at the wave's first k) of column tile c; wscale[c]: fp8:
 // the row's 128x128 block scales at that k (fp32); fp4: its E8M0 bytes there.
-
 template <WFmt F, int MT, int NCT, bool PK>
 __device__ __forceinline__ void load_stage(Stage<F, MT, NCT>& st, const uint8_t* const (&wrow)[NCT],
                                            const void* const (&wscale)[NCT],
