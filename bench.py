@@ -117,6 +117,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="block32_bf16")
+    ap.add_argument("--tau", type=float, default=None, help="mass threshold (default: the workload's)")
+    ap.add_argument("--top-k", type=int, default=None, help="top-k (default: the workload's)")
     ap.add_argument("--layout", default="panels", choices=["panels", "rows"],
                     help="expert weight storage: MFMA panels (packed once at load) or row-major")
     ap.add_argument("--layers", type=int, default=4)
@@ -146,7 +148,8 @@ def main():
         del src, dst
 
     wl = W.WORKLOADS[args.workload]
-    K, tau = wl.top_k, wl.mass_threshold
+    K = wl.top_k if args.top_k is None else args.top_k
+    tau = wl.mass_threshold if args.tau is None else args.tau
     N, H, E, I, Is, B = wl.rows, wl.hidden, wl.num_experts, wl.inter, wl.shared_inter, wl.num_blocks
     t0 = time.time()
     inp = W.generate(wl)
@@ -243,6 +246,8 @@ def main():
     call_bytes = (touched * (3 * H * I * wsz + sc_up + sc_dn) + (3 * H * Is * wsz + sc_up_s + sc_dn_s)
                   + 4 * E * H + N * H * 2 * asz)
     mfma_flops = 6.0 * H * I * pairs + 6.0 * H * Is * N
+    up_flops = 4.0 * H * I * pairs + 4.0 * H * Is * n_sh
+    dn_flops = 2.0 * H * I * pairs + 2.0 * H * Is * n_sh
     router_flops = 2.0 * N * H * E
 
     mean_stage = stage_ms.mean(0)
@@ -264,6 +269,17 @@ def main():
                     "traffic": traffic, "kernel": kname,
                     "algorithmic_bytes_per_launch": int(dom_bytes.mean()),
                     "avg_launch_us": round(float(stage_ms[:, dom].mean() * 1e3), 2)}
+        # past the ridge (MFMA peak / HBM peak flop per byte) the kernel's
+        # roof is the matrix cores: report it against the MFMA peak instead
+        dom_flops = up_flops if dom == 2 else dn_flops
+        mfma_peak = MFMA_PEAK_TFLOPS[{W.BF16: "bf16", W.F32: "f32", W.FP8: "fp8_e4m3",
+                                      W.FP4: "fp4_e2m1"}[wl.weight_dtype]]
+        if dom_flops.mean() / dom_bytes.mean() > mfma_peak * 1e12 / (HBM_PEAK_GBPS * 1e9):
+            tflops = float(dom_flops.sum() / (stage_ms[:, dom].sum() * 1e-3) / 1e12)
+            roofline.update({"bound": "mfma", "achieved": round(tflops, 2), "peak": mfma_peak,
+                             "unit": "TFLOP/s", "frac": round(tflops / mfma_peak, 4),
+                             "algorithmic_flops_per_launch": float(dom_flops.mean()),
+                             "hbm_gbps": round(achieved, 1)})
     else:
         roofline = {"bound": "alu", "achieved": None, "peak": None, "unit": None, "frac": None,
                     "traffic": None, "kernel": dom_name}

@@ -93,6 +93,12 @@ WORKLOADS: Dict[str, Workload] = {
                                         BF16, 0.9, seed=7, expert_budget=64, live_fraction=0.5),
     # one 32-row block with 4-bit experts (MXFP4 stand-in), bf16 activations
     "block32_mxfp4": Workload("block32_mxfp4", 1, 32, 2048, 256, 8, 512, 512, BF16, FP4, 0.9, seed=8),
+    # more blocks per call than the 64-block case, fp8 weights: the mean rows
+    # per expert equals the block count, so past ~160 blocks the GEMMs have
+    # more than 312 flop per weight byte (the bf16 MFMA ridge against HBM)
+    "blocks128_fp8": Workload("blocks128_fp8", 128, 32, 2048, 256, 8, 512, 512, BF16, FP8, 0.9, seed=9),
+    "blocks256_fp8": Workload("blocks256_fp8", 256, 32, 2048, 256, 8, 512, 512, BF16, FP8, 0.9, seed=10),
+    "blocks512_fp8": Workload("blocks512_fp8", 512, 32, 2048, 256, 8, 512, 512, BF16, FP8, 0.9, seed=11),
 }
 
 # Threshold / top-k sweep run on the skewed workload (1.0 = unrestricted top-k;
