@@ -108,9 +108,9 @@ struct TiledGemm {
   // Each lane group kg reads the 16 weight bytes at byte 16kg of every 64
   // bytes of its row (fp8 through the paired order above), i.e. one chunk
   // (expert_frag.h) per 64 row bytes.
-  // This lane's chunk 0 of a weight matrix W (rows of rowb bytes) whose
-  // panel (16 rows, see clover_moe.h) `panel` holds, at panel row `prow`, this
-  // lane's weight row; that row is row `row` of W in row-major storage.
+  // This lane's chunk 0 of a weight matrix W (rows of rowb bytes): in
+  // row-major storage its weight row is row `row` of W; in panel storage it
+  // is panel row lane % 16 of panel `panel` (16 rows, see clover_moe.h).
   static __device__ __forceinline__ const uint8_t* bchunk0(const uint8_t* W, size_t rowb, int row, int panel,
                                                            int lane) {
     if constexpr (PK) return W + (size_t)panel * 16 * rowb + 16 * lane;
