@@ -46,7 +46,8 @@
  *  - Every pointer argument of clover_moe_block_forward, and every pointer in
  *    the structs, is a DEVICE pointer unless stated otherwise; the struct
  *    objects themselves live in host memory.  Arrays are row-major and
- *    contiguous.  Device pointers must be 16-byte aligned.
+ *    contiguous (expert weights may instead be MFMA panels, see
+ *    cmoe_layout).  Device pointers must be 16-byte aligned.
  *  - Ownership: the caller allocates and frees everything, including the
  *    workspace.  The library allocates no memory, keeps no pointer after the
  *    call returns, never synchronises the host and never changes the current
@@ -123,8 +124,9 @@ typedef struct {
  *                      lanes per load), so that every load a wave issues is
  *                      1 KiB of whole, consecutive cache lines.  Made from the
  *                      row-major matrices by clover_moe_pack_weights, which
- *                      defines the byte order.  Same bytes, same results
- *                      (up to the order of the fp32 sums inside an MFMA).
+ *                      defines the byte order.  The kernels give every lane
+ *                      the same weight bytes in the same registers in either
+ *                      layout, so the results are bit-identical.
  * Scale arrays are row-major in both layouts. */
 typedef enum {
     CMOE_LAYOUT_ROWS = 0,
