@@ -15,16 +15,18 @@ from test_gpu_parity import FEW, MID
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("wl", [
-    MID.with_(name="graph_mid_tiled", seed=131),                      # tiled GEMMs (16 rows per expert)
-    FEW.with_(name="graph_few_register", seed=132),                   # register GEMMs (one row tile)
-    MID.with_(name="graph_mid_noshared", shared_inter=0, seed=133),   # no shared expert
-], ids=lambda w: w.name)
-def test_graph_replay_matches_eager(wl):
+@pytest.mark.parametrize("wl,layout", [
+    (MID.with_(name="graph_mid_tiled", seed=131), "rows"),                     # tiled GEMMs (16 rows per expert)
+    (FEW.with_(name="graph_few_register", seed=132), "rows"),                  # register GEMMs (one row tile)
+    (MID.with_(name="graph_mid_noshared", shared_inter=0, seed=133), "rows"),  # no shared expert
+    (MID.with_(name="graph_mid_tiled_panels", seed=134), "panels"),            # MFMA-panel weights
+    (FEW.with_(name="graph_few_register_panels", seed=135), "panels"),
+], ids=lambda v: v.name if hasattr(v, "name") else v)
+def test_graph_replay_matches_eager(wl, layout):
     import torch
     inp = W.generate(wl)
     K, tau = wl.top_k, wl.mass_threshold
-    dp = cm.upload(inp)
+    dp = cm.upload(inp, layout=layout)
     ws = cm.alloc_workspace(dp.problem, K)
     rt_t, rt = cm.alloc_routing(dp.problem, K)
     out = torch.empty((wl.rows, wl.hidden), dtype=torch.bfloat16, device="cuda")

@@ -47,10 +47,15 @@ def test_pack_matches_the_definition(count, rows, row_bytes, gate_up):
     rng = np.random.default_rng(count * 1000 + rows + row_bytes + gate_up)
     a = rng.integers(0, 256, size=(count, rows, row_bytes), dtype=np.uint8)
     src = torch.from_numpy(a).cuda()
-    dst = torch.full_like(src, 0xA5)
+    # dst inside a larger buffer, with 4 KiB canaries on both sides
+    n = a.size
+    buf = torch.full((n + 8192,), 0xA5, dtype=torch.uint8, device="cuda")
+    dst = buf[4096:4096 + n]
     cm.clover_moe_pack_weights(src, dst, count, rows, row_bytes, gate_up)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(dst.cpu().numpy().reshape(-1), panels_by_definition(a, bool(gate_up)))
+    got = buf.cpu().numpy()
+    np.testing.assert_array_equal(got[4096:4096 + n], panels_by_definition(a, bool(gate_up)))
+    assert np.all(got[:4096] == 0xA5) and np.all(got[4096 + n:] == 0xA5), "write outside dst"
     np.testing.assert_array_equal(src.cpu().numpy(), a)  # the source is left alone
 
 
