@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
                                                             const float* __restrict__ w,
                                                             const float* __restrict__ bias,
                                                             float* __restrict__ logits, int N,
-                                                            int H, int E) {
+                                                            int H, int E, int emajor) {
   constexpr int RT = 8 * TR;                 // rows per workgroup
   constexpr int ET = 4 * TE;                 // experts per workgroup
   constexpr int KP = KB + 4;                 // padded LDS row (breaks bank aliasing)
@@ -77,8 +77,9 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
   const int q = tid & 31;
   const int rq = q & 7;    // row group: rows rq, rq + 8, ..., rq + 8(TR-1)
   const int eq = q >> 3;   // expert group: experts eq*TE .. eq*TE + TE-1
-  const int row0 = blockIdx.x * RT;
-  const int e0 = blockIdx.y * ET;
+  // emajor: expert slices along x, row groups along y (see launch_shape)
+  const int row0 = (emajor ? blockIdx.y : blockIdx.x) * RT;
+  const int e0 = (emajor ? blockIdx.x : blockIdx.y) * ET;
   const int L = H / 8;     // chunk length, a multiple of KB
   const int S = L / KB;    // slices (1 when NBUF == 1)
 
@@ -226,16 +227,24 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
   }
 }
 
+// Workgroups are dispatched to the 8 XCDs round-robin by linear id, and each
+// XCD has its own L2.  emajor puts the expert slices along x: the row groups
+// of one slice then have ids a multiple of the slice count apart, which is a
+// multiple of 8 for E = 256, so they share an XCD and its L2 holds that
+// slice of Wr for all of them; x is then fetched by every XCD.  That is the
+// cheaper side when there are few rows (one 32-row block: 3 MB instead of
+// 8 MB from HBM), the dearer one with many (2048 rows: 66 MB instead of 24).
 template <int TR, int TE, int KB, int NBUF = 2>
-static void launch_shape(const Plan& p, const void* x, const float* w, const float* b,
+static void launch_shape(const Plan& p, const void* x, const float* w, const float* b, bool emajor,
                          hipStream_t s) {
-  dim3 grid((p.N + 8 * TR - 1) / (8 * TR), (p.E + 4 * TE - 1) / (4 * TE));
+  const unsigned rg = (p.N + 8 * TR - 1) / (8 * TR), es = (p.E + 4 * TE - 1) / (4 * TE);
+  const dim3 grid = emajor ? dim3(es, rg) : dim3(rg, es);
   if (p.act == CMOE_BF16)
     router_logits_kernel<TR, TE, KB, NBUF, uint16_t><<<grid, 256, 0, s>>>(
-        static_cast<const uint16_t*>(x), w, b, p.logits, p.N, p.H, p.E);
+        static_cast<const uint16_t*>(x), w, b, p.logits, p.N, p.H, p.E, emajor);
   else
     router_logits_kernel<TR, TE, KB, NBUF, float><<<grid, 256, 0, s>>>(
-        static_cast<const float*>(x), w, b, p.logits, p.N, p.H, p.E);
+        static_cast<const float*>(x), w, b, p.logits, p.N, p.H, p.E, emajor);
 }
 
 hipError_t launch_router(const Plan& p, const void* x, const float* router_w,
@@ -245,15 +254,15 @@ hipError_t launch_router(const Plan& p, const void* x, const float* router_w,
   if (p.N <= 256) {
     // few rows (one block per call): one accumulator per thread keeps
     // enough workgroups in flight; whole chunks in one slice where they fit
-    if (L == 256) launch_shape<1, 1, 256, 1>(p, x, router_w, router_b, s);
-    else if (L == 128) launch_shape<1, 1, 128, 1>(p, x, router_w, router_b, s);
-    else if (L % 64 == 0) launch_shape<1, 1, 64>(p, x, router_w, router_b, s);
-    else if (L % 32 == 0) launch_shape<1, 1, 32>(p, x, router_w, router_b, s);
-    else launch_shape<1, 1, 16>(p, x, router_w, router_b, s);
+    if (L == 256) launch_shape<1, 1, 256, 1>(p, x, router_w, router_b, true, s);
+    else if (L == 128) launch_shape<1, 1, 128, 1>(p, x, router_w, router_b, true, s);
+    else if (L % 64 == 0) launch_shape<1, 1, 64>(p, x, router_w, router_b, true, s);
+    else if (L % 32 == 0) launch_shape<1, 1, 32>(p, x, router_w, router_b, true, s);
+    else launch_shape<1, 1, 16>(p, x, router_w, router_b, true, s);
   } else {
     // many rows: 4x4 register tiles, 16-position slices (about 60 KiB of
     // LDS, so two workgroups share a CU)
-    launch_shape<4, 4, 16>(p, x, router_w, router_b, s);
+    launch_shape<4, 4, 16>(p, x, router_w, router_b, false, s);
   }
   return hipGetLastError();
 }
