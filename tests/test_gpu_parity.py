@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
+import sparse_moe_ffn_softmax_amd as cm
 import workloads as W
 from parity import assert_ffn_close, assert_routing_equal, check, run_gpu
 
@@ -220,6 +221,14 @@ def test_blocks16_bf16_sampled():
 def test_blocks64_fp8_sampled():
     inp = W.generate(W.WORKLOADS["blocks64_fp8"])
     check(inp, rows=W.row_sample(inp.wl.rows, 16, seed=4), threads=16)
+
+
+def test_blocks256_fp8_panels_sampled():
+    """The large-call shape at full size (8192 rows, 128-row tiles, several
+    tiles per expert) on panel weights, the layout the bench times."""
+    inp = W.generate(W.WORKLOADS["blocks256_fp8"])
+    check(inp, rows=W.row_sample(inp.wl.rows, 16, seed=10), threads=16,
+          dp=cm.upload(inp, layout="panels"))
 
 
 # ---------------------------------------------------------------------------
