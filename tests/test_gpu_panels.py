@@ -83,6 +83,11 @@ CASES = [
     MID.with_(name="p_mid_fp4", weight_dtype=W.FP4, seed=324),
     MID.with_(name="p_mid_Is_ne_I", inter=128, shared_inter=384, seed=325),
     MID.with_(name="p_mid_rows32_fp8", block_rows=32, num_blocks=3, weight_dtype=W.FP8, seed=326),
+    # expert budget and live rows, a skewed router at a low threshold and k 4,
+    # and a two-row verification call
+    MID.with_(name="p_mid_budget6_live50", live_fraction=0.5, expert_budget=6, seed=331),
+    FEW.with_(name="p_few_skewed_tau08_k4", bias_sigma=1.0, mass_threshold=0.8, top_k=4, seed=332),
+    FEW.with_(name="p_few_rows2", block_rows=2, num_blocks=3, seed=333),
 ]
 
 
@@ -98,7 +103,7 @@ def test_panels_give_the_row_major_result_bit_for_bit(wl):
     np.testing.assert_array_equal(bits(out_p), bits(out_r))
 
 
-@pytest.mark.parametrize("wl", [CASES[0], CASES[3], CASES[8], CASES[11]], ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", [CASES[0], CASES[3], CASES[8], CASES[11], CASES[16]], ids=lambda w: w.name)
 def test_panels_against_the_oracle(wl):
     inp = W.generate(wl)
     check(inp, dp=cm.upload(inp, layout="panels"))
