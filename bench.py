@@ -43,8 +43,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence (hip_runtime_api.h)
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "fp8_e4m3": 2500.0,  # fp8 and fp4 weights are
-                    "fp4_e2m1": 2500.0}                                    # widened to bf16 MFMA
+# dense MFMA datasheet peaks (TFLOP/s) by the operand type the matrix cores run
+MFMA_DATASHEET_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+# the MFMA operand type of each weight format: fp8 (W8A16) and 4-bit weights
+# are widened to bf16 in registers and run on the bf16 MFMA
+MFMA_KIND = {"bf16": "bf16", "fp8_e4m3": "bf16", "fp4_e2m1": "bf16", "f32": "f32"}
 
 
 def hip():
@@ -53,6 +56,7 @@ def hip():
     L.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
     L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
     L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     return L
 
 
@@ -115,6 +119,121 @@ def measured_traffic(kernel: str, workload: str, src: str, layout: str):
     return d.get("hbm_bytes_per_launch")
 
 
+def measure_peaks(H_, stream_ptr):
+    """Achievable HBM read bandwidth and bf16 / fp8 MFMA rates of this GPU,
+    from the probes of libclover_moe_peaks.so (a streaming read of 4 GiB with
+    the panel loads' pattern; waves issuing independent MFMAs back to back)."""
+    import torch
+    from sparse_moe_ffn_softmax_amd import _build
+    P = ctypes.CDLL(_build.PEAKS_LIB)
+    P.cmoe_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                 ctypes.c_void_p]
+    P.cmoe_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    P.cmoe_peak_mfma_flop.restype = ctypes.c_longlong
+    ev = []
+    for _ in range(2):
+        e = ctypes.c_void_p()
+        assert H_.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) == 0
+        ev.append(e.value)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            assert H_.hipEventRecord(ev[0], stream_ptr) == 0
+            fn()
+            assert H_.hipEventRecord(ev[1], stream_ptr) == 0
+            torch.cuda.synchronize()
+            f = ctypes.c_float()
+            assert H_.hipEventElapsedTime(ctypes.byref(f), ev[0], ev[1]) == 0
+            best = f.value if best is None else min(best, f.value)
+        return best * 1e-3
+
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    blocks_rd = 256 * 8
+    sink = torch.empty(blocks_rd, dtype=torch.int32, device="cuda")
+    t_rd = timed(lambda: P.cmoe_peak_read(buf.data_ptr(), nbytes, sink.data_ptr(), blocks_rd, stream_ptr), 5)
+    del buf
+    blocks, iters = 1024, 2000
+    out = torch.empty(blocks * 256 * 4, dtype=torch.float32, device="cuda")
+    res = {"hbm_read_gbps": round(nbytes / t_rd / 1e9, 1)}
+    for kind, name in ((0, "mfma_bf16_tflops"), (1, "mfma_fp8_tflops")):
+        t = timed(lambda: P.cmoe_peak_mfma(kind, out.data_ptr(), blocks, iters, stream_ptr), 3)
+        flop = P.cmoe_peak_mfma_flop(kind) * 8 * iters * blocks * 4
+        res[name] = round(flop / t / 1e12, 1)
+    for e in ev:
+        H_.hipEventDestroy(e)
+    res["probe"] = ("streaming read of 4 GiB (each wave load 1 KiB of consecutive lines, "
+                    "non-temporal); 1024 workgroups x 4 waves x 2000 rounds of 8 independent MFMAs "
+                    "(bf16 16x16x32; fp8 e4m3 16x16x128 with unit scales); best of repeated runs")
+    return res
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def percentiles(a):
+    import numpy as np
+    a = np.asarray(a, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 2), "p10": round(float(np.percentile(a, 10)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2), "mean": round(float(a.mean()), 2)}
+
+
+def cpu_baseline(inp, B, N, budget_s):
+    """The oracle timed on this host: all cores (OpenMP over rows), then one
+    thread on a bounded sample.  Full calls when they fit the budget;
+    otherwise the FFN of the first blocks' rows only (routing still covers
+    every row), scaled to block-passes/s by the blocks computed."""
+    import oracle
+    wl = inp.wl
+    R = wl.block_rows
+    nproc = len(os.sched_getaffinity(0))
+    threads = int(os.environ.get("OMP_NUM_THREADS") or min(16, nproc))
+
+    def leg(nthreads, budget):
+        t1 = time.perf_counter()
+        oracle.forward(inp, threads=nthreads, rows=np.arange(min(N, R)))
+        one_block = time.perf_counter() - t1
+        # blocks whose rows fit the budget (one-block time includes all routing)
+        nb = int(max(1, min(B, budget / max(one_block, 1e-4))))
+        rows = None if nb >= B else np.arange(nb * R)
+        reps = 1
+        if nb >= B:
+            t1 = time.perf_counter()
+            oracle.forward(inp, threads=nthreads)
+            one = time.perf_counter() - t1
+            reps = max(1, min(20, int(budget / max(one, 1e-3))))
+        t1 = time.perf_counter()
+        for _ in range(reps):
+            oracle.forward(inp, threads=nthreads, rows=rows)
+        el = time.perf_counter() - t1
+        blocks = nb if rows is not None else B
+        what = (f"{reps} full call(s) (routing and fp64 FFN for all {N} rows)" if rows is None else
+                f"one call with routing for all {N} rows and the fp64 FFN for the first {nb} of {B} "
+                f"blocks ({nb * R} rows)")
+        return reps * blocks / el, el, what
+
+    import numpy as np
+    v_all, el_all, what_all = leg(threads, budget_s * 0.6)
+    v_one, el_one, what_one = leg(1, budget_s * 0.4)
+    return {
+        "value": round(v_all, 4), "unit": "block-passes/s", "cores": threads, "kind": "oracle",
+        "sample": f"{wl.name}: {what_all}, {el_all:.1f} s wall, {threads} OpenMP threads over rows",
+        "single_thread": {"value": round(v_one, 4), "unit": "block-passes/s", "cores": 1,
+                          "sample": f"{what_one}, {el_one:.1f} s wall"},
+        "host": {"nproc": nproc, "os_cpu_count": os.cpu_count(), "cpu_model": cpu_model()},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +247,8 @@ def main():
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="rough budget of the oracle CPU-baseline leg (0 disables it)")
+    ap.add_argument("--no-peaks", dest="peaks", action="store_false",
+                    help="skip measuring the achievable HBM read and MFMA rates of the GPU")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="copy a device buffer of this many bytes once before the workload: "
                          "a plain copy kernel of known size for calibrating HBM byte counters")
@@ -204,6 +325,42 @@ def main():
     t_end = time.perf_counter()
     print(f"[bench] timed {args.steps} steps", file=sys.stderr, flush=True)
 
+    # per-call pass: the same steps again, one event between consecutive calls
+    call_ev = []
+    for _ in range(args.steps + 1):
+        e = ctypes.c_void_p()
+        assert H_.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) == 0
+        call_ev.append(e.value)
+    sp = stream.cuda_stream
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        i = args.warmup + s
+        assert H_.hipEventRecord(call_ev[s], sp) == 0
+        cm.clover_moe_block_forward(dp.problem, layers[i % len(layers)], x, tau, K, out,
+                                    routings[i], ws, stream=stream, options=opts)
+    assert H_.hipEventRecord(call_ev[args.steps], sp) == 0
+    torch.cuda.synchronize()
+    call_us = []
+    f = ctypes.c_float()
+    for s in range(args.steps):
+        assert H_.hipEventElapsedTime(ctypes.byref(f), call_ev[s], call_ev[s + 1]) == 0
+        call_us.append(f.value * 1e3)
+    for e in call_ev:
+        H_.hipEventDestroy(e)
+
+    # single-call latency: one call on an idle GPU, from the host's issue to
+    # its completion seen by the host (argument marshalling, launch, kernels)
+    lat_us = []
+    for s in range(min(args.steps, 20)):
+        i = args.warmup + s
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        cm.clover_moe_block_forward(dp.problem, layers[i % len(layers)], x, tau, K, out,
+                                    routings[i], ws, stream=stream, options=opts)
+        torch.cuda.synchronize()
+        lat_us.append((time.perf_counter() - t0) * 1e6)
+    print(f"[bench] per-call and latency passes done", file=sys.stderr, flush=True)
+
     # stage pass: the same steps again, with HIP events between the kernels
     torch.cuda.synchronize()
     for s in range(args.steps):
@@ -212,6 +369,10 @@ def main():
                                            routings[i], ws, events[s], stream=stream, options=opts)
     torch.cuda.synchronize()
     print(f"[bench] stage pass done", file=sys.stderr, flush=True)
+
+    peaks = measure_peaks(H_, sp) if args.peaks else None
+    if peaks:
+        print(f"[bench] peaks measured: {peaks['hbm_read_gbps']} GB/s read", file=sys.stderr, flush=True)
 
     ms_per_step = (t_end - t_start) * 1e3 / args.steps
     stage_ms = np.zeros((args.steps, cm.NUM_STAGES))
@@ -247,8 +408,13 @@ def main():
     # experts (+ shared), x once, h written once
     up_bytes = (touched * (2 * I * H * wsz + sc_up) + (2 * Is * H * wsz + sc_up_s) + N * H * asz
                 + (pairs * I + n_sh * Is) * hsz)
+    # the library's per-pair down outputs y: fp32, or bf16 when tiles are
+    # taller than 16 rows and the activations are bf16 (the workspace plan)
+    want = -(-(N * K * 3 // 2) // E)
+    tiled = want > 16
+    ysz = 2 if (tiled and wl.act_dtype == W.BF16) else 4
     dn_bytes = (touched * (H * I * wsz + sc_dn) + (H * Is * wsz + sc_dn_s) + (pairs * I + n_sh * Is) * hsz
-                + (pairs + n_sh) * H * 4)
+                + (pairs + n_sh) * H * ysz)
     # whole call (weights, router, x in, out)
     call_bytes = (touched * (3 * H * I * wsz + sc_up + sc_dn) + (3 * H * Is * wsz + sc_up_s + sc_dn_s)
                   + 4 * E * H + N * H * 2 * asz)
@@ -266,8 +432,6 @@ def main():
         achieved = float(dom_bytes.sum() / (stage_ms[:, dom].sum() * 1e-3) / 1e9)
         # the library's work-tile rule: 16-row tiles run the register-operand
         # kernels (expert_gemm.hip), taller tiles the LDS-tiled ones
-        want = -(-(N * K * 3 // 2) // E)
-        tiled = want > 16
         kname = f"expert_{'up' if dom == 2 else 'down'}{'_tiled' if tiled else ''}_kernel"
         traffic = measured_traffic(kname, wl.name, "expert_tiled.hip" if tiled else "expert_gemm.hip",
                                    args.layout)
@@ -279,8 +443,10 @@ def main():
         # past the ridge (MFMA peak / HBM peak flop per byte) the kernel's
         # roof is the matrix cores: report it against the MFMA peak instead
         dom_flops = up_flops if dom == 2 else dn_flops
-        mfma_peak = MFMA_PEAK_TFLOPS[{W.BF16: "bf16", W.F32: "f32", W.FP8: "fp8_e4m3",
-                                      W.FP4: "fp4_e2m1"}[wl.weight_dtype]]
+        mfma_peak = MFMA_DATASHEET_TFLOPS[MFMA_KIND[wl.weight_dtype]]
+        if peaks:
+            roofline["frac_of_measured_peak"] = round(achieved / peaks["hbm_read_gbps"], 4)
+            roofline["measured_peak"] = peaks["hbm_read_gbps"]
         if dom_flops.mean() / dom_bytes.mean() > mfma_peak * 1e12 / (HBM_PEAK_GBPS * 1e9):
             tflops = float(dom_flops.sum() / (stage_ms[:, dom].sum() * 1e-3) / 1e12)
             roofline.update({"bound": "mfma", "achieved": round(tflops, 2), "peak": mfma_peak,
@@ -292,6 +458,16 @@ def main():
                     "traffic": None, "kernel": dom_name}
 
     value = B / (ms_per_step * 1e-3)
+    rate = mfma_flops.mean() / (ms_per_step * 1e-3) / 1e12
+    mk = MFMA_KIND[wl.weight_dtype]
+    mfma_util = {f"vs_{mk}_datasheet": round(float(rate / MFMA_DATASHEET_TFLOPS[mk]), 5)}
+    if wl.weight_dtype == W.FP8:
+        mfma_util["vs_fp8_datasheet"] = round(float(rate / MFMA_DATASHEET_TFLOPS["fp8"]), 5)
+    if peaks and mk in ("bf16", "fp8"):
+        mfma_util[f"vs_{mk}_measured"] = round(float(rate / peaks[f"mfma_{mk}_tflops"]), 5)
+        if wl.weight_dtype == W.FP8:
+            mfma_util["vs_fp8_measured"] = round(float(rate / peaks["mfma_fp8_tflops"]), 5)
+    call_gbps = float(call_bytes.mean() / (ms_per_step * 1e-3) / 1e9)
     res = {
         "metric": "MoE block-passes/s + achieved HBM GB/s & MFMA util vs peak, 32-row block",
         "value": round(value, 2),
@@ -314,36 +490,25 @@ def main():
         "call": {
             "device_us_staged": round(float(device_ms.mean() * 1e3), 2),
             "algorithmic_bytes": int(call_bytes.mean()),
-            "hbm_gbps": round(float(call_bytes.mean() / (ms_per_step * 1e-3) / 1e9), 1),
-            "hbm_frac": round(float(call_bytes.mean() / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS), 4),
-            "mfma_tflops": round(float(mfma_flops.mean() / (ms_per_step * 1e-3) / 1e12), 3),
-            "mfma_util": round(float(mfma_flops.mean() / (ms_per_step * 1e-3) / 1e12
-                                     / MFMA_PEAK_TFLOPS[wl.weight_dtype]), 5),
+            "hbm_gbps": round(call_gbps, 1),
+            "hbm_frac": round(call_gbps / HBM_PEAK_GBPS, 4),
+            "hbm_frac_of_measured_peak": round(call_gbps / peaks["hbm_read_gbps"], 4) if peaks else None,
+            "mfma_tflops": round(float(rate), 3),
+            "mfma_datapath": mk,
+            "mfma_util": mfma_util,
+            "device_us_per_call": percentiles(call_us),
+            "single_call_latency_us": percentiles(lat_us),
             "router_gflop": round(router_flops / 1e9, 3),
             "experts_touched": float(touched.mean()),
             "routed_pairs": float(pairs.mean()),
         },
         "stages_us": {n: round(float(v * 1e3), 2) for n, v in zip(cm.STAGE_NAMES, mean_stage)},
+        "peaks_measured": peaks,
         "cpu_baseline": None,
     }
 
     if args.cpu_seconds > 0:
-        import oracle
-        threads = int(os.environ.get("OMP_NUM_THREADS") or min(16, len(os.sched_getaffinity(0))))
-        t1 = time.perf_counter()
-        oracle.forward(inp, threads=threads)
-        one = time.perf_counter() - t1
-        reps = max(1, min(20, int(args.cpu_seconds / max(one, 1e-3))))
-        t1 = time.perf_counter()
-        for _ in range(reps):
-            oracle.forward(inp, threads=threads)
-        el = time.perf_counter() - t1
-        res["cpu_baseline"] = {
-            "value": round(reps * B / el, 4), "unit": "block-passes/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{reps} full calls of the {wl.name} workload (routing and fp64 FFN for all "
-                      f"{N} rows), {el:.1f} s wall, OpenMP over rows, after one untimed call",
-        }
+        res["cpu_baseline"] = cpu_baseline(inp, B, N, args.cpu_seconds)
     print(json.dumps(res))
 
 

@@ -55,11 +55,15 @@
  *    completes.
  *  - Inputs are never written.  `out` and the workspace must not overlap any
  *    input.
- *  - Errors: every argument is checked before any work is queued and before
- *    any byte is written; an invalid call returns a nonzero status and leaves
- *    every buffer untouched.  clover_moe_last_error() then holds a
- *    thread-local description.  Faults inside kernels surface at the caller's
- *    next synchronisation.
+ *  - Errors (InfiniLM PR #604, "Notes for Reviewers": options the
+ *    implementation does not support are refused explicitly, and a
+ *    conversion that would be wrong is refused before anything is written):
+ *    every argument is checked before any work is queued and before any byte
+ *    is written; an invalid call returns a nonzero status and leaves every
+ *    buffer untouched.  There is no silent fallback to another dtype, shape
+ *    or path.  clover_moe_last_error() then holds a thread-local
+ *    description.  Faults inside kernels surface at the caller's next
+ *    synchronisation.
  *  - Non-finite inputs are not checked; their results are undefined.
  *  - Thread safety: calls are independent; the library has no global
  *    mutable state apart from the thread-local error text.
@@ -190,7 +194,19 @@ typedef struct {
 } cmoe_options;
 
 /* Bytes of device workspace clover_moe_block_forward needs for this problem
- * and top_k.  Host-only; queues no work.  Writes *bytes on success. */
+ * and top_k (InfiniLM PR #604, "Checklist": mask, state and workspace bounds
+ * and their lifetime are part of the checked contract).  Host-only; queues no
+ * work.  Writes *bytes on success.
+ *
+ *  problem: host pointer; validated exactly as clover_moe_block_forward does
+ *  top_k:   1..min(8, E)
+ *  bytes:   host pointer, written on success only
+ * Lifetime: the workspace is caller-owned device memory; a call may use it
+ * until the work queued on its stream completes, and keeps nothing in it
+ * between calls (its contents on entry do not matter).  Two calls whose
+ * work may overlap in time need two workspaces.
+ * Errors: CMOE_ERR_NULL (problem or bytes is NULL), and the CMOE_ERR_VALUE /
+ * CMOE_ERR_UNSUPPORTED codes of the problem checks. */
 cmoe_status clover_moe_workspace_size(const cmoe_problem* problem, int32_t top_k, size_t* bytes);
 
 /* One MoE layer over B blocks (steps 1-6 above), queued on `stream`.
@@ -267,10 +283,18 @@ cmoe_status clover_moe_block_forward_staged(const cmoe_problem* problem, const c
 cmoe_status clover_moe_pack_weights(const void* src, void* dst, int64_t count, int32_t rows,
                                     int32_t row_bytes, int32_t gate_up, void* stream);
 
-/* Static text of a status code. */
+/* Error reporting (InfiniLM PR #604, "Notes for Reviewers": unsupported
+ * options are refused explicitly, so a caller must be able to tell why).
+ *
+ * clover_moe_status_string: static text of a status code (any value; unknown
+ * codes give "unknown status").  The pointer is to static storage: never
+ * freed, valid for the life of the process, safe from any thread.
+ *
+ * clover_moe_last_error: text describing the last non-OK status returned on
+ * the calling thread (which argument, which value, which limit).  The
+ * pointer is owned by the library and stays valid until the next call into
+ * the library on the same thread; successful calls leave it unchanged. */
 const char* clover_moe_status_string(cmoe_status status);
-
-/* Thread-local text describing the last non-OK status returned on this thread. */
 const char* clover_moe_last_error(void);
 
 #ifdef __cplusplus

@@ -1,4 +1,6 @@
-"""Build of the HIP library libclover_moe.so for gfx950 (hipcc, in-tree).
+"""Build of the HIP library libclover_moe.so for gfx950 (hipcc, in-tree), and
+of libclover_moe_peaks.so, the benchmark's achievable-peak probes (not part of
+the library's C ABI).
 
 Every HIP source is compiled with fp contraction off (the routing steps rely
 on the exact operation sequence written in the source) and with packed fp32
@@ -18,6 +20,8 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libclover_moe.so")
 SOURCES = ["api.cpp", "router.hip", "route_block.hip", "permute_blocks.hip", "expert_gemm.hip",
            "expert_tiled.hip", "combine.hip", "pack.hip"]
+PEAKS_LIB = os.path.join(PKG, "libclover_moe_peaks.so")
+PEAKS_SOURCES = ["peaks.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -39,17 +43,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build() -> str:
-    """Compile every source and link libclover_moe.so; returns its path."""
-    os.makedirs(OBJ, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build() -> str:
+    """Compile every source, link libclover_moe.so and libclover_moe_peaks.so;
+    returns the path of the former."""
+    os.makedirs(OBJ, exist_ok=True)
+    srcs = SOURCES + PEAKS_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PEAKS_LIB)
     return LIB
 
 

@@ -79,7 +79,8 @@ cmoe_status check_problem(const cmoe_problem* p, int32_t top_k) {
                        (p->act_dtype == CMOE_BF16 && p->weight_dtype == CMOE_FP4_E2M1);
   if (!ok_pair)
     return fail(CMOE_ERR_UNSUPPORTED,
-                "dtype pair (act=%d, weight=%d) unsupported: use (F32,F32), (BF16,BF16) or (BF16,FP8_E4M3)",
+                "dtype pair (act=%d, weight=%d) unsupported: use (F32,F32), (BF16,BF16), (BF16,FP8_E4M3) "
+                "or (BF16,FP4_E2M1)",
                 p->act_dtype, p->weight_dtype);
   if (top_k < 1 || top_k > p->num_experts)
     return fail(CMOE_ERR_VALUE, "top_k=%d must be in [1, num_experts=%d]", top_k, p->num_experts);

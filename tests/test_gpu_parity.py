@@ -207,28 +207,62 @@ def skewed():
     return W.generate(W.WORKLOADS["block32_skewed"])
 
 
+def _report(name, mx, mean, ref):
+    print(f"[parity] {name}: all {ref['out'].size} outputs max|d|/max|ref|={mx:.3e} "
+          f"sum|d|/sum|ref|={mean:.3e} coreset sizes {sorted(set(ref['coreset_size'].tolist()))[:6]}...")
+
+
 @pytest.mark.parametrize("tau,k", W.SKEWED_SWEEP)
-def test_block32_skewed_sweep(skewed, tau, k):
-    rows = W.row_sample(32, 8, seed=2)
-    check(skewed, tau=tau, top_k=k, rows=rows, threads=16)
+def test_block32_skewed_sweep_full(skewed, tau, k):
+    mx, mean, ref = check(skewed, tau=tau, top_k=k, threads=16)
+    _report(f"block32_skewed tau={tau} k={k}", mx, mean, ref)
 
 
-def test_blocks16_bf16_sampled():
+@pytest.mark.parametrize("tau,k", W.SKEWED_SWEEP)
+def test_block32_skewed_strong_full(tau, k):
+    """Bias sigma 2.5: coresets of roughly 20-110 experts (the low end of the
+    threshold sweep)."""
+    inp = W.generate(W.WORKLOADS["block32_skewed_strong"])
+    mx, mean, ref = check(inp, tau=tau, top_k=k, threads=16)
+    _report(f"block32_skewed_strong tau={tau} k={k}", mx, mean, ref)
+
+
+def test_blocks16_bf16_full():
     inp = W.generate(W.WORKLOADS["blocks16_bf16"])
-    check(inp, rows=W.row_sample(inp.wl.rows, 24, seed=3), threads=16)
+    mx, mean, ref = check(inp, threads=16)
+    _report("blocks16_bf16", mx, mean, ref)
 
 
-def test_blocks64_fp8_sampled():
+def test_blocks64_fp8_full():
     inp = W.generate(W.WORKLOADS["blocks64_fp8"])
-    check(inp, rows=W.row_sample(inp.wl.rows, 16, seed=4), threads=16)
+    mx, mean, ref = check(inp, threads=16)
+    _report("blocks64_fp8", mx, mean, ref)
 
 
-def test_blocks256_fp8_panels_sampled():
+def test_blocks64_fp8_panels_full():
+    """The 64-block call on panel weights, the layout the benchmark times."""
+    inp = W.generate(W.WORKLOADS["blocks64_fp8"])
+    mx, mean, ref = check(inp, threads=16, dp=cm.upload(inp, layout="panels"))
+    _report("blocks64_fp8 (panels)", mx, mean, ref)
+
+
+@pytest.mark.parametrize("wt", [W.BF16, W.FP8, W.FP4])
+def test_tall_tiles_at_model_width_full(wt):
+    """8 blocks of 32 rows over 32 experts at H 2048, I 512: about 64 rows per
+    expert, so the many-row kernels run tall tiles (up to 96 rows) with the
+    hidden and intermediate sizes of the model (16 and 4 k stages)."""
+    wl = W.Workload(f"tall_{wt}", 8, 32, 2048, 32, 8, 512, 512, W.BF16, wt, 0.9, seed=111)
+    mx, mean, ref = check(W.generate(wl), threads=16)
+    assert ref["expert_counts"].max() > 64
+    _report(wl.name, mx, mean, ref)
+
+
+def test_blocks256_fp8_panels_full():
     """The large-call shape at full size (8192 rows, 128-row tiles, several
     tiles per expert) on panel weights, the layout the bench times."""
     inp = W.generate(W.WORKLOADS["blocks256_fp8"])
-    check(inp, rows=W.row_sample(inp.wl.rows, 16, seed=10), threads=16,
-          dp=cm.upload(inp, layout="panels"))
+    mx, mean, ref = check(inp, threads=16, dp=cm.upload(inp, layout="panels"))
+    _report("blocks256_fp8 (panels)", mx, mean, ref)
 
 
 # ---------------------------------------------------------------------------

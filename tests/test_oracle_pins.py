@@ -219,6 +219,61 @@ def test_block_mass_is_column_sum_of_probabilities():
         assert abs(math.fsum(mass[b]) - R) < 1e-13
 
 
+def _order_case_logits(g, names, E):
+    vals = {"0": 0.0, "zero": g["zero_logit"], "tiny": g["tiny_logit"]}
+    return np.array([vals[n] for n in names], np.float32).reshape(1, E)
+
+
+def test_softmax_normaliser_order_hand_derived():
+    """Z of one row under the contract's chunk-and-tree order, against a hand
+    derivation in which every other plausible order gives another value."""
+    g = json.load(open(os.path.join(GOLDEN, "z_mass_order.json")))
+    zc = g["z_case"]
+    E = zc["num_experts"]
+    wl = small(num_experts=E, block_rows=1, top_k=1)
+    inp = W.MoEInputs(wl, None, None, None, None, None, None, None, None, None, None, None)
+    l = _order_case_logits(g, zc["logits"], E)
+    u, p = oracle.softmax(inp, l)
+    ulp = 2.0 ** -52
+    tiny = [e for e, n in enumerate(zc["logits"]) if n == "tiny"]
+    # preconditions of the derivation (t in (0.5u, 0.75u); exact 0 and 1)
+    assert all(0.5 * ulp < u[0, e] < 0.75 * ulp for e in tiny)
+    assert u[0, 0] == 1.0 and all(u[0, e] == 0.0 for e, n in enumerate(zc["logits"]) if n == "zero")
+    z = float.fromhex(zc["expected_Z"])
+    assert p[0, 0] == 1.0 / z
+    for other in zc["other_orders_Z"].values():
+        assert p[0, 0] != 1.0 / float.fromhex(other)
+
+
+def test_block_mass_row_order_hand_derived():
+    """mass[b, e] sums rows in ascending order: a hand-derived block where the
+    descending and the pairwise orders give other values."""
+    g = json.load(open(os.path.join(GOLDEN, "z_mass_order.json")))
+    mc = g["mass_case"]
+    R, E = mc["block_rows"], mc["num_experts"]
+    wl = small(num_experts=E, block_rows=R, top_k=1)
+    inp = W.MoEInputs(wl, None, None, None, None, None, None, None, None, None, None, None)
+    names = []
+    for r in range(R):
+        row = ["zero"] * E
+        if r == 0:
+            row[0] = "0"
+        elif r <= 3:
+            row[1], row[0] = "0", "tiny"
+        else:
+            row[2] = "0"
+        names.append(row)
+    l = np.concatenate([_order_case_logits(g, row, E) for row in names])
+    u, p = oracle.softmax(inp, l)
+    ulp = 2.0 ** -52
+    assert p[0, 0] == 1.0 and np.all(p[4:, 0] == 0.0)
+    assert all(0.5 * ulp < p[r, 0] < 0.75 * ulp for r in (1, 2, 3))
+    mass = oracle.block_mass(inp, p)
+    assert mass[0, 0] == float.fromhex(mc["expected_mass_expert0"])
+    for other in mc["other_orders_mass_expert0"].values():
+        assert mass[0, 0] != float.fromhex(other)
+
+
 def _coreset_invariants(mass, tau, ids, m):
     E = mass.shape[0]
     order = sorted(range(E), key=lambda e: (-mass[e], e))

@@ -79,6 +79,10 @@ WORKLOADS: Dict[str, Workload] = {
     # same shapes with a per-expert router bias ~N(0,1): coreset sizes vary widely
     "block32_skewed": Workload("block32_skewed", 1, 32, 2048, 256, 8, 512, 512, BF16, BF16, 0.9,
                                seed=2, bias_sigma=1.0),
+    # supplementary: a stronger bias (sigma 2.5) reaches the low end of the
+    # coreset-size range (tens of experts) that sigma 1 does not
+    "block32_skewed_strong": Workload("block32_skewed_strong", 1, 32, 2048, 256, 8, 512, 512, BF16, BF16,
+                                      0.9, seed=12, bias_sigma=2.5),
     # 16 independent 32-row blocks per call, bf16
     "blocks16_bf16": Workload("blocks16_bf16", 16, 32, 2048, 256, 8, 512, 512, BF16, BF16, 0.9, seed=3),
     # 64 blocks x 32 rows, fp8 e4m3 expert weights with fp32 128x128 block scales
@@ -265,13 +269,3 @@ def generate(wl: Workload) -> MoEInputs:
 def with_arrays(inp: MoEInputs, **kw) -> MoEInputs:
     """Copy of ``inp`` with some arrays replaced (used to build special cases)."""
     return dataclasses.replace(inp, **kw)
-
-
-def row_sample(num_rows: int, count: int, seed: int) -> np.ndarray:
-    """Sorted sample of row indices used for sampled full-size parity checks.
-    Always includes the first and last row."""
-    rng = np.random.default_rng(seed + 7919)
-    count = min(count, num_rows)
-    picks = set(rng.choice(num_rows, size=count, replace=False).tolist())
-    picks.update({0, num_rows - 1})
-    return np.array(sorted(picks), dtype=np.int64)
