@@ -49,7 +49,8 @@
  *    contiguous (expert weights may instead be MFMA panels, see
  *    cmoe_layout).  Device pointers must be 16-byte aligned.
  *  - Ownership: the caller allocates and frees everything, including the
- *    workspace.  The library allocates no memory, keeps no pointer after the
+ *    workspace (clover_moe_block_forward_noalloc uses a static array of the
+ *    library instead).  The library allocates no memory, keeps no pointer after the
  *    call returns, never synchronises the host and never changes the current
  *    device.  Buffers must stay valid until the work queued on `stream`
  *    completes.
@@ -66,7 +67,9 @@
  *    synchronisation.
  *  - Non-finite inputs are not checked; their results are undefined.
  *  - Thread safety: calls are independent; the library has no global
- *    mutable state apart from the thread-local error text.
+ *    mutable state apart from the thread-local error text and the per-GPU
+ *    scratch array of clover_moe_block_forward_noalloc (calls of that entry
+ *    point must not overlap on one GPU).
  *  - A call queues kernels on `stream` and nothing else (no memset, no
  *    allocation, no host synchronisation), so it can be captured in a HIP
  *    graph; replays reproduce the eager results bit for bit.
@@ -234,6 +237,34 @@ cmoe_status clover_moe_block_forward_ex(const cmoe_problem* problem, const cmoe_
                                         const cmoe_options* options, void* out,
                                         const cmoe_routing* routing, void* workspace,
                                         size_t workspace_bytes, void* stream);
+
+/* Largest workspace of clover_moe_block_forward_noalloc, in bytes (128 MiB:
+ * enough for 64 blocks of 32 rows at H 2048, 256 experts, top-8, I 512). */
+#define CLOVER_MOE_NOALLOC_MAX_WORKSPACE (128u * 1024u * 1024u)
+
+/* clover_moe_block_forward_ex without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops
+ * that must not call hipMalloc, harnesses that forbid allocation).
+ *
+ * The workspace is a static device array of CLOVER_MOE_NOALLOC_MAX_WORKSPACE
+ * bytes inside the library, one per GPU, held from the first use on that GPU
+ * until the process ends.  The call allocates nothing (no hipMalloc, no
+ * hipFree, no allocating library routine); the first call on a device looks up
+ * that device's array address once.
+ *
+ * Arguments and results are those of clover_moe_block_forward_ex; `stream`
+ * must belong to the current device (NULL = its default stream).  Every call
+ * on one GPU shares that GPU's array, which keeps the last call's contents
+ * (no call depends on them): calls whose work may overlap on one GPU (other
+ * streams, other threads) race and give undefined results; serialise them.
+ * Errors: those of clover_moe_block_forward_ex; CMOE_ERR_WORKSPACE when the
+ * problem needs more than CLOVER_MOE_NOALLOC_MAX_WORKSPACE bytes (see
+ * clover_moe_workspace_size); CMOE_ERR_VALUE when the stream belongs to
+ * another device; CMOE_ERR_HIP when the array's address cannot be taken. */
+cmoe_status clover_moe_block_forward_noalloc(const cmoe_problem* problem, const cmoe_weights* weights,
+                                             const void* x, float mass_threshold, int32_t top_k,
+                                             const cmoe_options* options, void* out,
+                                             const cmoe_routing* routing, void* stream);
 
 /* Number of kernel stages clover_moe_block_forward queues, in order:
  * 0 router logits, 1 per-block routing (softmax, mass, coreset, top-k, gates;

@@ -24,8 +24,9 @@ CMOE_LAYOUT_ROWS, CMOE_LAYOUT_PANELS = 0, 1
 LAYOUT_CODES = {"rows": CMOE_LAYOUT_ROWS, "panels": CMOE_LAYOUT_PANELS}
 
 EXPORTED = ("clover_moe_workspace_size", "clover_moe_block_forward", "clover_moe_block_forward_ex",
-            "clover_moe_block_forward_staged", "clover_moe_pack_weights", "clover_moe_status_string",
-            "clover_moe_last_error")
+            "clover_moe_block_forward_staged", "clover_moe_block_forward_noalloc", "clover_moe_pack_weights",
+            "clover_moe_status_string", "clover_moe_last_error")
+NOALLOC_MAX_WORKSPACE = 128 * 1024 * 1024  # CLOVER_MOE_NOALLOC_MAX_WORKSPACE
 NUM_STAGES = 5
 STAGE_NAMES = ("router", "route_blocks", "expert_up", "expert_down", "combine")
 
@@ -85,6 +86,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.clover_moe_block_forward_ex.argtypes = ex_args
     L.clover_moe_block_forward_staged.restype = ctypes.c_int
     L.clover_moe_block_forward_staged.argtypes = ex_args + [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]
+    L.clover_moe_block_forward_noalloc.restype = ctypes.c_int
+    L.clover_moe_block_forward_noalloc.argtypes = [
+        ctypes.POINTER(cmoe_problem), ctypes.POINTER(cmoe_weights), ctypes.c_void_p, ctypes.c_float,
+        ctypes.c_int32, ctypes.POINTER(cmoe_options), ctypes.c_void_p, ctypes.POINTER(cmoe_routing),
+        ctypes.c_void_p]
     L.clover_moe_pack_weights.restype = ctypes.c_int
     L.clover_moe_pack_weights.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
@@ -147,6 +153,25 @@ def clover_moe_block_forward(problem: cmoe_problem, weights: cmoe_weights, x, ma
         _check(load_library().clover_moe_block_forward_ex(
             ctypes.byref(problem), ctypes.byref(weights), _ptr(x), ctypes.c_float(mass_threshold),
             top_k, ctypes.byref(options), _ptr(out), rt, _ptr(workspace), workspace_bytes, stream))
+
+
+def clover_moe_block_forward_noalloc(problem: cmoe_problem, weights: cmoe_weights, x,
+                                     mass_threshold: float, top_k: int, out,
+                                     routing: Optional[cmoe_routing] = None, stream=None,
+                                     options: Optional[cmoe_options] = None) -> None:
+    """Queue one call without a workspace argument: the library's static
+    per-GPU scratch array serves as the workspace (calls must not overlap on
+    one GPU)."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    rt = ctypes.byref(routing) if routing is not None else None
+    opt = ctypes.byref(options) if options is not None else None
+    _check(load_library().clover_moe_block_forward_noalloc(
+        ctypes.byref(problem), ctypes.byref(weights), _ptr(x), ctypes.c_float(mass_threshold),
+        top_k, opt, _ptr(out), rt, stream))
 
 
 def clover_moe_pack_weights(src, dst, count: int, rows: int, row_bytes: int, gate_up: int,

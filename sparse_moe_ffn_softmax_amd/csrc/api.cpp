@@ -12,6 +12,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -31,6 +32,30 @@ cmoe_status fail(cmoe_status s, const char* fmt, ...) {
   va_end(ap);
   g_last_error = buf;
   return s;
+}
+
+// The workspace of clover_moe_block_forward_noalloc: one static array per
+// GPU the library runs on, held until the process ends.  Host code never
+// passes `scratch` itself to a kernel (in host code the name is a host-side
+// stand-in, not a device address): each device's address comes from
+// hipGetSymbolAddress, taken once with that device current.
+static __device__ __align__(256) uint8_t scratch[CLOVER_MOE_NOALLOC_MAX_WORKSPACE];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of the current device's scratch array, looked up on the
+// first use on that device.
+hipError_t scratch_address(int dev, void** ptr) {
+  ScratchSlot& s = g_scratch[dev];
+  std::call_once(s.once, [&] { s.err = hipGetSymbolAddress(&s.ptr, HIP_SYMBOL(scratch)); });
+  *ptr = s.ptr;
+  return s.err;
 }
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -361,6 +386,39 @@ cmoe_status clover_moe_block_forward_staged(const cmoe_problem* problem, const c
   if (!stage_events) return fail(CMOE_ERR_NULL, "stage_events is NULL");
   return forward_impl(problem, w, x, mass_threshold, top_k, options, out, routing, workspace,
                       workspace_bytes, stream, stage_events, n_events);
+}
+
+cmoe_status clover_moe_block_forward_noalloc(const cmoe_problem* problem, const cmoe_weights* w,
+                                             const void* x, float mass_threshold, int32_t top_k,
+                                             const cmoe_options* options, void* out,
+                                             const cmoe_routing* routing, void* stream) {
+  const cmoe_status s = check_problem(problem, top_k);
+  if (s != CMOE_OK) return s;
+  const size_t need = cmoe::workspace_bytes(*problem, top_k);
+  if (need > CLOVER_MOE_NOALLOC_MAX_WORKSPACE)
+    return fail(CMOE_ERR_WORKSPACE,
+                "this problem needs %zu bytes of workspace; the no-allocation entry point has %zu "
+                "(use clover_moe_block_forward_ex with a caller workspace)",
+                need, (size_t)CLOVER_MOE_NOALLOC_MAX_WORKSPACE);
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(CMOE_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(CMOE_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  if (stream) {
+    int sdev = -1;
+    e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+    if (e != hipSuccess) return fail(CMOE_ERR_HIP, "hipStreamGetDevice failed: %s", hipGetErrorString(e));
+    if (sdev != dev)
+      return fail(CMOE_ERR_VALUE, "stream belongs to device %d, the current device is %d", sdev, dev);
+  }
+  void* ws = nullptr;
+  e = scratch_address(dev, &ws);
+  if (e != hipSuccess || !ws)
+    return fail(CMOE_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                hipGetErrorString(e));
+  return forward_impl(problem, w, x, mass_threshold, top_k, options, out, routing, ws,
+                      CLOVER_MOE_NOALLOC_MAX_WORKSPACE, stream, nullptr, 0);
 }
 
 cmoe_status clover_moe_pack_weights(const void* src, void* dst, int64_t count, int32_t rows,
