@@ -126,7 +126,7 @@ def measure_peaks(H_, stream_ptr):
     import torch
     from sparse_moe_ffn_softmax_amd import _build
     P = ctypes.CDLL(_build.PEAKS_LIB)
-    P.cmoe_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+    P.cmoe_peak_read.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
                                  ctypes.c_void_p]
     P.cmoe_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     P.cmoe_peak_mfma_flop.restype = ctypes.c_longlong
@@ -152,22 +152,29 @@ def measure_peaks(H_, stream_ptr):
 
     nbytes = 4 << 30
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
-    blocks_rd = 256 * 8
-    sink = torch.empty(blocks_rd, dtype=torch.int32, device="cuda")
-    t_rd = timed(lambda: P.cmoe_peak_read(buf.data_ptr(), nbytes, sink.data_ptr(), blocks_rd, stream_ptr), 5)
+    reads = {}
+    for pattern, blocks_rd in ((0, 2048), (1, 2048), (1, 4096)):
+        sink = torch.empty(blocks_rd, dtype=torch.int32, device="cuda")
+        t_rd = timed(lambda: P.cmoe_peak_read(pattern, buf.data_ptr(), nbytes, sink.data_ptr(), blocks_rd,
+                                              stream_ptr), 5)
+        reads[f"pattern{pattern}_wg{blocks_rd}"] = round(nbytes / t_rd / 1e9, 1)
     del buf
     blocks, iters = 1024, 2000
     out = torch.empty(blocks * 256 * 4, dtype=torch.float32, device="cuda")
-    res = {"hbm_read_gbps": round(nbytes / t_rd / 1e9, 1)}
-    for kind, name in ((0, "mfma_bf16_tflops"), (1, "mfma_fp8_tflops")):
+    res = {"hbm_read_gbps": max(reads.values()), "hbm_read_by_pattern": reads}
+    for kind, name in ((0, "mfma_bf16_16x16x32_tflops"), (2, "mfma_bf16_32x32x16_tflops"),
+                       (1, "mfma_fp8_16x16x128_tflops"), (3, "mfma_fp8_32x32x64_tflops")):
         t = timed(lambda: P.cmoe_peak_mfma(kind, out.data_ptr(), blocks, iters, stream_ptr), 3)
-        flop = P.cmoe_peak_mfma_flop(kind) * 8 * iters * blocks * 4
+        flop = P.cmoe_peak_mfma_flop(kind) * iters * blocks * 4
         res[name] = round(flop / t / 1e12, 1)
+    res["mfma_bf16_tflops"] = max(res["mfma_bf16_16x16x32_tflops"], res["mfma_bf16_32x32x16_tflops"])
+    res["mfma_fp8_tflops"] = max(res["mfma_fp8_16x16x128_tflops"], res["mfma_fp8_32x32x64_tflops"])
     for e in ev:
         H_.hipEventDestroy(e)
-    res["probe"] = ("streaming read of 4 GiB (each wave load 1 KiB of consecutive lines, "
-                    "non-temporal); 1024 workgroups x 4 waves x 2000 rounds of 8 independent MFMAs "
-                    "(bf16 16x16x32; fp8 e4m3 16x16x128 with unit scales); best of repeated runs")
+    res["probe"] = ("streaming read of 4 GiB (each wave load 1 KiB of consecutive lines, non-temporal; "
+                    "grid-strided or one slab per workgroup; the best); 1024 workgroups x 4 waves x 2000 "
+                    "rounds of MFMAs on independent chains (16x16 and 32x32 bf16 and fp8 e4m3 with unit "
+                    "scales); best of repeated runs")
     return res
 
 

@@ -342,13 +342,15 @@ static cmoe_status forward_impl(const cmoe_problem* problem, const cmoe_weights*
         if (e == hipSuccess && plan.B > 1) e = cmoe::launch_permute_blocks(plan, st);
         break;
       case 2:
-        e = plan.mt_max == 1 ? cmoe::launch_expert_up(plan, *w, x, st)
-                             : cmoe::launch_expert_tiled(plan, *w, x, true, st);
+        e = plan.mt_max == 1                       ? cmoe::launch_expert_up(plan, *w, x, st)
+            : cmoe::expert_many_fits(plan, true) ? cmoe::launch_expert_many(plan, *w, x, true, st)
+                                                   : cmoe::launch_expert_tiled(plan, *w, x, true, st);
         break;
       case 3:
-        e = fused ? cmoe::launch_expert_down_combine(plan, *w, out, st)
-            : plan.mt_max == 1 ? cmoe::launch_expert_down(plan, *w, st)
-                               : cmoe::launch_expert_tiled(plan, *w, x, false, st);
+        e = fused                                   ? cmoe::launch_expert_down_combine(plan, *w, out, st)
+            : plan.mt_max == 1                      ? cmoe::launch_expert_down(plan, *w, st)
+            : cmoe::expert_many_fits(plan, false) ? cmoe::launch_expert_many(plan, *w, x, false, st)
+                                                    : cmoe::launch_expert_tiled(plan, *w, x, false, st);
         break;
       case 4:
         if (!fused) e = cmoe::launch_combine(plan, out, st);

@@ -104,6 +104,10 @@ hipError_t launch_expert_down_combine(const Plan& p, const cmoe_weights& w, void
 // mt_max > 1: LDS-staged activation tiles (expert_tiled.hip); up = gate/up + SwiGLU, else down
 hipError_t launch_expert_tiled(const Plan& p, const cmoe_weights& w, const void* x, bool up,
                                hipStream_t s);
+// mt_max > 1 on 16-bit activations with I = 512 (and Is = 0 or I): persistent
+// kernels on the 32x32 MFMA (expert_many.hip); up = gate/up + SwiGLU, else down
+bool expert_many_fits(const Plan& p, bool up);
+hipError_t launch_expert_many(const Plan& p, const cmoe_weights& w, const void* x, bool up, hipStream_t s);
 hipError_t launch_combine(const Plan& p, void* out, hipStream_t s);
 // count row-major matrices of rows x row_bytes bytes -> MFMA panels (clover_moe.h)
 hipError_t launch_pack_panels(const void* src, void* dst, int64_t count, int rows, int row_bytes, int gate_up,

@@ -90,10 +90,11 @@ struct Frag<WFmt::FP8> {
     return u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
                  __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
   }
-  static __device__ __forceinline__ f32x4 mma(A a, B b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, widen(b)), c, 0, 0,
-                                                   0);
+  static __device__ __forceinline__ f32x4 mma(A a, B b, f32x4 c) { return mma_wide(a, widen(b), c); }
+  // the MFMA on weights already widened by widen()
+  static __device__ __forceinline__ f32x4 mma_wide(A a, u32x4 wb, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, wb),
+                                                   c, 0, 0, 0);
   }
 };
 

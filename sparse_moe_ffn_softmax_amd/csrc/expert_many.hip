@@ -1,0 +1,349 @@
+// expert_many.hip -- grouped expert GEMMs for calls that route many rows to
+// each expert (many blocks per call), on the 32x32x16 bf16 MFMA.
+//
+//   expert_down_many : y = h W2_e^T, a tile's whole h resident in LDS
+//
+// SwiGLU experts and one shared expert (Clover-35B-A3B-Preview CMF model card,
+// introduction); fp8 weights are E4M3 with one fp32 scale per 128x128 block
+// and bf16 activations (InfiniLM PR #584, "Benchmark"); 4-bit weights are
+// MXFP4 (E2M1 codes, E8M0 scale per 32 elements of a row), widened to bf16
+// exactly with their scale.  Fragment layouts: expert_frag32.h.
+//
+// The grids are persistent: one workgroup of kManyWaves waves per CU, each
+// owning a contiguous run of units (a work tile and a group of output
+// columns), tiles in the work list's order.  Every unit moves the same weight
+// bytes, so equal runs of units balance the HBM traffic across the CUs.  The
+// weights stream through a ring of register stages that runs on across unit
+// boundaries: while a stage's MFMAs run, the following stages (of this unit
+// or the next) are in flight.  Each tile's 32-row MFMA tile count is
+// dispatched at run time (rows / 32 rounded up).
+#include "cmoe_device.h"
+#include "cmoe_launch.h"
+#include "expert_frag32.h"
+
+namespace cmoe {
+
+struct ManyArgs {
+  const void* x;     // activations [N,H] (gate/up)
+  const void* w;     // W13 [E,2I,H] (gate/up) or W2 [E,H,I] (down)
+  const void* ws;    // scales of w (fp8: fp32 per 128x128 block; fp4: E8M0 per 32 of a row)
+  const void* sw;    // the shared expert's matrix
+  const void* sws;   // its scales
+  const Tile* tiles;
+  const int32_t* tile_count;
+  const int32_t* pair_row;
+  void* h;           // [N*K*I + N*Is] bf16
+  void* y;           // [N*K + N, H], bf16 (y_act) or fp32
+  int y_act;
+  int N, H, E, I, Is, K;
+};
+
+constexpr int kManyWaves = 8;
+constexpr int kManyThreads = 64 * kManyWaves;
+
+// ---------------------------------------------------------------------------
+// Down GEMM.  A tile's h (at most 128 rows of I = 512 bf16, 136 KiB with the
+// row padding) is staged into LDS once per tile by direct global-to-LDS loads
+// (a quarter-wave load fills one 256-byte stage row) and stays there for all
+// of the tile's units.  A unit is the tile times 256 output columns, 32 per
+// wave, over the four 128-deep stages of I; the ring holds the four stages of
+// one unit, each refilled with the next unit's same stage as soon as its
+// MFMAs have issued.
+// ---------------------------------------------------------------------------
+// The work tiles a workgroup's run of units touches, copied to LDS once: a
+// tile record read from global memory inside the unit loop is a vector load,
+// and the wait for it (vector loads complete in order) would also wait for
+// every weight load in flight.
+constexpr int kManySlots = 64;
+struct TileCache {
+  Tile t[kManySlots];
+  int lo, n;
+};
+__device__ __forceinline__ void cache_tiles(TileCache& c, const Tile* tiles, int slot_lo, int slot_hi) {
+  const int n = slot_hi - slot_lo + 1;  // <= kManySlots (the grid's size)
+  if ((int)threadIdx.x < n) c.t[threadIdx.x] = tiles[slot_lo + threadIdx.x];
+  if (threadIdx.x == 0) {
+    c.lo = slot_lo;
+    c.n = n;
+  }
+  __syncthreads();
+}
+// the tile of a slot in the run (the host sizes the grid so that no run spans
+// more than kManySlots tiles).  The fields are made wave-uniform (scalar
+// registers), so that branches on them are scalar branches: seen as
+// divergent, every arm's registers would stay live at once.
+__device__ __forceinline__ Tile cached_tile(const TileCache& c, int slot) {
+  const Tile v = c.t[slot - c.lo];
+  Tile t;
+  t.expert = __builtin_amdgcn_readfirstlane(v.expert);
+  t.start = __builtin_amdgcn_readfirstlane(v.start);
+  t.rows = __builtin_amdgcn_readfirstlane(v.rows);
+  t.pad = 0;
+  return t;
+}
+
+constexpr int kDownManyCols = 32 * kManyWaves;  // y columns per unit
+constexpr int kDownManyStages = 4;              // I = 512
+
+template <WFmt F, int MTM, bool PK>
+__global__ __launch_bounds__(kManyThreads, 1) void expert_down_many_kernel(ManyArgs a) {
+  using WF = W32<F, PK>;
+  using Stage = typename WF::Stage;
+  using WT = typename Frag<F>::WT;
+  constexpr int S = kDownManyStages, T = 32 * MTM;
+  __shared__ uint16_t As[S * T * kA32Pitch];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rl = lane & 31, hh = lane >> 5;
+  const int ncg = a.H / kDownManyCols;
+  const long long total = (long long)(*a.tile_count) * ncg;
+  const int u0 = (int)(total * blockIdx.x / gridDim.x);
+  const int u1 = (int)(total * (blockIdx.x + 1) / gridDim.x);
+  if (u0 >= u1) return;  // uniform over the workgroup
+  __shared__ TileCache tc;
+  cache_tiles(tc, a.tiles, u0 / ncg, (u1 - 1) / ncg);
+
+  // the weight source of unit u for this lane
+  struct Src {
+    const uint8_t* base;
+    const float* s8;
+    const uint8_t* s4;
+  };
+  auto src_of = [&](int u) {
+    const Tile t = cached_tile(tc, u / ncg);
+    const bool shared = t.expert == a.E;
+    const int inter = shared ? a.Is : a.I;
+    const size_t rowb = (size_t)inter * sizeof(WT) / Frag<F>::kPack;
+    const uint8_t* W = shared ? static_cast<const uint8_t*>(a.sw)
+                              : static_cast<const uint8_t*>(a.w) + (size_t)t.expert * a.H * rowb;
+    const int c0 = (u % ncg) * kDownManyCols + wave * 32;
+    Src s;
+    s.base = WF::lane_base(W, rowb, c0 + rl, c0 / 16 + rl / 16, lane);
+    s.s8 = nullptr;
+    s.s4 = nullptr;
+    if constexpr (F == WFmt::FP8) {
+      // the wave's 32 output rows lie in one 128-row scale block row
+      const float* Sc = static_cast<const float*>(shared ? a.sws : a.ws);
+      if (!shared) Sc += (size_t)t.expert * (a.H / 128) * (a.I / 128);
+      s.s8 = Sc + (size_t)(c0 / 128) * (inter / 128);
+    } else if constexpr (F == WFmt::FP4) {
+      const uint8_t* Sc = static_cast<const uint8_t*>(shared ? a.sws : a.ws);
+      if (!shared) Sc += (size_t)t.expert * a.H * (a.I / 32);
+      s.s4 = Sc + (size_t)(c0 + rl) * (inter / 32);
+    }
+    return s;
+  };
+
+  // h of tile t into LDS: load j of this wave fills row r of stage st, the
+  // first 16 lanes 16 bytes each (lane i lands at 16 i bytes from the row's
+  // start).  Rows past the tile re-read row 0.
+  auto stage_h = [&](const Tile& t, int mt) {
+    const bool shared = t.expert == a.E;
+    const int inter = shared ? a.Is : a.I;
+    const uint16_t* hb = static_cast<const uint16_t*>(a.h) +
+                         (shared ? (size_t)a.N * a.K * a.I + (size_t)t.start * a.Is : (size_t)t.start * a.I);
+    const int rows = 32 * mt;
+    for (int j = wave; j < S * rows; j += kManyWaves) {
+      const int st = j / rows, r = j % rows;
+      const int rr = r < t.rows ? r : 0;
+      const uint16_t* src = hb + (size_t)rr * inter + st * 128 + (lane & 15) * 8;
+      uint16_t* dst = As + ((size_t)st * T + r) * kA32Pitch;
+      if (lane < 16) __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    }
+  };
+
+  Stage w[S];
+  {
+    const Src s0 = src_of(u0);
+#pragma unroll
+    for (int s = 0; s < S; ++s) WF::load(w[s], s0.base, s0.s8, s0.s4, s, lane);
+  }
+  int cur_slot = -1;
+  auto unit = [&](int u) {
+    const Tile t = cached_tile(tc, u / ncg);
+    const int slot = u / ncg;
+    const int mt = (t.rows + 31) / 32;
+    if (slot != cur_slot) {
+      __syncthreads();  // every wave is done with the previous tile's h
+      stage_h(t, mt);
+      __syncthreads();  // (the compiler waits for the direct loads here)
+      cur_slot = slot;
+    }
+    // the next unit's source (the last unit re-reads its own: every load is
+    // unconditional, so the compiler's waits stay exact)
+    const Src sn = src_of(u + 1 < u1 ? u + 1 : u);
+    const int c = (u % ncg) * kDownManyCols + wave * 32 + rl;
+    const bool shared = t.expert == a.E;
+    const size_t y0 = ((shared ? (size_t)a.N * a.K : 0) + (size_t)t.start) * a.H;
+    f32x16 acc[MTM];
+#pragma unroll
+    for (int i = 0; i < MTM; ++i) acc[i] = f32x16{};
+    static_for<0, S>([&](auto SI) {
+      constexpr int s = decltype(SI)::value;
+      const uint16_t* As_s = As + (size_t)s * T * kA32Pitch;
+      // the tile's row-tile count, dispatched inside the stage so that the
+      // ring registers have one definition per stage
+      static_for<1, MTM + 1>([&](auto M) {
+        constexpr int MT = decltype(M)::value;
+        if (mt != MT) return;
+        if constexpr (F == WFmt::FP8) {
+          // row tiles two at a time: their stage partials, then times the
+          // block scale; each widened weight step feeds both MFMAs
+          const float sc = __uint_as_float(w[s].sc);
+          static_for<0, (MT + 1) / 2>([&](auto PI) {
+            constexpr int i0 = 2 * decltype(PI)::value;
+            constexpr int NP = i0 + 1 < MT ? 2 : 1;
+            f32x16 tmp[NP];
+            u32x4 av[NP];
+#pragma unroll
+            for (int j = 0; j < NP; ++j) {
+              tmp[j] = f32x16{};
+              av[j] = lds_frag(As_s, (i0 + j) * 32 + rl, WF::ack(0, hh));
+            }
+#pragma unroll
+            for (int tt = 0; tt < WF::STEPS; ++tt) {
+              u32x4 an[NP];
+#pragma unroll
+              for (int j = 0; j < NP; ++j)
+                an[j] = tt + 1 < WF::STEPS ? lds_frag(As_s, (i0 + j) * 32 + rl, WF::ack(tt + 1, hh)) : av[j];
+              u32x2 codes = WF::codes8(w[s], tt);
+              asm volatile("" : "+v"(codes));  // widen here, once per pair of row tiles
+              const u32x4 b = Frag<WFmt::FP8>::widen(codes);
+#pragma unroll
+              for (int j = 0; j < NP; ++j) tmp[j] = mfma32(av[j], b, tmp[j]);
+#pragma unroll
+              for (int j = 0; j < NP; ++j) av[j] = an[j];
+            }
+#pragma unroll
+            for (int j = 0; j < NP; ++j)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) acc[i0 + j][v] = __builtin_fmaf(sc, tmp[j][v], acc[i0 + j][v]);
+          });
+        } else {
+          u32x4 av[MT];
+#pragma unroll
+          for (int i = 0; i < MT; ++i) av[i] = lds_frag(As_s, i * 32 + rl, WF::ack(0, hh));
+#pragma unroll
+          for (int tt = 0; tt < WF::STEPS; ++tt) {
+            u32x4 an[MT];
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+              an[i] = tt + 1 < WF::STEPS ? lds_frag(As_s, i * 32 + rl, WF::ack(tt + 1, hh)) : av[i];
+            const u32x4 b = WF::bop(w[s], tt);
+#pragma unroll
+            for (int i = 0; i < MT; ++i) acc[i] = mfma32(av[i], b, acc[i]);
+#pragma unroll
+            for (int i = 0; i < MT; ++i) av[i] = an[i];
+          }
+        }
+      });
+      // this stage's registers now carry the next unit's same stage (the
+      // barriers keep the scheduler from hoisting the loads above the
+      // MFMAs that still read the old contents)
+      __builtin_amdgcn_sched_barrier(0);
+      WF::load(w[s], sn.base, sn.s8, sn.s4, s, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // y in bf16 (this kernel runs on 16-bit activations only); whole 32-row
+    // tiles unmasked, the tile's last one row by row
+    // (H passes through an empty asm so that the row addresses are computed
+    // here: hoisted out of the unit loop, all 16 * MTM of them stay live)
+    int Hs = a.H;
+    asm volatile("" : "+s"(Hs));
+    uint16_t* yb = static_cast<uint16_t*>(a.y) + y0 + c + (size_t)(4 * hh) * Hs;
+#pragma unroll
+    for (int i = 0; i < MTM; ++i) {
+      if (i >= mt) break;
+      const bool whole = (i + 1) * 32 <= t.rows;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = i * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+        if (whole || m < t.rows) yb[(size_t)(i * 32 + 8 * (v >> 2) + (v & 3)) * Hs] = f32_to_bf16(acc[i][v]);
+      }
+    }
+  };
+  // The first unit is peeled: the loop is then entered after the same
+  // sequence of loads as its back edge, and the compiler's waits for the
+  // ring registers stay exact (with the prologue's loads merged in at the
+  // loop header they degrade to waiting for everything in flight).
+  unit(u0);
+  for (int u = u0 + 1; u < u1; ++u) unit(u);
+}
+
+// CUs of the current device, for the persistent grids (queried once per device)
+static int cu_count() {
+  static int counts[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!counts[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    counts[dev] = n;
+  }
+  return counts[dev];
+}
+
+bool expert_many_fits(const Plan& p, bool up) {
+  // y in the activation dtype (the workspace plan's rule for tiles taller than 16 rows)
+  const bool base = p.mt_max > 1 && p.act == CMOE_BF16 && p.y_act && p.wt != CMOE_F32 &&
+                    (p.Is == 0 || p.Is == p.I) && p.tile_rows % 32 == 0;
+  if (up) return false;
+  return base && p.I == 128 * kDownManyStages && p.H % kDownManyCols == 0;
+}
+
+// Persistent grid: one workgroup per CU, or more when a run of units could
+// otherwise span more tiles than a workgroup caches.
+static unsigned many_grid(int max_tiles, int units_per_tile) {
+  const long long units = (long long)max_tiles * units_per_tile;
+  const long long per = (long long)(kManySlots - 2) * units_per_tile;  // units a run may hold
+  const long long need = (units + per - 1) / per;
+  const long long g = cu_count();
+  return (unsigned)(need > g ? need : g);
+}
+
+template <WFmt F, bool PK>
+static void launch_down_many(const ManyArgs& a, int mtm, int max_tiles, hipStream_t s) {
+  const unsigned grid = many_grid(max_tiles, a.H / kDownManyCols);
+  switch (mtm) {
+    case 1: expert_down_many_kernel<F, 1, PK><<<grid, kManyThreads, 0, s>>>(a); break;
+    case 2: expert_down_many_kernel<F, 2, PK><<<grid, kManyThreads, 0, s>>>(a); break;
+    case 3: expert_down_many_kernel<F, 3, PK><<<grid, kManyThreads, 0, s>>>(a); break;
+    default: expert_down_many_kernel<F, 4, PK><<<grid, kManyThreads, 0, s>>>(a); break;
+  }
+}
+
+hipError_t launch_expert_many(const Plan& p, const cmoe_weights& w, const void* x, bool up, hipStream_t s) {
+  ManyArgs a;
+  a.x = x;
+  a.w = up ? w.w13 : w.w2;
+  a.ws = up ? w.w13_scale : w.w2_scale;
+  a.sw = up ? w.shared_w13 : w.shared_w2;
+  a.sws = up ? w.shared_w13_scale : w.shared_w2_scale;
+  a.tiles = p.tiles;
+  a.tile_count = p.tile_count;
+  a.pair_row = p.pair_row;
+  a.h = p.h;
+  a.y = p.y;
+  a.y_act = p.y_act;
+  a.N = p.N;
+  a.H = p.H;
+  a.E = p.E;
+  a.I = p.I;
+  a.Is = p.Is;
+  a.K = p.K;
+  const int mtm = p.tile_rows / 32;
+  if (!up) {
+    if (p.wt == CMOE_FP8_E4M3) {
+      if (p.panels) launch_down_many<WFmt::FP8, true>(a, mtm, p.max_tiles, s);
+      else launch_down_many<WFmt::FP8, false>(a, mtm, p.max_tiles, s);
+    } else if (p.wt == CMOE_FP4_E2M1) {
+      if (p.panels) launch_down_many<WFmt::FP4, true>(a, mtm, p.max_tiles, s);
+      else launch_down_many<WFmt::FP4, false>(a, mtm, p.max_tiles, s);
+    } else {
+      if (p.panels) launch_down_many<WFmt::BF16, true>(a, mtm, p.max_tiles, s);
+      else launch_down_many<WFmt::BF16, false>(a, mtm, p.max_tiles, s);
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace cmoe

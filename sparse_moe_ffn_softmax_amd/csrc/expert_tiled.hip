@@ -59,30 +59,23 @@ struct TiledArgs {
 
 constexpr int kTiledMaxStages = 128;  // fp8 block scales held per weight row (hidden <= 16384)
 
-// One workgroup's GEMM: acc[mt] (16 x 16 each) for this wave's 16 columns,
-// over k in [0, Kdim).  asrc[i]: source row pointer (stage 0) of the i-th
-// activation vector this thread stages (rows past the tile repeat the tile's
-// first row, so that every load is unconditional); brow: this lane's weight
-// chunk 0 (bchunk0); bsc: its fp8 block scales, one per 128 k, in LDS.  PK:
-// the weights are stored in MFMA panels.
-template <WFmt F, int MT, bool PK>
-struct TiledGemm {
+// The k order, the LDS placement of staged activation rows, and one stage
+// (128 k for 16-bit activations) of weight loads and MFMAs, shared by the
+// tiled kernels below.  A stage of a staged activation row is 256 bytes,
+// stored with a 288-byte pitch; PK: the weights are stored in MFMA panels.
+template <WFmt F, bool PK>
+struct StageOps {
   using Fr = Frag<F>;
   using AT = typename Fr::AT;
   using WT = typename Fr::WT;
-  static constexpr int T = 16 * MT;
   static constexpr int KS = 256 / (int)sizeof(AT);  // k per stage (256 bytes of a row)
   static constexpr int U = KS / Fr::kStep;          // MFMA steps per stage
   static constexpr int VPR = 16;                    // 16-byte vectors per row per stage
-  static constexpr int NW = tiled_waves(MT);        // waves per workgroup
-  static constexpr int THREADS = 64 * NW;
-  static constexpr int RPP = THREADS / VPR;         // rows staged per pass of the workgroup
-  static constexpr int AV = T / RPP;                // vectors per thread per stage
   // 288-byte rows: the MFMA fragment reads (16 rows at one offset, the four
   // lane groups 64 contiguous bytes) are free of bank conflicts (a 272-byte
   // pitch measured 3.7 conflict cycles per read on gfx950)
   static constexpr int PAD = 32 / (int)sizeof(AT);
-  using Lds = AT[2][T][KS + PAD];
+  static constexpr int PITCH = KS + PAD;            // elements per staged row
   // k order inside a stage.  MFMA only needs A and B to agree on it, so fp8
   // pairs steps: lane group kg takes k [16kg, 16kg+16) of each 64-deep step
   // pair, and its weights arrive as one 16-byte load per two steps (8 fp8
@@ -105,6 +98,15 @@ struct TiledGemm {
     else return c;                                                          // c = 4u + kg
   }
   static __device__ __forceinline__ int aread(int u, int kg) { return (4 * u + kg) * (16 / (int)sizeof(AT)); }
+  static __device__ __forceinline__ int aread_sw(int u, int kg, int swz) {
+    return ((4 * u + kg) ^ swz) * (16 / (int)sizeof(AT));
+  }
+  // inverse of apos: the k-order chunk stored at position q
+  static __device__ __forceinline__ int ainv(int q) {
+    if constexpr (kPair) return (q & 8) | ((q & 3) << 1) | ((q >> 2) & 1);
+    else if constexpr (F == WFmt::FP4) return ((q & 3) << 2) | (q >> 2);
+    else return q;
+  }
   // Each lane group kg reads the 16 weight bytes at byte 16kg of every 64
   // bytes of its row (fp8 through the paired order above), i.e. one chunk
   // (expert_frag.h) per 64 row bytes.
@@ -122,10 +124,116 @@ struct TiledGemm {
     uint32_t sc;
   };
 
+  // Weights of the stage at k0: this lane's chunks from brow (its chunk 0);
+  // bsc: fp4: this lane's row of E8M0 bytes.
+  static __device__ __forceinline__ void load_b(BSet& bs, const uint8_t* brow, const void* bsc, int k0) {
+    constexpr int QB = kChunk<PK>;
+    auto& b = bs.b;
+    if constexpr (F == WFmt::FP4) {
+      const u32x4 v = load_chunk<PK>(brow + (k0 / 128) * QB);
+#pragma unroll
+      for (int u = 0; u < U; ++u) b[u] = v[u];
+      bs.sc = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(bsc) + k0 / 32);
+      // keep the next stage's loads ahead of this stage's scale use, which
+      // would otherwise be hoisted and wait for every load in flight
+      __builtin_amdgcn_sched_barrier(0);
+    } else if constexpr (kPair) {
+#pragma unroll
+      for (int j = 0; j < U / 2; ++j) {
+        const u32x4 v = load_chunk<PK>(brow + (k0 / 64 + j) * QB);
+        b[2 * j] = typename Fr::B{v[0], v[1]};
+        b[2 * j + 1] = typename Fr::B{v[2], v[3]};
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        b[u] = __builtin_bit_cast(typename Fr::B,
+                                  load_chunk<PK>(brow + ((k0 + u * Fr::kStep) * (int)sizeof(WT) / 64) * QB));
+    }
+  }
+
+  // MFMAs of one stage for MTX row tiles: a0 is this lane's staged row
+  // (row `col` of the stage buffer), rows `pitch` elements apart, its
+  // 16-byte chunk q stored at position q ^ swz; sc8: fp8: the stage's fp32
+  // block scale.  Per k step the MTX activation fragments are read first,
+  // then the MTX MFMAs issue.
+  template <int MTX, bool kRewiden = false>
+  static __device__ __forceinline__ void mma(const AT* a0, int pitch, int swz, const BSet& bs, float sc8,
+                                             int kg, f32x4 (&acc)[MTX]) {
+    const auto& b = bs.b;
+    if constexpr (F == WFmt::FP4) {
+      const float sc = Fr::scale_of((bs.sc >> (8 * kg)) & 0xFFu);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        typename Fr::A av[MTX];
+#pragma unroll
+        for (int mt = 0; mt < MTX; ++mt) av[mt] = Fr::load_a(a0 + mt * 16 * pitch + aread_sw(u, kg, swz));
+#pragma unroll
+        for (int mt = 0; mt < MTX; ++mt) acc[mt] = Fr::mma(av[mt], b[u], sc, acc[mt]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if constexpr (F == WFmt::FP8) {
+      f32x4 tmp[MTX];
+#pragma unroll
+      for (int mt = 0; mt < MTX; ++mt) tmp[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        typename Fr::A av[MTX];
+#pragma unroll
+        for (int mt = 0; mt < MTX; ++mt) av[mt] = Fr::load_a(a0 + mt * 16 * pitch + aread_sw(u, kg, swz));
+        // kRewiden: widen here, from the codes, whatever the caller did
+        // before: a caller running several passes over the same weights
+        // would otherwise keep every widened step alive
+        typename Fr::B bu = b[u];
+        if constexpr (kRewiden) asm volatile("" : "+v"(bu));
+        const u32x4 wb = Fr::widen(bu);
+#pragma unroll
+        for (int mt = 0; mt < MTX; ++mt) tmp[mt] = Fr::mma_wide(av[mt], wb, tmp[mt]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MTX; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[mt][v] = __builtin_fmaf(sc8, tmp[mt][v], acc[mt][v]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        typename Fr::A av[MTX];
+#pragma unroll
+        for (int mt = 0; mt < MTX; ++mt) av[mt] = Fr::load_a(a0 + mt * 16 * pitch + aread_sw(u, kg, swz));
+#pragma unroll
+        for (int mt = 0; mt < MTX; ++mt) acc[mt] = Fr::mma(av[mt], b[u], acc[mt]);
+        // keep the scheduler from hoisting every k step's operands at once
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+};
+
+// One workgroup's GEMM: acc[mt] (16 x 16 each) for this wave's 16 columns,
+// over k in [0, Kdim).  asrc[i]: source row pointer (stage 0) of the i-th
+// activation vector this thread stages (rows past the tile repeat the tile's
+// first row, so that every load is unconditional); brow: this lane's weight
+// chunk 0 (bchunk0); bsc: its fp8 block scales, one per 128 k, in LDS.  PK:
+// the weights are stored in MFMA panels.
+template <WFmt F, int MT, bool PK>
+struct TiledGemm : StageOps<F, PK> {
+  using Ops = StageOps<F, PK>;
+  using Fr = Frag<F>;
+  using AT = typename Fr::AT;
+  using WT = typename Fr::WT;
+  using BSet = typename Ops::BSet;
+  static constexpr int T = 16 * MT;
+  static constexpr int KS = Ops::KS, VPR = Ops::VPR, PITCH = Ops::PITCH;
+  static constexpr int NW = tiled_waves(MT);        // waves per workgroup
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int RPP = THREADS / VPR;         // rows staged per pass of the workgroup
+  static constexpr int AV = T / RPP;                // vectors per thread per stage
+  using Lds = AT[2][T][PITCH];
+
   static __device__ __forceinline__ void run(Lds& As, const AT* const (&asrc)[AV],
                                              const uint8_t* brow, const void* bsc, int Kdim,
                                              f32x4 (&acc)[MT]) {
-    constexpr int QB = kChunk<PK>;
     const int tid = threadIdx.x, lane = tid & 63;
     const int col = lane & 15, kg = lane >> 4;
     const int seg = tid % VPR, r0 = tid / VPR;
@@ -142,78 +250,15 @@ struct TiledGemm {
     auto store_a = [&](int buf) {
 #pragma unroll
       for (int i = 0; i < AV; ++i)
-        *reinterpret_cast<u32x4*>(&As[buf][r0 + i * RPP][apos(seg) * (16 / (int)sizeof(AT))]) = areg[i];
+        *reinterpret_cast<u32x4*>(&As[buf][r0 + i * RPP][Ops::apos(seg) * (16 / (int)sizeof(AT))]) = areg[i];
     };
-    auto load_b = [&](BSet& bs, int k0) {
-      auto& b = bs.b;
-      if constexpr (F == WFmt::FP4) {
-        const u32x4 v = load_chunk<PK>(brow + (k0 / 128) * QB);
-#pragma unroll
-        for (int u = 0; u < U; ++u) b[u] = v[u];
-        bs.sc = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(bsc) + k0 / 32);
-        // keep the next stage's loads ahead of this stage's scale use, which
-        // would otherwise be hoisted and wait for every load in flight
-        __builtin_amdgcn_sched_barrier(0);
-      } else if constexpr (kPair) {
-#pragma unroll
-        for (int j = 0; j < U / 2; ++j) {
-          const u32x4 v = load_chunk<PK>(brow + (k0 / 64 + j) * QB);
-          b[2 * j] = typename Fr::B{v[0], v[1]};
-          b[2 * j + 1] = typename Fr::B{v[2], v[3]};
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          b[u] = __builtin_bit_cast(typename Fr::B,
-                                    load_chunk<PK>(brow + ((k0 + u * Fr::kStep) * (int)sizeof(WT) / 64) * QB));
-      }
-    };
-    // Every row tile runs (rows past the tile are zeros in LDS): a guard per
-    // row tile would make each MFMA wait for its own LDS read.  Per k step the
-    // MT activation fragments are read first, then the MT MFMAs issue.
+    auto load_b = [&](BSet& bs, int k0) { Ops::load_b(bs, brow, bsc, k0); };
+    // Every row tile runs (the rows past the tile repeat the tile's first
+    // row in LDS, and their outputs are never stored): a guard per row tile
+    // would make each MFMA wait for its own LDS read.
     auto compute = [&](BSet& bs, int buf, int k0) {
-      auto& b = bs.b;
-      if constexpr (F == WFmt::FP4) {
-        const float sc = Fr::scale_of((bs.sc >> (8 * kg)) & 0xFFu);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          typename Fr::A av[MT];
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) av[mt] = Fr::load_a(&As[buf][mt * 16 + col][aread(u, kg)]);
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[mt] = Fr::mma(av[mt], b[u], sc, acc[mt]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      } else if constexpr (F == WFmt::FP8) {
-        f32x4 tmp[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) tmp[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          typename Fr::A av[MT];
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) av[mt] = Fr::load_a(&As[buf][mt * 16 + col][aread(u, kg)]);
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) tmp[mt] = Fr::mma(av[mt], b[u], tmp[mt]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        const float sc = static_cast<const float*>(bsc)[k0 / 128];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) acc[mt][v] = __builtin_fmaf(sc, tmp[mt][v], acc[mt][v]);
-      } else {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          typename Fr::A av[MT];
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) av[mt] = Fr::load_a(&As[buf][mt * 16 + col][aread(u, kg)]);
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[mt] = Fr::mma(av[mt], b[u], acc[mt]);
-          // keep the scheduler from hoisting every k step's operands at once
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+      const float sc8 = F == WFmt::FP8 ? static_cast<const float*>(bsc)[k0 / 128] : 0.f;
+      Ops::template mma<MT>(&As[buf][col][0], PITCH, 0, bs, sc8, kg, acc);
     };
 
     // Schedule: while stage s feeds the MFMAs, stage s+1's activations and

@@ -103,6 +103,31 @@ def test_threshold_on_a_prefix_sum_takes_the_serial_cut(tau, m):
     assert np.all(ref["coreset_size"] == m)
 
 
+# many rows per expert at I = 512: the down GEMM that keeps a tile's whole h
+# in LDS (persistent grid, row tiles dispatched per tile)
+RES = W.Workload("res_bf16", 8, 32, 256, 16, 4, 512, 512, W.BF16, W.BF16, 0.9, seed=121)
+
+
+@pytest.mark.parametrize("wl,layout", [
+    (RES, "rows"),
+    (RES.with_(name="res_fp8", weight_dtype=W.FP8, seed=122), "rows"),
+    (RES.with_(name="res_fp4", weight_dtype=W.FP4, seed=123), "rows"),
+    (RES.with_(name="res_fp8_panels", weight_dtype=W.FP8, seed=124), "panels"),
+    (RES.with_(name="res_bf16_panels", seed=131), "panels"),
+    (RES.with_(name="res_noshared", shared_inter=0, seed=125), "rows"),
+    (RES.with_(name="res_H384", hidden=384, seed=126), "rows"),
+    (RES.with_(name="res_mt2", num_blocks=4, num_experts=64, top_k=8, seed=127), "rows"),
+    (RES.with_(name="res_hot", bias_sigma=3.0, seed=128), "rows"),
+    (RES.with_(name="res_live_budget", live_fraction=0.6, expert_budget=6, seed=129), "rows"),
+    (RES.with_(name="res_rows8", block_rows=8, num_blocks=32, seed=130), "rows"),
+], ids=lambda v: v if isinstance(v, str) else v.name)
+def test_resident_down_shapes(wl, layout):
+    inp = W.generate(wl)
+    _, _, ref = check(inp, threads=16, dp=cm.upload(inp, layout=layout))
+    if wl.name == "res_hot":
+        assert ref["expert_counts"].max() > 96   # an expert spans several tiles
+
+
 # 4-bit experts (MXFP4: E2M1 codes, E8M0 scale per 32 elements), widened to
 # bf16 exactly in both kernel families
 @pytest.mark.parametrize("wl", [
