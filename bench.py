@@ -256,6 +256,9 @@ def main():
                     help="rough budget of the oracle CPU-baseline leg (0 disables it)")
     ap.add_argument("--no-peaks", dest="peaks", action="store_false",
                     help="skip measuring the achievable HBM read and MFMA rates of the GPU")
+    ap.add_argument("--act-fp8", action="store_true",
+                    help="fp8 weights only: MXFP8 activations into the expert GEMMs (W8A8, "
+                         "cmoe_options.activation_fp8)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="copy a device buffer of this many bytes once before the workload: "
                          "a plain copy kernel of known size for calibrating HBM byte counters")
@@ -313,8 +316,8 @@ def main():
     x = dp.tensors["x"]
     # expert budget / live rows: the _ex entry point with the workload's options
     opts = None
-    if wl.expert_budget or dp.tensors.get("live_rows") is not None:
-        opts = cm.make_options(wl.expert_budget, dp.tensors.get("live_rows"))
+    if wl.expert_budget or dp.tensors.get("live_rows") is not None or args.act_fp8:
+        opts = cm.make_options(wl.expert_budget, dp.tensors.get("live_rows"), int(args.act_fp8))
     for i in range(args.warmup):
         cm.clover_moe_block_forward(dp.problem, layers[i % len(layers)], x, tau, K, out,
                                     routings[i], ws, stream=stream, options=opts)
@@ -437,11 +440,21 @@ def main():
     device_ms = stage_ms.sum(1)
     if dom_bytes is not None:
         achieved = float(dom_bytes.sum() / (stage_ms[:, dom].sum() * 1e-3) / 1e9)
-        # the library's work-tile rule: 16-row tiles run the register-operand
-        # kernels (expert_gemm.hip), taller tiles the LDS-tiled ones
-        kname = f"expert_{'up' if dom == 2 else 'down'}{'_tiled' if tiled else ''}_kernel"
-        traffic = measured_traffic(kname, wl.name, "expert_tiled.hip" if tiled else "expert_gemm.hip",
-                                   args.layout)
+        # the library's kernel choice: 16-row work tiles run the register-operand
+        # kernels (expert_gemm.hip); taller tiles the many-row kernels
+        # (expert_many.hip) where their shapes fit, else the LDS-tiled ones
+        many_dn = (tiled and I == 512 and H % 256 == 0 and Is in (0, I) and wl.act_dtype == W.BF16
+                   and wl.weight_dtype != W.F32)
+        if dom == 2:
+            kname, src = (("expert_up_mx_kernel", "expert_many.hip") if args.act_fp8 else
+                          ("expert_up_tiled_kernel", "expert_tiled.hip") if tiled else
+                          ("expert_up_kernel", "expert_gemm.hip"))
+        else:
+            kname, src = (("expert_down_many_kernel", "expert_many.hip") if many_dn else
+                          ("expert_down_tiled_kernel", "expert_tiled.hip") if tiled else
+                          ("expert_down_kernel", "expert_gemm.hip"))
+        wl_key = wl.name + ("_w8a8" if args.act_fp8 else "")
+        traffic = measured_traffic(kname, wl_key, src, args.layout)
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                     "traffic": traffic, "kernel": kname,
@@ -450,7 +463,7 @@ def main():
         # past the ridge (MFMA peak / HBM peak flop per byte) the kernel's
         # roof is the matrix cores: report it against the MFMA peak instead
         dom_flops = up_flops if dom == 2 else dn_flops
-        mfma_peak = MFMA_DATASHEET_TFLOPS[MFMA_KIND[wl.weight_dtype]]
+        mfma_peak = MFMA_DATASHEET_TFLOPS["fp8" if args.act_fp8 else MFMA_KIND[wl.weight_dtype]]
         if peaks:
             roofline["frac_of_measured_peak"] = round(achieved / peaks["hbm_read_gbps"], 4)
             roofline["measured_peak"] = peaks["hbm_read_gbps"]
@@ -466,14 +479,16 @@ def main():
 
     value = B / (ms_per_step * 1e-3)
     rate = mfma_flops.mean() / (ms_per_step * 1e-3) / 1e12
-    mk = MFMA_KIND[wl.weight_dtype]
+    mk = "fp8" if args.act_fp8 else MFMA_KIND[wl.weight_dtype]
     mfma_util = {f"vs_{mk}_datasheet": round(float(rate / MFMA_DATASHEET_TFLOPS[mk]), 5)}
     if wl.weight_dtype == W.FP8:
         mfma_util["vs_fp8_datasheet"] = round(float(rate / MFMA_DATASHEET_TFLOPS["fp8"]), 5)
+        mfma_util["vs_bf16_datasheet"] = round(float(rate / MFMA_DATASHEET_TFLOPS["bf16"]), 5)
     if peaks and mk in ("bf16", "fp8"):
         mfma_util[f"vs_{mk}_measured"] = round(float(rate / peaks[f"mfma_{mk}_tflops"]), 5)
         if wl.weight_dtype == W.FP8:
             mfma_util["vs_fp8_measured"] = round(float(rate / peaks["mfma_fp8_tflops"]), 5)
+            mfma_util["vs_bf16_measured"] = round(float(rate / peaks["mfma_bf16_tflops"]), 5)
     call_gbps = float(call_bytes.mean() / (ms_per_step * 1e-3) / 1e9)
     res = {
         "metric": "MoE block-passes/s + achieved HBM GB/s & MFMA util vs peak, 32-row block",
@@ -486,13 +501,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {W.BF16: "bf16", W.F32: "f32", W.FP8: "fp8_e4m3 weights, bf16 activations",
-                  W.FP4: "fp4_e2m1 (MXFP4) weights, bf16 activations"}[wl.weight_dtype],
+        "dtype": ("fp8_e4m3 weights, MXFP8 activations into the expert GEMMs (W8A8)" if args.act_fp8 else
+                  {W.BF16: "bf16", W.F32: "f32", W.FP8: "fp8_e4m3 weights, bf16 activations",
+                   W.FP4: "fp4_e2m1 (MXFP4) weights, bf16 activations"}[wl.weight_dtype]),
         "data": "synthetic (seeded normal inputs and random-init weights of the stated shapes)",
         "config": {"workload": wl.name, "num_blocks": B, "block_rows": wl.block_rows, "hidden": H,
                    "experts": E, "top_k": K, "inter": I, "shared_inter": Is,
                    "mass_threshold": tau, "weight_copies_rotated": args.layers,
-                   "weight_layout": args.layout},
+                   "weight_layout": args.layout, "activation_fp8": bool(args.act_fp8)},
         "roofline": roofline,
         "call": {
             "device_us_staged": round(float(device_ms.mean() * 1e3), 2),

@@ -190,10 +190,27 @@ typedef struct {
  *                 (topk_idx -1, gates 0).  A block with no live row has an
  *                 empty coreset (size 0, ids -1).  Its logits are still
  *                 computed.
+ *  activation_fp8: 0 (default) or 1.  With 1, the expert GEMMs take their
+ *                 activations in fp8 too (W8A8): x and h are rounded to
+ *                 OCP MXFP8 (E4M3 codes, one E8M0 power-of-two scale per 32
+ *                 consecutive elements of a row, the smallest scale that
+ *                 keeps the group's largest magnitude within 448, codes
+ *                 rounded to nearest even) and multiplied on the fp8
+ *                 matrix cores.  The fp8 weights of InfiniLM PR #584
+ *                 ("Benchmark") are served with bf16 activations; this is
+ *                 an opt-in trade of accuracy for speed, checked against
+ *                 the same oracle at a looser bound.  Only for fp8 weights
+ *                 with bf16 activations, inter 512, shared_inter 0 or 512,
+ *                 hidden 512, 1024 or 2048 and calls with many routed rows
+ *                 per expert (work tiles of 32 rows or more: N*top_k above
+ *                 about 10.7 E routed pairs);
+ *                 other calls return CMOE_ERR_UNSUPPORTED.  Router, routing
+ *                 and combine are unchanged.
  */
 typedef struct {
     int32_t expert_budget;
     const uint8_t* live_rows;
+    int32_t activation_fp8;
 } cmoe_options;
 
 /* Bytes of device workspace clover_moe_block_forward needs for this problem
@@ -230,8 +247,10 @@ cmoe_status clover_moe_block_forward(const cmoe_problem* problem, const cmoe_wei
                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* clover_moe_block_forward with options (see cmoe_options; NULL = none).
- * Errors: expert_budget outside [0, E] is CMOE_ERR_VALUE; a live_rows range
- * that is misaligned or overlaps an output is CMOE_ERR_ALIGN / CMOE_ERR_ALIAS. */
+ * Errors: expert_budget outside [0, E] or activation_fp8 other than 0 or 1 is
+ * CMOE_ERR_VALUE; activation_fp8 = 1 on a call it does not cover is
+ * CMOE_ERR_UNSUPPORTED; a live_rows range that is misaligned or overlaps an
+ * output is CMOE_ERR_ALIGN / CMOE_ERR_ALIAS. */
 cmoe_status clover_moe_block_forward_ex(const cmoe_problem* problem, const cmoe_weights* weights,
                                         const void* x, float mass_threshold, int32_t top_k,
                                         const cmoe_options* options, void* out,

@@ -51,7 +51,8 @@ class cmoe_routing(ctypes.Structure):
 
 
 class cmoe_options(ctypes.Structure):
-    _fields_ = [("expert_budget", ctypes.c_int32), ("live_rows", ctypes.c_void_p)]
+    _fields_ = [("expert_budget", ctypes.c_int32), ("live_rows", ctypes.c_void_p),
+                ("activation_fp8", ctypes.c_int32)]
 
 
 class ClovermoeError(RuntimeError):
@@ -238,9 +239,10 @@ def make_weights(router_w, w13, w2, router_b=None, w13_scale=None, w2_scale=None
                         _ptr(shared_w2_scale), LAYOUT_CODES[layout])
 
 
-def make_options(expert_budget: int = 0, live_rows=None) -> cmoe_options:
-    """live_rows: a [N] uint8 device tensor (1 = live) or None."""
-    return cmoe_options(int(expert_budget), _ptr(live_rows))
+def make_options(expert_budget: int = 0, live_rows=None, activation_fp8: int = 0) -> cmoe_options:
+    """live_rows: a [N] uint8 device tensor (1 = live) or None; activation_fp8:
+    1 = MXFP8 activations into the fp8-weight expert GEMMs (W8A8)."""
+    return cmoe_options(int(expert_budget), _ptr(live_rows), int(activation_fp8))
 
 
 def make_routing(**tensors) -> cmoe_routing:

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libclover_moe.so")
 SOURCES = ["api.cpp", "router.hip", "route_block.hip", "permute_blocks.hip", "expert_gemm.hip",
-           "expert_tiled.hip", "expert_many.hip", "combine.hip", "pack.hip"]
+           "expert_tiled.hip", "expert_many.hip", "quant.hip", "combine.hip", "pack.hip"]
 PEAKS_LIB = os.path.join(PKG, "libclover_moe_peaks.so")
 PEAKS_SOURCES = ["peaks.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -115,7 +115,7 @@ cmoe_status check_problem(const cmoe_problem* p, int32_t top_k) {
 
 struct Layout {
   size_t logits, topk, gates, counts, offsets, pair_row, pair_pos, blockmask, blockpre, tiles,
-      tile_count, h, y, total;
+      tile_count, h, y, x8, total;
   int max_tiles, mt_max, y_act;
 };
 
@@ -160,6 +160,9 @@ Layout layout(const cmoe_problem& p, int K) {
   // stored in the activation dtype, halving its write and read traffic.
   L.y_act = L.mt_max > 1 && p.act_dtype == CMOE_BF16;
   L.y = take((NK + N) * H * (L.y_act ? 2 : 4));
+  // fp8 activations (cmoe_options.activation_fp8): x as MXFP8 codes [N, H]
+  // and E8M0 scales [N, H/32], for the many-row fp8-weight GEMMs
+  L.x8 = p.weight_dtype == CMOE_FP8_E4M3 && L.y_act ? take(N * H + N * H / 32) : 0;
   L.total = off;
   return L;
 }
@@ -202,6 +205,8 @@ void carve(Plan& p, const cmoe_problem& pr, int K, void* ws, const cmoe_routing*
   p.h = base + L.h;
   p.y = base + L.y;
   p.y_act = L.y_act;
+  p.act8 = 0;
+  p.x8 = L.x8 ? base + L.x8 : nullptr;
   p.coreset_ids = rt ? rt->coreset_ids : nullptr;
   p.coreset_size = rt ? rt->coreset_size : nullptr;
   p.block_mass = rt ? rt->block_mass : nullptr;
@@ -250,9 +255,11 @@ static cmoe_status forward_impl(const cmoe_problem* problem, const cmoe_weights*
     return fail(CMOE_ERR_VALUE, "mass_threshold=%g must be in (0, 1]", (double)mass_threshold);
   const int budget = options ? options->expert_budget : 0;
   const uint8_t* live = options ? options->live_rows : nullptr;
+  const int act8 = options ? options->activation_fp8 : 0;
   if (budget < 0 || budget > p.num_experts)
     return fail(CMOE_ERR_VALUE, "expert_budget=%d must be in [0, num_experts=%d]", budget,
                 p.num_experts);
+  if (act8 != 0 && act8 != 1) return fail(CMOE_ERR_VALUE, "activation_fp8=%d must be 0 or 1", act8);
 
   const size_t need = cmoe::workspace_bytes(p, top_k);
   if (!workspace || workspace_bytes < need)
@@ -326,6 +333,13 @@ static cmoe_status forward_impl(const cmoe_problem* problem, const cmoe_weights*
   plan.live = live;
   plan.budget = budget;
   plan.panels = w->layout == CMOE_LAYOUT_PANELS;
+  plan.act8 = act8;
+  if (act8 && (!plan.x8 || !cmoe::expert_many_fits(plan, true) || !cmoe::expert_many_fits(plan, false)))
+    return fail(CMOE_ERR_UNSUPPORTED,
+                "activation_fp8 needs fp8 weights with bf16 activations, inter=512, shared_inter 0 or "
+                "512, hidden 512, 1024 or 2048 and work tiles of 32 rows or more (N*top_k above about "
+                "10.7 per expert); here weight=%d act=%d inter=%d shared_inter=%d hidden=%d, tile rows %d",
+                p.weight_dtype, p.act_dtype, p.inter, p.shared_inter, p.hidden, plan.tile_rows);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   // few routed pairs: the down GEMM writes `out` itself (stage 4 is empty)

@@ -56,6 +56,8 @@ struct Plan {
   int y_act;             // y stored in act_dtype (else fp32), see carve()
   const uint8_t* live;   // [N] live-row mask, or nullptr (every row live)
   int budget;            // coreset cap per block, 0 = none
+  int act8;              // fp8 (MXFP8) activations into the many-row GEMMs (cmoe_options.activation_fp8)
+  void* x8;              // [N, H] e4m3 codes then [N, H/32] E8M0 scales (act8)
   // optional caller outputs
   int32_t* coreset_ids;
   int32_t* coreset_size;
@@ -109,6 +111,8 @@ hipError_t launch_expert_tiled(const Plan& p, const cmoe_weights& w, const void*
 bool expert_many_fits(const Plan& p, bool up);
 hipError_t launch_expert_many(const Plan& p, const cmoe_weights& w, const void* x, bool up, hipStream_t s);
 hipError_t launch_combine(const Plan& p, void* out, hipStream_t s);
+// bf16 rows [rows, cols] -> MXFP8 codes [rows, cols] and E8M0 scales [rows, cols/32]
+hipError_t launch_quant_mx8(const void* src, long long rows, int cols, void* dst, void* scales, hipStream_t s);
 // count row-major matrices of rows x row_bytes bytes -> MFMA panels (clover_moe.h)
 hipError_t launch_pack_panels(const void* src, void* dst, int64_t count, int rows, int row_bytes, int gate_up,
                               hipStream_t s);

@@ -34,6 +34,7 @@
 namespace cmoe {
 
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
 
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -113,6 +114,79 @@ struct W32 {
     else return 8 * h + 4 * (t >> 2) + (t & 3);
   }
 };
+
+// ---------------------------------------------------------------------------
+// fp8 activations (MXFP8: OCP e4m3 codes with an E8M0 scale per 32
+// consecutive elements of a row) times fp8 weights on
+// v_mfma_scale_f32_32x32x64_f8f6f4.
+//
+// Scale blocks of that MFMA (checked on gfx950 with single-lane scale
+// changes): of the 32 codes lane l supplies, the first 16 of lanes r and r+32
+// form one 32-element block, scaled by lane r's E8M0 byte, and their last 16
+// the other block, scaled by lane r+32's.  A 64-deep step over k [64q, 64q+64)
+// therefore gives lane (r, h), h = l/32, the codes k 64q + 16h .. +16 and
+// 64q + 32 + 16h .. +16, and its scale byte is that of group 2q + h (k
+// 64q + 32h .. +32), so each activation group of 32 consecutive k is one
+// scale block.  The weights follow the same k order: pieces h and h+2 of each
+// 64-byte segment; their block scale is applied by the caller (unit MFMA
+// scale, byte 127).
+// ---------------------------------------------------------------------------
+template <bool PK>
+struct W32Mx {
+  static constexpr int SEGS = 2;           // 64-byte segments per 128-deep stage
+  static constexpr int SEGSTRIDE = PK ? 1024 : 64;
+  static constexpr int PSTRIDE = PK ? 512 : 32;  // piece h+2 after piece h
+  struct Stage {
+    u32x4 c[4];      // [2q]: piece h of segment q, [2q+1]: piece h+2
+    uint32_t sc;     // the row's fp32 block scale for the stage (bits)
+  };
+  static __device__ __forceinline__ const uint8_t* lane_base(const uint8_t* W, size_t rowb, int row, int panel,
+                                                             int lane) {
+    const int rl = lane & 31, h = lane >> 5;
+    if constexpr (PK) return W + (size_t)panel * 16 * rowb + 16 * (rl & 15) + 256 * h;
+    else return W + (size_t)row * rowb + 16 * h;
+  }
+  static __device__ __forceinline__ void load(Stage& st, const uint8_t* base, const float* sc_fp8, int s) {
+#pragma unroll
+    for (int q = 0; q < SEGS; ++q)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        st.c[2 * q + j] = load_chunk<PK>(base + (size_t)(s * SEGS + q) * SEGSTRIDE + j * PSTRIDE);
+    st.sc = __float_as_uint(sc_fp8[s]);
+  }
+  static __device__ __forceinline__ i32x8 operand(const Stage& st, int q) {
+    const u32x4 a = st.c[2 * q], b = st.c[2 * q + 1];
+    return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+  }
+};
+
+// fp8 x fp8 MFMA with the activation's E8M0 byte (scale_a) and unit weight scale
+__device__ __forceinline__ f32x16 mfma_mx(i32x8 a, i32x8 b, int scale_a, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, 127);
+}
+
+// Staged fp8 activation rows: 128 codes per stage with a 144-byte pitch (the
+// 16 rows one read touches fall in distinct bank groups).
+constexpr int kA8Pitch = 144;
+
+// The two 16-byte pieces of lane (r, h)'s step q from a staged fp8 row
+__device__ __forceinline__ i32x8 lds_frag8(const uint8_t* row, int q, int h) {
+  const u32x4 a = *reinterpret_cast<const u32x4*>(row + 64 * q + 16 * h);
+  const u32x4 b = *reinterpret_cast<const u32x4*>(row + 64 * q + 32 + 16 * h);
+  return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+}
+
+// E8M0 scale of a group of 32 values whose largest magnitude is amax: the
+// smallest e with amax / 2^e <= 448 (the largest e4m3 magnitude), from the
+// bits of amax (448 = 1.75 * 2^8); byte e + 127, clamped to [0, 254].
+__device__ __forceinline__ int mx8_scale_byte(float amax) {
+  const uint32_t b = __float_as_uint(amax);
+  const int ex = (int)((b >> 23) & 0xFFu);       // biased exponent (0: zero or subnormal)
+  if (ex == 0) return 0;                          // 2^-127: codes of such values are 0 or tiny
+  const int e = (ex - 127) - ((b & 0x7FFFFFu) <= 0x600000u ? 8 : 7);
+  const int s = e + 127;
+  return s < 0 ? 0 : (s > 254 ? 254 : s);
+}
 
 constexpr int kA32Pitch = 136;  // elements per staged activation row (272 bytes)
 

@@ -36,11 +36,11 @@ TOL = {
 SENTINEL = 768.0
 
 
-def run_gpu(inp, tau: float, top_k: int, dp=None, workspace=None, outputs=None):
+def run_gpu(inp, tau: float, top_k: int, dp=None, workspace=None, outputs=None, act_fp8=False):
     """One call through the C ABI; returns (out as fp64 numpy, routing dict).
-    Workloads with an expert budget or live rows go through the _ex entry
-    point with those options.  `outputs`: the routing outputs requested
-    (None = all)."""
+    Workloads with an expert budget or live rows, and calls with fp8
+    activations, go through the _ex entry point with those options.
+    `outputs`: the routing outputs requested (None = all)."""
     import torch
     wl = inp.wl
     dp = dp or cm.upload(inp)
@@ -49,8 +49,8 @@ def run_gpu(inp, tau: float, top_k: int, dp=None, workspace=None, outputs=None):
     odt = torch.bfloat16 if wl.act_dtype == W.BF16 else torch.float32
     out = torch.full((wl.rows, wl.hidden), SENTINEL, dtype=odt, device="cuda")
     opts = None
-    if wl.expert_budget or dp.tensors.get("live_rows") is not None:
-        opts = cm.make_options(wl.expert_budget, dp.tensors.get("live_rows"))
+    if wl.expert_budget or dp.tensors.get("live_rows") is not None or act_fp8:
+        opts = cm.make_options(wl.expert_budget, dp.tensors.get("live_rows"), int(act_fp8))
     cm.clover_moe_block_forward(dp.problem, dp.weights, dp.tensors["x"], tau, top_k, out, rt, ws,
                                 options=opts)
     torch.cuda.synchronize()
@@ -95,16 +95,18 @@ def assert_ffn_close(out, ref, weight_dtype, rows=None):
     return mx, mean
 
 
-def check(inp, tau=None, top_k=None, rows=None, threads=0, dp=None, outputs=None):
+def check(inp, tau=None, top_k=None, rows=None, threads=0, dp=None, outputs=None, act_fp8=False):
     """Full parity check of one call; returns (max_rel, mean_rel, oracle result).
-    `outputs`: the routing outputs the call requests (None = all)."""
+    `outputs`: the routing outputs the call requests (None = all).  With
+    act_fp8 the call runs with MXFP8 activations and its FFN output is held
+    to the fp8-weight bar against the exact oracle."""
     wl = inp.wl
     tau = wl.mass_threshold if tau is None else tau
     top_k = wl.top_k if top_k is None else top_k
     print(f"[parity] {wl.name} B={wl.num_blocks} R={wl.block_rows} H={wl.hidden} E={wl.num_experts} "
-          f"I={wl.inter} Is={wl.shared_inter} {wl.act_dtype}/{wl.weight_dtype} tau={tau} k={top_k}",
-          flush=True)
-    out, gpu = run_gpu(inp, tau, top_k, dp=dp, outputs=outputs)
+          f"I={wl.inter} Is={wl.shared_inter} {wl.act_dtype}/{wl.weight_dtype} tau={tau} k={top_k}"
+          f"{' act_fp8' if act_fp8 else ''}", flush=True)
+    out, gpu = run_gpu(inp, tau, top_k, dp=dp, outputs=outputs, act_fp8=act_fp8)
     ref = oracle.forward(inp, tau=tau, top_k=top_k, rows=rows, threads=threads)
     assert_routing_equal(gpu, ref)
     if inp.live_rows is not None:

@@ -158,11 +158,10 @@ def test_missing_weights_rejected():
     assert call(w=weights(router_b=fake(13, 4))) == cm.CMOE_ERR_ALIGN
 
 
-def call_ex(opts, **kw):
-    prob = problem()
-    k = 8
+def call_ex(opts, prob=None, fp8=False, k=8):
+    prob = prob or problem()
     lib = cm.load_library()
-    return lib.clover_moe_block_forward_ex(ctypes.byref(prob), ctypes.byref(weights()), fake(10),
+    return lib.clover_moe_block_forward_ex(ctypes.byref(prob), ctypes.byref(weights(fp8=fp8)), fake(10),
                                            ctypes.c_float(0.9), k, ctypes.byref(opts), fake(11), None,
                                            fake(12), cm.clover_moe_workspace_size(prob, k), None)
 
@@ -177,6 +176,37 @@ def call_ex(opts, **kw):
 def test_invalid_options_rejected(opts, expect):
     assert call_ex(cm.cmoe_options(opts.get("expert_budget", 0), opts.get("live_rows"))) == expect
     assert cm.clover_moe_last_error()
+
+
+# fp8 activations: a value other than 0/1 is invalid; calls outside the
+# covered shapes are unsupported (checked before any work is queued)
+FP8_MANY = dict(weight_dtype="fp8_e4m3", num_blocks=64)
+
+
+@pytest.mark.parametrize("pkw,fp8,k,act8,expect", [
+    (FP8_MANY, True, 8, 2, cm.CMOE_ERR_VALUE),
+    (FP8_MANY, True, 8, -1, cm.CMOE_ERR_VALUE),
+    (dict(num_blocks=64), False, 8, 1, cm.CMOE_ERR_UNSUPPORTED),                     # bf16 weights
+    (dict(num_blocks=64, weight_dtype="fp4_e2m1"), True, 8, 1, cm.CMOE_ERR_UNSUPPORTED),
+    (dict(weight_dtype="fp8_e4m3"), True, 8, 1, cm.CMOE_ERR_UNSUPPORTED),            # one block: 16-row tiles
+    (dict(FP8_MANY, inter=1024), True, 8, 1, cm.CMOE_ERR_UNSUPPORTED),
+    (dict(FP8_MANY, shared_inter=256), True, 8, 1, cm.CMOE_ERR_UNSUPPORTED),
+    (dict(FP8_MANY, hidden=4096), True, 8, 1, cm.CMOE_ERR_UNSUPPORTED),
+    (dict(FP8_MANY, hidden=768), True, 8, 1, cm.CMOE_ERR_UNSUPPORTED),
+])
+def test_activation_fp8_rejected(pkw, fp8, k, act8, expect):
+    opts = cm.make_options(activation_fp8=act8)
+    assert call_ex(opts, prob=problem(**pkw), fp8=fp8, k=k) == expect
+    assert "activation_fp8" in cm.clover_moe_last_error()
+
+
+def test_activation_fp8_workspace_holds_the_codes():
+    # fp8 weights with tall tiles reserve N*H codes and N*H/32 scale bytes
+    p8 = problem(**FP8_MANY)
+    pb = problem(num_blocks=64)
+    n, h = 64 * 32, 2048
+    extra = cm.clover_moe_workspace_size(p8, 8) - cm.clover_moe_workspace_size(pb, 8)
+    assert n * h + n * h // 32 <= extra < n * h + n * h // 32 + 256
 
 
 def test_routing_outputs_checked_for_alias_and_alignment():
