@@ -227,6 +227,148 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
   }
 }
 
+// ---------------------------------------------------------------------------
+// Many rows: the same chains on the matrix cores.  v_mfma_f32_32x32x1_2b_f32
+// has depth 1: each step adds one product to each of its 2 x 32 x 32 fp32
+// accumulators, and on gfx950 that step rounds exactly as an fp32 fma does
+// (checked bit for bit against v_fma_f32 chains, with operands of ordinary
+// and of denormal-range magnitude).  A chain of these MFMAs over ascending h
+// is therefore the chunk's fma chain itself, for 2048 (row, expert, chunk)
+// chains at once.
+//
+// A workgroup of 8 waves owns 64 rows x 32 experts.  Wave w takes the row
+// block w / 4 and the chunk pair (w % 4, w % 4 + 4), one chunk per MFMA
+// block: lane l supplies x[row l % 32] and Wr[expert l % 32] of chunk
+// w % 4 + 4 (l / 32).  Output register v of lane l is block v / 16, row
+// 8 ((v % 16) / 4) + 4 (l / 32) + v % 4, expert l % 32 (checked on gfx950),
+// so lane l adds its chunk pair (p_c + p_{c+4}, the tree's first level) in
+// registers; the other two levels run after an exchange through LDS.
+//
+// Operands are staged through LDS P positions of every chunk at a time
+// (coalesced 16-byte loads through registers, double-buffered: the loads of
+// stage s+1 are in flight while stage s feeds the MFMAs).  Read from global
+// memory lane by lane instead, every load touches 64 different cache lines,
+// and the per-CU fetch rate, not the matrix cores, sets the pace.  x keeps
+// its storage type in LDS; rows are padded to 16 bytes past a multiple of
+// 256, so the 32 rows a half-wave reads fall in distinct bank groups.
+// ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(32))) float f32x32;
+
+template <typename XT, int P>
+struct RouterStage {
+  static constexpr int kXRow = 8 * P * (int)sizeof(XT) + 16;   // bytes per staged x row (8 chunks)
+  static constexpr int kWRow = 8 * P * 4 + 16;                 // bytes per staged Wr row
+  static constexpr int kBytes = 64 * kXRow + 32 * kWRow;       // one buffer
+  static constexpr int kXV = P * (int)sizeof(XT) / 16;          // 16-byte vectors per row and chunk
+  static constexpr int kWV = P * 4 / 16;
+  static constexpr int kNX = 64 * 8 * kXV, kNW = 32 * 8 * kWV;  // vectors per stage
+  static constexpr int kVPT = (kNX + kNW) / 512;                // per thread
+  static_assert(kNX % 512 == 0 && kNW % 512 == 0, "whole rounds of 512 vectors");
+  static_assert(2 * kBytes <= 160 * 1024 && 2 * kBytes >= 4 * 64 * 33 * 4, "LDS budget");
+};
+
+template <typename XT, int P>
+__global__ __launch_bounds__(512) void router_mfma_kernel(const XT* __restrict__ x, const float* __restrict__ w,
+                                                          const float* __restrict__ bias,
+                                                          float* __restrict__ logits, int N, int H, int E) {
+  using RS = RouterStage<XT, P>;
+  constexpr int XN = XVec<XT>::kN;   // x values per 16-byte vector
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * RS::kBytes];
+  auto part = reinterpret_cast<float(*)[64][33]>(smem);  // after the chains: s_c = p_c + p_{c+4}
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rb = wave >> 2, cp = wave & 3;
+  const int blk = lane >> 5, i = lane & 31;
+  const int row0 = blockIdx.x * 64, e0 = blockIdx.y * 32;
+  const int L = H / 8, NS = L / P;   // chunk length and its stages
+  const int c = cp + 4 * blk;        // this lane's chunk
+
+  // staging: vector v = tid + 512 t; the first kNX are x (row, chunk, piece),
+  // the rest Wr.  Rows past N and experts past E read the last valid one
+  // (their results are not stored).
+  u32x4 reg[RS::kVPT];
+  auto gload = [&](int st) {
+#pragma unroll
+    for (int t = 0; t < RS::kVPT; ++t) {
+      const int v = tid + 512 * t;
+      if (t < RS::kNX / 512) {
+        const int k = v % RS::kXV, rc = v / RS::kXV, cc = rc & 7, r = rc >> 3;
+        const int row = min(row0 + r, N - 1);
+        reg[t] = *reinterpret_cast<const u32x4*>(x + (size_t)row * H + (size_t)cc * L + st * P + k * XN);
+      } else {
+        const int vw = v - RS::kNX;
+        const int k = vw % RS::kWV, ec = vw / RS::kWV, cc = ec & 7, e = ec >> 3;
+        const int ex = min(e0 + e, E - 1);
+        reg[t] = *reinterpret_cast<const u32x4*>(w + (size_t)ex * H + (size_t)cc * L + st * P + k * 4);
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+    uint8_t* base = smem + buf * RS::kBytes;
+#pragma unroll
+    for (int t = 0; t < RS::kVPT; ++t) {
+      const int v = tid + 512 * t;
+      if (t < RS::kNX / 512) {
+        const int k = v % RS::kXV, rc = v / RS::kXV, cc = rc & 7, r = rc >> 3;
+        *reinterpret_cast<u32x4*>(base + r * RS::kXRow + (cc * RS::kXV + k) * 16) = reg[t];
+      } else {
+        const int vw = v - RS::kNX;
+        const int k = vw % RS::kWV, ec = vw / RS::kWV, cc = ec & 7, e = ec >> 3;
+        *reinterpret_cast<u32x4*>(base + 64 * RS::kXRow + e * RS::kWRow + (cc * RS::kWV + k) * 16) = reg[t];
+      }
+    }
+  };
+
+  f32x32 acc = f32x32{};
+  // this lane's operands inside a staged buffer: its row's and its expert's chunk c
+  const int xoff = (32 * rb + i) * RS::kXRow + c * P * (int)sizeof(XT);
+  const int woff = 64 * RS::kXRow + i * RS::kWRow + c * P * 4;
+  auto compute = [&](int buf) {
+    const uint8_t* base = smem + buf * RS::kBytes;
+#pragma unroll
+    for (int p = 0; p < P; p += 8) {
+      float xv[8];
+#pragma unroll
+      for (int j = 0; j < 8 / XN; ++j)
+        XVec<XT>::widen(*reinterpret_cast<const u32x4*>(base + xoff + (p + j * XN) * (int)sizeof(XT)), xv + j * XN);
+      const u32x4 w0 = *reinterpret_cast<const u32x4*>(base + woff + p * 4);
+      const u32x4 w1 = *reinterpret_cast<const u32x4*>(base + woff + p * 4 + 16);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(xv[k], __uint_as_float(k < 4 ? w0[k] : w1[k - 4]), acc, 0, 0,
+                                                   0);
+    }
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int st = 0; st < NS; ++st) {
+    if (st + 1 < NS) gload(st + 1);
+    // (keeps the next stage's loads above the MFMAs: sunk to their stores,
+    // each stage would wait a full memory round trip)
+    __builtin_amdgcn_sched_barrier(0);
+    compute(st & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (st + 1 < NS) lstore((st + 1) & 1);
+    __syncthreads();
+  }
+  // first tree level in registers, then the exchange (over the staging buffers)
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int r = 32 * rb + 8 * (v >> 2) + 4 * blk + (v & 3);
+    part[cp][r][i] = acc[v] + acc[v + 16];
+  }
+  __syncthreads();
+  for (int o = tid; o < 64 * 32; o += 512) {
+    const int r = o >> 5, e = o & 31;
+    const int rr = row0 + r, ee = e0 + e;
+    if (rr >= N || ee >= E) continue;
+    float l = (part[0][r][e] + part[2][r][e]) + (part[1][r][e] + part[3][r][e]);
+    if (bias) l = l + bias[ee];
+    logits[(size_t)rr * E + ee] = l;
+  }
+}
+
 // Workgroups are dispatched to the 8 XCDs round-robin by linear id, and each
 // XCD has its own L2.  emajor puts the expert slices along x: the row groups
 // of one slice then have ids a multiple of the slice count apart, which is a
@@ -247,6 +389,21 @@ static void launch_shape(const Plan& p, const void* x, const float* w, const flo
         static_cast<const float*>(x), w, b, p.logits, p.N, p.H, p.E, emajor);
 }
 
+template <typename XT>
+static void launch_mfma(const Plan& p, const void* x, const float* w, const float* b, hipStream_t s) {
+  const dim3 grid((p.N + 63) / 64, (p.E + 31) / 32);
+  const XT* xt = static_cast<const XT*>(x);
+  // 32 positions per stage where the chunk length allows it and the buffers
+  // fit (bf16 x); else 16 (H/8 is a multiple of 16)
+  if constexpr (sizeof(XT) == 2) {
+    if ((p.H / 8) % 32 == 0) {
+      router_mfma_kernel<XT, 32><<<grid, 512, 0, s>>>(xt, w, b, p.logits, p.N, p.H, p.E);
+      return;
+    }
+  }
+  router_mfma_kernel<XT, 16><<<grid, 512, 0, s>>>(xt, w, b, p.logits, p.N, p.H, p.E);
+}
+
 hipError_t launch_router(const Plan& p, const void* x, const float* router_w,
                          const float* router_b, hipStream_t s) {
   // chunk length H/8 is a multiple of 16 (H is a multiple of 128)
@@ -260,9 +417,12 @@ hipError_t launch_router(const Plan& p, const void* x, const float* router_w,
     else if (L % 32 == 0) launch_shape<1, 1, 32>(p, x, router_w, router_b, true, s);
     else launch_shape<1, 1, 16>(p, x, router_w, router_b, true, s);
   } else {
-    // many rows: 4x4 register tiles, 16-position slices (about 60 KiB of
-    // LDS, so two workgroups share a CU)
-    launch_shape<4, 4, 16>(p, x, router_w, router_b, false, s);
+    // many rows: the matrix-core chains.  Row tiles along x: the expert
+    // tiles of one row tile have linear ids a multiple of the row-tile count
+    // apart, so with a multiple of 8 row tiles they share an XCD and x is
+    // fetched by one XCD only; Wr (2 MB at E = 256) is fetched by all
+    if (p.act == CMOE_BF16) launch_mfma<uint16_t>(p, x, router_w, router_b, s);
+    else launch_mfma<float>(p, x, router_w, router_b, s);
   }
   return hipGetLastError();
 }

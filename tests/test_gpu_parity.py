@@ -128,6 +128,20 @@ def test_resident_down_shapes(wl, layout):
         assert ref["expert_counts"].max() > 96   # an expert spans several tiles
 
 
+# more than 256 rows: the router's matrix-core chains (bit-exact logits),
+# across row and expert counts that leave partial tiles, hidden sizes with an
+# unrolled chain (512 .. 4096) or the general loop (384), and fp32 activations
+@pytest.mark.parametrize("wl", [
+    W.Workload("router_n300_e20_h384", 75, 4, 384, 20, 4, 128, 128, W.BF16, W.BF16, 0.9, seed=161),
+    W.Workload("router_n320_e40_h512_f32", 10, 32, 512, 40, 4, 128, 0, W.F32, W.F32, 0.9, seed=162),
+    W.Workload("router_n1024_e256_h1024", 32, 32, 1024, 256, 8, 128, 128, W.BF16, W.BF16, 0.9, seed=163),
+    W.Workload("router_n384_e64_h4096", 12, 32, 4096, 64, 8, 128, 128, W.BF16, W.BF16, 0.95, seed=164),
+    W.Workload("router_n264_e33_h640", 33, 8, 640, 33, 3, 128, 128, W.BF16, W.FP8, 0.8, seed=165),
+], ids=lambda w: w.name)
+def test_router_many_rows(wl):
+    check(W.generate(wl), threads=16)
+
+
 # 4-bit experts (MXFP4: E2M1 codes, E8M0 scale per 32 elements), widened to
 # bf16 exactly in both kernel families
 @pytest.mark.parametrize("wl", [
