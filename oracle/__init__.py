@@ -86,6 +86,16 @@ def lib():
         L.orc_forward_ex.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
                                      ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        L.orc_forward_ex_act8.restype = ctypes.c_int
+        L.orc_forward_ex_act8.argtypes = L.orc_forward_ex.argtypes
+        L.orc_round_bf16.restype = ctypes.c_double
+        L.orc_round_bf16.argtypes = [ctypes.c_double]
+        L.orc_e4m3_encode.restype = ctypes.c_uint8
+        L.orc_e4m3_encode.argtypes = [ctypes.c_double]
+        L.orc_mx8_scale_exp.restype = ctypes.c_int
+        L.orc_mx8_scale_exp.argtypes = [ctypes.c_double]
+        L.orc_mx8_round.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+        L.orc_expert_ffn_mx8.argtypes = L.orc_expert_ffn.argtypes
         _lib = L
     return _lib
 
@@ -144,6 +154,29 @@ def e8m0_to_double(s: int) -> float:
     return lib().orc_e8m0_to_double(int(s))
 
 
+# fp8 activations (the library's opt-in W8A8 mode, see clover_moe_oracle.h)
+
+def round_bf16(v: float) -> float:
+    return lib().orc_round_bf16(float(v))
+
+
+def e4m3_encode(v: float) -> int:
+    return int(lib().orc_e4m3_encode(float(v)))
+
+
+def mx8_scale_exp(amax: float) -> int:
+    return int(lib().orc_mx8_scale_exp(float(amax)))
+
+
+def mx8_round(v: np.ndarray) -> np.ndarray:
+    """Rows of 32-element groups rounded to MXFP8 and back (fp64)."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    assert v.size % 32 == 0
+    out = np.empty_like(v)
+    lib().orc_mx8_round(_ptr(v), v.size, _ptr(out))
+    return out
+
+
 # --------------------------------------------------------------------------
 # stages
 # --------------------------------------------------------------------------
@@ -199,24 +232,28 @@ def row_topk(logits_row, u_row, in_set, top_k: int):
 
 
 def expert_ffn(hidden: int, inter: int, wdtype: str, w13, w13_scale, w2, w2_scale,
-               xrow: np.ndarray) -> np.ndarray:
+               xrow: np.ndarray, act_fp8: bool = False) -> np.ndarray:
+    """One expert on one row; with act_fp8, xrow must already be MXFP8-rounded
+    (mx8_round) and h is rounded to bf16 and MXFP8 inside."""
     w13 = np.ascontiguousarray(w13)
     w2 = np.ascontiguousarray(w2)
     xrow = np.ascontiguousarray(xrow, dtype=np.float64)
     y = np.zeros(hidden, dtype=np.float64)
-    lib().orc_expert_ffn(hidden, inter, _DT[wdtype], _ptr(w13), _ptr(w13_scale), _ptr(w2),
-                         _ptr(w2_scale), _ptr(xrow), _ptr(y))
+    fn = lib().orc_expert_ffn_mx8 if act_fp8 else lib().orc_expert_ffn
+    fn(hidden, inter, _DT[wdtype], _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), _ptr(xrow), _ptr(y))
     return y
 
 
 def forward(inp, tau: Optional[float] = None, top_k: Optional[int] = None,
             rows: Optional[np.ndarray] = None, threads: int = 0, ffn: bool = True,
-            expert_budget: Optional[int] = None, live_rows: Optional[np.ndarray] = None) -> dict:
+            expert_budget: Optional[int] = None, live_rows: Optional[np.ndarray] = None,
+            act_fp8: bool = False) -> dict:
     """Whole call.  ``rows``: row indices whose FFN output is computed (None =
     all).  ``expert_budget`` and ``live_rows`` default to the workload's
-    (``inp.wl.expert_budget``, ``inp.live_rows``).  Returns a dict with 'out'
-    (fp64 [N,H], NaN for rows not computed and for resolved rows) and every
-    routing array."""
+    (``inp.wl.expert_budget``, ``inp.live_rows``).  ``act_fp8``: MXFP8
+    activations into the expert GEMMs (fp8 weights only).  Returns a dict with
+    'out' (fp64 [N,H], NaN for rows not computed and for resolved rows) and
+    every routing array."""
     wl = inp.wl
     tau = wl.mass_threshold if tau is None else tau
     K = wl.top_k if top_k is None else top_k
@@ -244,9 +281,9 @@ def forward(inp, tau: Optional[float] = None, top_k: Optional[int] = None,
             mask[np.asarray(rows)] = 1
     p = _problem(inp)
     w = _weights(inp)
-    rc = lib().orc_forward_ex(ctypes.byref(p), ctypes.byref(w), _ptr(inp.x), ctypes.c_float(tau), K,
-                              int(budget), _ptr(live), _ptr(out), ctypes.byref(rt), _ptr(mask),
-                              threads)
+    fn = lib().orc_forward_ex_act8 if act_fp8 else lib().orc_forward_ex
+    rc = fn(ctypes.byref(p), ctypes.byref(w), _ptr(inp.x), ctypes.c_float(tau), K, int(budget), _ptr(live),
+            _ptr(out), ctypes.byref(rt), _ptr(mask), threads)
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (code {rc})")
     res["out"] = out

@@ -125,6 +125,67 @@ double orc_e8m0_to_double(uint8_t s)
     return s == 255 ? NAN : ldexp(1.0, (int)s - 127);
 }
 
+/* ------------------------------------------------------------------------ */
+/* fp8 activations (the library's opt-in W8A8 mode; not a step of the pages: */
+/* their fp8 experts run with bf16 activations, InfiniLM PR #584,            */
+/* "Benchmark").  Activations enter each expert GEMM as MXFP8, the layout of  */
+/* the OCP Microscaling (MX) format: E4M3 elements with one E8M0 power-of-two */
+/* scale per 32 consecutive elements of a row.  The scale of a group is the   */
+/* smallest 2^e that keeps its largest magnitude within 448 (the largest     */
+/* E4M3 value), so no element saturates; each element is v / 2^e rounded to  */
+/* the nearest E4M3 value, ties to the even code.  x is bf16 already; h is    */
+/* held in bf16 (round to nearest even) before it is rounded to MXFP8.        */
+/* ------------------------------------------------------------------------ */
+
+/* v rounded to bf16 (8 significant bits, round to nearest, ties to even) */
+double orc_round_bf16(double v)
+{
+    if (v == 0.0 || isnan(v) || isinf(v)) return v;
+    int ex;
+    frexp(v, &ex);                            /* |v| = f * 2^ex, f in [0.5, 1) */
+    double q = ldexp(v, 8 - ex);              /* 8 significant bits left of the point */
+    double r = nearbyint(q);                  /* default rounding: to nearest, ties to even */
+    return ldexp(r, ex - 8);
+}
+
+/* The E4M3 code nearest to v (ties to the even code), by comparing v with
+ * every finite non-negative code value; the sign bit is v's. */
+uint8_t orc_e4m3_encode(double v)
+{
+    double a = fabs(v);
+    int best = 0;
+    double bd = INFINITY;
+    for (int c = 0; c <= 0x7E; ++c) {
+        double d = fabs(orc_e4m3_to_double((uint8_t)c) - a);
+        if (d < bd || (d == bd && (c & 1) == 0)) {
+            bd = d;
+            best = c;
+        }
+    }
+    return (uint8_t)(best | (signbit(v) ? 0x80 : 0x00));
+}
+
+/* the scale exponent of a group whose largest magnitude is amax: the
+ * smallest e in [-127, 127] with amax <= 448 * 2^e (-127 for amax 0) */
+int orc_mx8_scale_exp(double amax)
+{
+    for (int e = -127; e <= 127; ++e)
+        if (amax <= ldexp(448.0, e)) return e;
+    return 127;
+}
+
+/* out[0..n) = v rounded to MXFP8 and back (n a multiple of 32) */
+void orc_mx8_round(const double* v, int n, double* out)
+{
+    for (int g = 0; g < n; g += 32) {
+        double amax = 0.0;
+        for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(v[g + i]));
+        int e = orc_mx8_scale_exp(amax);
+        for (int i = 0; i < 32; ++i)
+            out[g + i] = ldexp(orc_e4m3_to_double(orc_e4m3_encode(ldexp(v[g + i], -e))), e);
+    }
+}
+
 static double act_value(int dtype, const void* x, size_t i)
 {
     if (dtype == ORC_BF16) return orc_bf16_to_double(((const uint16_t*)x)[i]);
@@ -352,6 +413,38 @@ void orc_expert_ffn(int hidden, int inter, int wdtype, const void* w13, const vo
     free(h);
 }
 
+/* orc_expert_ffn with fp8 activations: xq is the input row already rounded
+ * to MXFP8; h is rounded to bf16 and then to MXFP8 before the down GEMM. */
+void orc_expert_ffn_mx8(int hidden, int inter, int wdtype, const void* w13, const void* w13_scale,
+                        const void* w2, const void* w2_scale, const double* xq, double* y)
+{
+    double* wrow = (double*)malloc(sizeof(double) * (size_t)(hidden > inter ? hidden : inter));
+    double* z = (double*)malloc(sizeof(double) * 2 * (size_t)inter);
+    double* h = (double*)malloc(sizeof(double) * (size_t)inter);
+    double* hq = (double*)malloc(sizeof(double) * (size_t)inter);
+    for (int i = 0; i < 2 * inter; ++i) {
+        widen_weight_row(wdtype, w13, w13_scale, hidden, i, wrow);
+        double acc = 0.0;
+        for (int c = 0; c < hidden; ++c) acc += wrow[c] * xq[c];
+        z[i] = acc;
+    }
+    for (int i = 0; i < inter; ++i) {
+        double a = z[i], v = z[inter + i];
+        h[i] = orc_round_bf16(a * (1.0 / (1.0 + exp(-a))) * v);
+    }
+    orc_mx8_round(h, inter, hq);
+    for (int o = 0; o < hidden; ++o) {
+        widen_weight_row(wdtype, w2, w2_scale, inter, o, wrow);
+        double acc = 0.0;
+        for (int i = 0; i < inter; ++i) acc += wrow[i] * hq[i];
+        y[o] = acc;
+    }
+    free(wrow);
+    free(z);
+    free(h);
+    free(hq);
+}
+
 /* bytes of a [rows, cols] weight matrix, and of its scales, in `dtype` storage */
 static size_t matrix_bytes(int dtype, size_t rows, size_t cols)
 {
@@ -381,9 +474,31 @@ int orc_forward(const orc_problem* p, const orc_weights* w, const void* x,
     return orc_forward_ex(p, w, x, tau, top_k, 0, NULL, out, rt, row_mask, threads);
 }
 
+static int forward_common(const orc_problem* p, const orc_weights* w, const void* x,
+                          float tau, int top_k, int expert_budget, const uint8_t* live,
+                          double* out, orc_routing* rt, const uint8_t* row_mask, int threads,
+                          int act_fp8);
+
 int orc_forward_ex(const orc_problem* p, const orc_weights* w, const void* x,
                    float tau, int top_k, int expert_budget, const uint8_t* live,
                    double* out, orc_routing* rt, const uint8_t* row_mask, int threads)
+{
+    return forward_common(p, w, x, tau, top_k, expert_budget, live, out, rt, row_mask, threads, 0);
+}
+
+int orc_forward_ex_act8(const orc_problem* p, const orc_weights* w, const void* x,
+                        float tau, int top_k, int expert_budget, const uint8_t* live,
+                        double* out, orc_routing* rt, const uint8_t* row_mask, int threads)
+{
+    if (p->weight_dtype != ORC_FP8_E4M3 || p->act_dtype != ORC_BF16) return 6;
+    if (p->hidden % 32 || p->inter % 32 || p->shared_inter % 32) return 6;
+    return forward_common(p, w, x, tau, top_k, expert_budget, live, out, rt, row_mask, threads, 1);
+}
+
+static int forward_common(const orc_problem* p, const orc_weights* w, const void* x,
+                          float tau, int top_k, int expert_budget, const uint8_t* live,
+                          double* out, orc_routing* rt, const uint8_t* row_mask, int threads,
+                          int act_fp8)
 {
     const int H = p->hidden, E = p->num_experts, I = p->inter, Is = p->shared_inter;
     const int R = p->block_rows, B = p->num_blocks, N = R * B, K = top_k;
@@ -485,10 +600,15 @@ int orc_forward_ex(const orc_problem* p, const orc_weights* w, const void* x,
             double* y = (double*)malloc(sizeof(double) * (size_t)H);
             double* acc = out + (size_t)r * H;
             for (int c = 0; c < H; ++c) xr[c] = act_value(p->act_dtype, x, (size_t)r * H + c);
+            if (act_fp8) orc_mx8_round(xr, H, xr);  /* in place: each group is read before written */
             for (int c = 0; c < H; ++c) acc[c] = 0.0;
             if (Is > 0 && w->shared_w13 && w->shared_w2) {
-                orc_expert_ffn(H, Is, p->weight_dtype, w->shared_w13, w->shared_w13_scale,
-                               w->shared_w2, w->shared_w2_scale, xr, y);
+                if (act_fp8)
+                    orc_expert_ffn_mx8(H, Is, p->weight_dtype, w->shared_w13, w->shared_w13_scale,
+                                       w->shared_w2, w->shared_w2_scale, xr, y);
+                else
+                    orc_expert_ffn(H, Is, p->weight_dtype, w->shared_w13, w->shared_w13_scale,
+                                   w->shared_w2, w->shared_w2_scale, xr, y);
                 for (int c = 0; c < H; ++c) acc[c] += y[c];
             }
             for (int j = 0; j < K; ++j) {
@@ -498,7 +618,8 @@ int orc_forward_ex(const orc_problem* p, const orc_weights* w, const void* x,
                 const char* w2e = (const char*)w->w2 + (size_t)e * w2_b;
                 const char* s13 = w13_sb ? (const char*)w->w13_scale + (size_t)e * w13_sb : NULL;
                 const char* s2 = w2_sb ? (const char*)w->w2_scale + (size_t)e * w2_sb : NULL;
-                orc_expert_ffn(H, I, wd, w13e, s13, w2e, s2, xr, y);
+                if (act_fp8) orc_expert_ffn_mx8(H, I, wd, w13e, s13, w2e, s2, xr, y);
+                else orc_expert_ffn(H, I, wd, w13e, s13, w2e, s2, xr, y);
                 double g = (double)gates[(size_t)r * K + j];
                 for (int c = 0; c < H; ++c) acc[c] += g * y[c];
             }

@@ -83,6 +83,17 @@ double orc_e4m3_to_double(uint8_t code);
 double orc_e2m1_to_double(uint8_t code);   /* low 4 bits */
 double orc_e8m0_to_double(uint8_t s);      /* 2^(s-127); s = 255 is NaN */
 
+/* ---- fp8 activations (the library's opt-in W8A8 mode) ----
+ * Not a step of the pages (their fp8 experts take bf16 activations,
+ * InfiniLM PR #584, "Benchmark").  MXFP8 is the OCP Microscaling layout:
+ * E4M3 elements, one E8M0 power-of-two scale per 32 consecutive elements of
+ * a row; here the scale is the smallest 2^e with max|v| <= 448 * 2^e (no
+ * element saturates) and elements round to nearest, ties to the even code. */
+double orc_round_bf16(double v);            /* to bf16, nearest, ties to even */
+uint8_t orc_e4m3_encode(double v);          /* nearest E4M3 code, ties to even */
+int orc_mx8_scale_exp(double amax);         /* smallest e in [-127,127], amax <= 448*2^e */
+void orc_mx8_round(const double* v, int n, double* out);  /* n % 32 == 0; out may be v */
+
 /* ---- routing stages ---- */
 
 /* logits[N,E] (fp32) under the chunked fp32 summation contract. */
@@ -140,6 +151,19 @@ int orc_forward(const orc_problem* p, const orc_weights* w, const void* x,
 int orc_forward_ex(const orc_problem* p, const orc_weights* w, const void* x,
                    float tau, int top_k, int expert_budget, const uint8_t* live_rows,
                    double* out, orc_routing* routing, const uint8_t* row_mask, int threads);
+
+/* orc_forward_ex with fp8 activations: every row of x is rounded to MXFP8
+ * before the expert GEMMs, and each expert's h is rounded to bf16 and then
+ * to MXFP8 before its down GEMM (orc_expert_ffn_mx8).  Routing is unchanged.
+ * fp8 weights with bf16 x only (else returns 6). */
+int orc_forward_ex_act8(const orc_problem* p, const orc_weights* w, const void* x,
+                        float tau, int top_k, int expert_budget, const uint8_t* live_rows,
+                        double* out, orc_routing* routing, const uint8_t* row_mask, int threads);
+
+/* fp64 SwiGLU FFN of one expert with fp8 activations: xq[H] already MXFP8;
+ * h rounded to bf16, then to MXFP8, before W2. */
+void orc_expert_ffn_mx8(int hidden, int inter, int wdtype, const void* w13, const void* w13_scale,
+                        const void* w2, const void* w2_scale, const double* xq, double* y);
 
 /* fp64 SwiGLU FFN of one expert weight set on one input row (widened to fp64):
  * y[H] = W2 * (silu(W13[0:I] x) * (W13[I:2I] x)).  wdtype as in orc_problem. */

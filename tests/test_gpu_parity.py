@@ -128,15 +128,16 @@ def test_resident_down_shapes(wl, layout):
         assert ref["expert_counts"].max() > 96   # an expert spans several tiles
 
 
-# more than 256 rows: the router's matrix-core chains (bit-exact logits),
-# across row and expert counts that leave partial tiles, hidden sizes with an
-# unrolled chain (512 .. 4096) or the general loop (384), and fp32 activations
+# many rows (grids of 128 or more 64 x 32 tiles): the router's matrix-core
+# chains (bit-exact logits), across row and expert counts that leave partial
+# tiles, hidden sizes with 32-position stages (512 .. 4096) or 16-position
+# ones (384, 640), and fp32 activations
 @pytest.mark.parametrize("wl", [
-    W.Workload("router_n300_e20_h384", 75, 4, 384, 20, 4, 128, 128, W.BF16, W.BF16, 0.9, seed=161),
-    W.Workload("router_n320_e40_h512_f32", 10, 32, 512, 40, 4, 128, 0, W.F32, W.F32, 0.9, seed=162),
+    W.Workload("router_n2080_e100_h384", 65, 32, 384, 100, 4, 128, 128, W.BF16, W.BF16, 0.9, seed=161),
+    W.Workload("router_n2048_e128_h512_f32", 64, 32, 512, 128, 4, 128, 0, W.F32, W.F32, 0.9, seed=162),
     W.Workload("router_n1024_e256_h1024", 32, 32, 1024, 256, 8, 128, 128, W.BF16, W.BF16, 0.9, seed=163),
-    W.Workload("router_n384_e64_h4096", 12, 32, 4096, 64, 8, 128, 128, W.BF16, W.BF16, 0.95, seed=164),
-    W.Workload("router_n264_e33_h640", 33, 8, 640, 33, 3, 128, 128, W.BF16, W.FP8, 0.8, seed=165),
+    W.Workload("router_n1536_e192_h4096", 48, 32, 4096, 192, 8, 128, 128, W.BF16, W.BF16, 0.95, seed=164),
+    W.Workload("router_n2112_e130_h640", 264, 8, 640, 130, 3, 128, 128, W.BF16, W.FP8, 0.8, seed=165),
 ], ids=lambda w: w.name)
 def test_router_many_rows(wl):
     check(W.generate(wl), threads=16)

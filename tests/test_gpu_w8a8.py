@@ -1,7 +1,9 @@
 """GPU parity of the opt-in fp8-activation path (cmoe_options.activation_fp8:
-MXFP8 activations into the fp8-weight expert GEMMs) against the exact oracle,
-held to the fp8-weight bar (max|d| <= 6e-2 max|ref|).  Routing is unchanged
-by the option and stays bit-exact."""
+MXFP8 activations into the fp8-weight expert GEMMs).  Each call is held to
+the oracle's fp8-activation reading at the bf16 bar (max|d| <= 2e-2
+max|ref|, sum|d| <= 5e-3 sum|ref|) and to the exact oracle at the fp8-weight bar (max|d| <= 6e-2
+max|ref|); see tests/parity.py.  Routing is unchanged by the option and
+stays bit-exact."""
 import pytest
 
 import sparse_moe_ffn_softmax_amd as cm

@@ -647,3 +647,156 @@ def test_block_without_live_rows_has_an_empty_coreset():
     assert r["coreset_size"][0] == 0 and np.all(r["coreset_ids"][0] == -1)
     assert np.all(r["block_mass"][0] == 0) and r["coreset_size"][1] > 0
     assert np.all(r["topk_idx"][: wl.block_rows] == -1)
+
+
+# ----------------------------------------------------------------------------
+# fp8 activations (the library's opt-in W8A8 mode): MXFP8 rounding, bf16
+# rounding of h, and the FFN that uses them
+# ----------------------------------------------------------------------------
+
+def _e4m3_values():
+    codes = np.arange(0x7F, dtype=np.uint8)                      # finite non-negative codes
+    return codes, torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+
+
+def test_e4m3_encode_round_trips_every_code():
+    for c in list(range(0x7F)) + list(range(0x80, 0xFF)):
+        v = oracle.e4m3_to_double(c)
+        assert oracle.e4m3_encode(v) == c, (hex(c), v)
+
+
+def test_e4m3_encode_midpoints_go_to_the_even_code():
+    codes, vals = _e4m3_values()
+    for c in range(0x7E):
+        mid = (vals[c] + vals[c + 1]) / 2       # exact in fp64
+        even = c if c % 2 == 0 else c + 1
+        assert oracle.e4m3_encode(mid) == even, (hex(c), mid)
+        assert oracle.e4m3_encode(-mid) == even | 0x80
+    # hand-derived: 1.0625 lies halfway between 1.0 (0x38) and 1.125 (0x39)
+    assert oracle.e4m3_encode(1.0625) == 0x38
+    assert oracle.e4m3_encode(1.1875) == 0x3A
+    assert oracle.e4m3_encode(2.0 ** -10) == 0x00   # half the smallest subnormal: to 0
+    assert oracle.e4m3_encode(3 * 2.0 ** -10) == 0x02
+
+
+def test_e4m3_encode_matches_torch_cast():
+    """torch's float8_e4m3fn cast rounds to nearest even within range."""
+    rng = np.random.default_rng(7)
+    v = np.concatenate([rng.uniform(-448, 448, 3000), rng.normal(0, 1, 3000) * 2.0 ** rng.integers(-12, 8, 3000)])
+    v = v.astype(np.float32)
+    v = v[np.abs(v) <= 448]
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_encode(float(a)) for a in v], dtype=np.uint8)
+    bad = np.flatnonzero((got != ref) & ~((v == 0) & ((got & 0x7F) == 0)))
+    assert bad.size == 0, (v[bad[:5]], got[bad[:5]], ref[bad[:5]])
+
+
+def test_mx8_scale_exponent_is_the_smallest_in_range():
+    rng = np.random.default_rng(8)
+    cases = [0.0, 448.0, 224.0, 1.0, 2.0 ** -130, 3.0e38]
+    for k in range(-20, 21, 5):
+        a = 448.0 * 2.0 ** k
+        cases += [a, np.nextafter(a, np.inf), np.nextafter(a, 0.0)]
+    cases += list(np.abs(rng.normal(0, 1, 500)) * 2.0 ** rng.integers(-30, 30, 500))
+    for a in cases:
+        e = oracle.mx8_scale_exp(a)
+        assert -127 <= e <= 127
+        assert a <= 448.0 * 2.0 ** e or e == 127
+        assert e == -127 or a > 448.0 * 2.0 ** (e - 1), (a, e)
+    assert oracle.mx8_scale_exp(0.0) == -127
+    assert oracle.mx8_scale_exp(448.0) == 0 and oracle.mx8_scale_exp(np.nextafter(448.0, 1e9)) == 1
+
+
+def test_mx8_round_keeps_representable_groups_and_bounds_the_error():
+    codes, vals = _e4m3_values()
+    rng = np.random.default_rng(9)
+    for k in (-9, 0, 5):
+        g = rng.choice(vals, 32) * np.where(rng.random(32) < 0.5, -1, 1)
+        g[3] = 448.0                                 # the group's largest magnitude is 448
+        g = g * 2.0 ** k
+        np.testing.assert_array_equal(oracle.mx8_round(g), g)
+    # elsewhere each element is within half an E4M3 step of v (relative
+    # 2^-4 for normal elements, 2^-10 * 2^e absolute below them)
+    v = rng.normal(0, 0.05, (64, 96))
+    q = oracle.mx8_round(v)
+    for r in range(64):
+        for g0 in range(0, 96, 32):
+            grp, qg = v[r, g0:g0 + 32], q[r, g0:g0 + 32]
+            e = oracle.mx8_scale_exp(np.abs(grp).max())
+            assert np.all(np.abs(qg - grp) <= np.maximum(np.abs(grp) * 2.0 ** -4, 2.0 ** (e - 10)) * (1 + 1e-15))
+            assert np.abs(qg).max() <= 448.0 * 2.0 ** e
+
+
+def _bf16_round_bits(v):
+    """bf16 rounding of fp64 values by integer arithmetic on their bits (round
+    to nearest even at 7 fraction bits)."""
+    b = np.ascontiguousarray(v, dtype=np.float64).view(np.uint64)
+    lsb = (b >> np.uint64(45)) & np.uint64(1)
+    r = (b + np.uint64((1 << 44) - 1) + lsb) & ~np.uint64((1 << 45) - 1)
+    return r.view(np.float64)
+
+
+def test_round_bf16_matches_bit_rounding_and_torch():
+    rng = np.random.default_rng(10)
+    v = rng.normal(0, 1, 4000) * 2.0 ** rng.integers(-40, 40, 4000)
+    ties = (1.0 + (2 * rng.integers(0, 128, 200) + 1) * 2.0 ** -8) * 2.0 ** rng.integers(-5, 5, 200)
+    allv = np.concatenate([v, ties, -ties])
+    got = np.array([oracle.round_bf16(a) for a in allv])
+    np.testing.assert_array_equal(got, _bf16_round_bits(allv))
+    f32 = v.astype(np.float32)   # torch casts fp32 to bf16 with round-to-nearest-even
+    ref = torch.from_numpy(f32).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(np.array([oracle.round_bf16(float(a)) for a in f32]), ref)
+
+
+def _torch_mx8(v):
+    """MXFP8 rounding written with torch: the group's scale from frexp of its
+    largest magnitude, the elements through torch's float8_e4m3fn cast."""
+    v = np.asarray(v, dtype=np.float64)
+    g = v.reshape(-1, 32)
+    amax = np.abs(g).max(axis=1)
+    m, ex = np.frexp(amax)                      # amax = m * 2^ex, m in [0.5, 1)
+    e = np.where(m * 2 <= 1.75, ex - 1 - 8, ex - 1 - 7)   # 448 = 1.75 * 2^8
+    e = np.where(amax == 0, -127, np.clip(e, -127, 127))
+    s = np.ldexp(1.0, e)[:, None]
+    q = torch.from_numpy(g / s).to(torch.float8_e4m3fn).double().numpy() * s
+    return q.reshape(v.shape)
+
+
+def test_mx8_round_matches_torch_formulation():
+    rng = np.random.default_rng(11)
+    v = rng.normal(0, 0.02, (40, 256)) * 2.0 ** rng.integers(-6, 6, (40, 1))
+    np.testing.assert_array_equal(oracle.mx8_round(v), _torch_mx8(v))
+
+
+def test_expert_ffn_with_fp8_activations_matches_independent_composition():
+    """One fp8 expert: x rounded to MXFP8, z = W13 x in fp64, h = silu(a) v
+    held in bf16 and rounded to MXFP8, y = W2 h; written with numpy and torch."""
+    wl = W.Workload("act8_ffn", 1, 8, 256, 4, 2, 256, 0, W.BF16, W.FP8, 0.9, seed=31)
+    inp = W.generate(wl)
+    w13 = _dequant(inp.w13[1], inp.w13_scale[1], W.FP8)
+    w2 = _dequant(inp.w2[1], inp.w2_scale[1], W.FP8)
+    x = W.bf16_bits_to_f32(inp.x).astype(np.float64)
+    for r in range(wl.rows):
+        xq = _torch_mx8(x[r])
+        z = w13 @ xq
+        a, v = z[:256], z[256:]
+        h = _bf16_round_bits(a / (1.0 + np.exp(-a)) * v)
+        ref = w2 @ _torch_mx8(h)
+        got = oracle.expert_ffn(256, 256, W.FP8, inp.w13[1], inp.w13_scale[1], inp.w2[1], inp.w2_scale[1],
+                                oracle.mx8_round(x[r]), act_fp8=True)
+        np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-11 * np.abs(ref).max())
+
+
+def test_forward_with_fp8_activations_routes_identically():
+    """The option changes only the expert GEMMs' inputs: routing is bit-equal,
+    and the output differs from the exact one by MXFP8-sized amounts."""
+    wl = W.WORKLOADS["tiny_fp32"].with_(act_dtype=W.BF16, weight_dtype=W.FP8, num_blocks=2, seed=33)
+    inp = W.generate(wl)
+    r0 = oracle.forward(inp)
+    r1 = oracle.forward(inp, act_fp8=True)
+    for k in ("topk_idx", "gates", "coreset_ids", "coreset_size", "logits", "block_mass", "perm"):
+        np.testing.assert_array_equal(r0[k], r1[k])
+    d = np.abs(r1["out"] - r0["out"]).max() / np.abs(r0["out"]).max()
+    assert 1e-4 < d < 0.1, d
+    with pytest.raises(ValueError):
+        oracle.forward(W.generate(W.WORKLOADS["tiny_fp32"]), act_fp8=True)   # fp32 weights: rejected
