@@ -35,6 +35,9 @@ A8 = W.Workload("w8a8_res", 8, 32, 512, 16, 4, 512, 512, W.BF16, W.FP8, 0.9, see
     (A8.with_(name="w8a8_H2048", hidden=2048, seed=144), "rows"),
     (A8.with_(name="w8a8_noshared", shared_inter=0, seed=145), "panels"),
     (A8.with_(name="w8a8_mt1", num_blocks=4, num_experts=64, top_k=8, seed=146), "rows"),
+    (A8.with_(name="w8a8_mt1_H1024", num_blocks=4, num_experts=64, top_k=8, hidden=1024, seed=152), "panels"),
+    (A8.with_(name="w8a8_mt2", num_experts=32, seed=153), "panels"),
+    (A8.with_(name="w8a8_mt2_H2048_rows", num_experts=32, hidden=2048, seed=154), "rows"),
     (A8.with_(name="w8a8_mt4", num_experts=8, seed=147), "panels"),
     (A8.with_(name="w8a8_mt4_rows", num_experts=8, seed=148), "rows"),
     (A8.with_(name="w8a8_hot", bias_sigma=3.0, seed=149), "rows"),
