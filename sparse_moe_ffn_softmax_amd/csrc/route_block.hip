@@ -525,12 +525,22 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(Plan plan, float 
     const int half = lane >> 5, hl = lane & 31;
     const int r = 2 * wave + half;
     const bool row_ok = row_is_live(r);
+    // (the LDS reads are unconditional and the tests bitwise: written with
+    // short-circuit conditions, each candidate became a branch around its
+    // own LDS round trip.  rank_s is unset without mass work, where m = E.)
     uint64_t key[8];
+    int rk[8];
+    float lg[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      rk[s] = rank_s[hl + 32 * s];
+      lg[s] = l_s[r][hl + 32 * s];
+    }
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int e = hl + 32 * s;
-      const bool ok = row_ok && e < E && (m >= E || rank_s[e] < m);
-      key[s] = ok ? (static_cast<uint64_t>(logit_key(l_s[r][e])) << 32) | static_cast<uint32_t>(~e) : 0ull;
+      const bool ok = row_ok & (e < E) & ((m >= E) | (rk[s] < m));
+      key[s] = ok ? (static_cast<uint64_t>(logit_key(lg[s])) << 32) | static_cast<uint32_t>(~e) : 0ull;
     }
     sort8_desc(key);
     // the lane's candidates stay in registers: a lane whose head is taken
