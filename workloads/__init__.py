@@ -87,7 +87,7 @@ WORKLOADS: Dict[str, Workload] = {
     "blocks16_bf16": Workload("blocks16_bf16", 16, 32, 2048, 256, 8, 512, 512, BF16, BF16, 0.9, seed=3),
     # 64 blocks x 32 rows, fp8 e4m3 expert weights with fp32 128x128 block scales
     "blocks64_fp8": Workload("blocks64_fp8", 64, 32, 2048, 256, 8, 512, 512, BF16, FP8, 0.9, seed=4),
-    # 16 blocks with fp8 weights (32-row work tiles): the fp8-activation GEMMs' two-column-block form
+    # 16 blocks with fp8 weights (32-row work tiles), with and without fp8 activations
     "blocks16_fp8": Workload("blocks16_fp8", 16, 32, 2048, 256, 8, 512, 512, BF16, FP8, 0.9, seed=13),
     # autoregressive decode: one row per call, plain top-8 (threshold 1)
     "decode1_bf16": Workload("decode1_bf16", 1, 1, 2048, 256, 8, 512, 512, BF16, BF16, 1.0, seed=5),
