@@ -231,9 +231,16 @@ struct TiledGemm : StageOps<F, PK> {
   static constexpr int AV = T / RPP;                // vectors per thread per stage
   using Lds = AT[2][T][PITCH];
 
+  // MTX: the row tiles that hold rows of this tile (1..MT), a compile-time
+  // count chosen per tile by the caller: the MFMAs and fragment reads of the
+  // others are skipped (their accumulators stay zero and are never stored).
+  // Staging still covers all T rows, so the load counts stay fixed.
+  template <int MTX = MT>
   static __device__ __forceinline__ void run(Lds& As, const AT* const (&asrc)[AV],
                                              const uint8_t* brow, const void* bsc, int Kdim,
                                              f32x4 (&acc)[MT]) {
+    static_assert(MTX >= 1 && MTX <= MT, "row tiles");
+    f32x4(&accx)[MTX] = *reinterpret_cast<f32x4(*)[MTX]>(&acc[0]);
     const int tid = threadIdx.x, lane = tid & 63;
     const int col = lane & 15, kg = lane >> 4;
     const int seg = tid % VPR, r0 = tid / VPR;
@@ -253,12 +260,12 @@ struct TiledGemm : StageOps<F, PK> {
         *reinterpret_cast<u32x4*>(&As[buf][r0 + i * RPP][Ops::apos(seg) * (16 / (int)sizeof(AT))]) = areg[i];
     };
     auto load_b = [&](BSet& bs, int k0) { Ops::load_b(bs, brow, bsc, k0); };
-    // Every row tile runs (the rows past the tile repeat the tile's first
-    // row in LDS, and their outputs are never stored): a guard per row tile
-    // would make each MFMA wait for its own LDS read.
+    // The MTX row tiles all run (rows past the tile in the last one repeat
+    // the tile's first row in LDS, and their outputs are never stored): a
+    // guard per row tile would make each MFMA wait for its own LDS read.
     auto compute = [&](BSet& bs, int buf, int k0) {
       const float sc8 = F == WFmt::FP8 ? static_cast<const float*>(bsc)[k0 / 128] : 0.f;
-      Ops::template mma<MT>(&As[buf][col][0], PITCH, 0, bs, sc8, kg, acc);
+      Ops::template mma<MTX>(&As[buf][col][0], PITCH, 0, bs, sc8, kg, accx);
     };
 
     // Schedule: while stage s feeds the MFMAs, stage s+1's activations and
@@ -333,6 +340,19 @@ struct TiledGemm : StageOps<F, PK> {
   }
 };
 
+// The GEMM of one tile with its own row-tile count: ceil(rows / 16), made
+// wave-uniform so that one instantiation runs per tile.
+template <class G, int MT>
+__device__ __forceinline__ void run_rows(int rows, typename G::Lds& As, const typename G::AT* const (&asrc)[G::AV],
+                                         const uint8_t* brow, const void* bsc, int Kdim, f32x4 (&acc)[MT]) {
+  const int mtx = __builtin_amdgcn_readfirstlane((rows + 15) >> 4);
+  static_for<1, MT>([&](auto M) {
+    constexpr int MX = decltype(M)::value;
+    if (mtx == MX) G::template run<MX>(As, asrc, brow, bsc, Kdim, acc);
+  });
+  if (mtx >= MT) G::template run<MT>(As, asrc, brow, bsc, Kdim, acc);
+}
+
 template <WFmt F, int MT, bool PK>
 __global__ __launch_bounds__(64 * tiled_waves(MT)) void expert_up_tiled_kernel(TiledArgs a) {
   using G = TiledGemm<F, MT, PK>;
@@ -383,7 +403,7 @@ __global__ __launch_bounds__(64 * tiled_waves(MT)) void expert_up_tiled_kernel(T
     for (int i = tid; i < 2 * ns; i += G::THREADS) sc_s[i / ns][i % ns] = S[(size_t)srow[i / ns] * ns + i % ns];
   }
   f32x4 acc[MT];
-  G::run(As, asrc, brow, bsc, H, acc);
+  run_rows<G, MT>(t.rows, As, asrc, brow, bsc, H, acc);
 
   AT* h = static_cast<AT*>(a.h) +
           (shared ? (size_t)a.N * a.K * a.I + (size_t)t.start * a.Is : (size_t)t.start * a.I);
@@ -444,7 +464,7 @@ __global__ __launch_bounds__(64 * tiled_waves(MT)) void expert_down_tiled_kernel
     for (int i = tid; i < ns; i += G::THREADS) sc_s[0][i] = S[(size_t)srow * ns + i];
   }
   f32x4 acc[MT];
-  G::run(As, asrc, brow, bsc, inter, acc);
+  run_rows<G, MT>(t.rows, As, asrc, brow, bsc, inter, acc);
 
   const size_t y0 = ((shared ? (size_t)a.N * a.K : 0) + (size_t)t.start) * H;
 #pragma unroll
