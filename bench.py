@@ -218,7 +218,7 @@ def cpu_baseline(inp, B, N, budget_s):
             t1 = time.perf_counter()
             oracle.forward(inp, threads=nthreads)
             one = time.perf_counter() - t1
-            reps = max(1, min(20, int(budget / max(one, 1e-3))))
+            reps = max(1, min(500, int(budget / max(one, 1e-3))))
         t1 = time.perf_counter()
         for _ in range(reps):
             oracle.forward(inp, threads=nthreads, rows=rows)
