@@ -40,6 +40,7 @@ A8 = W.Workload("w8a8_res", 8, 32, 512, 16, 4, 512, 512, W.BF16, W.FP8, 0.9, see
     (A8.with_(name="w8a8_mt2_H2048_rows", num_experts=32, hidden=2048, seed=154), "rows"),
     (A8.with_(name="w8a8_mt4", num_experts=8, seed=147), "panels"),
     (A8.with_(name="w8a8_mt4_rows", num_experts=8, seed=148), "rows"),
+    (A8.with_(name="w8a8_mt4_H2048", num_experts=8, hidden=2048, seed=155), "panels"),
     (A8.with_(name="w8a8_hot", bias_sigma=3.0, seed=149), "rows"),
     (A8.with_(name="w8a8_live_budget", live_fraction=0.6, expert_budget=6, seed=150), "panels"),
     (A8.with_(name="w8a8_rows8", block_rows=8, num_blocks=32, seed=151), "rows"),
