@@ -51,6 +51,9 @@ struct ManyArgs {
 constexpr int kManyWaves = 8;
 constexpr int kManyThreads = 64 * kManyWaves;
 
+// fp32 to bf16 bits, rounded to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
 // ---------------------------------------------------------------------------
 // Down GEMM.  A tile's h (at most 128 rows of I = 512 bf16, 136 KiB with the
 // row padding) is staged into LDS once per tile by direct global-to-LDS loads
@@ -357,11 +360,15 @@ __global__ __launch_bounds__(kManyThreads, 1) void expert_down_many_kernel(ManyA
 #pragma unroll
     for (int i = 0; i < MTM; ++i) {
       if (i >= mt) break;
-      const bool whole = (i + 1) * 32 <= t.rows;
+      uint16_t* yr = yb + (size_t)(32 * i) * Hs;
+      if ((i + 1) * 32 <= t.rows) {  // a scalar branch: no per-store lane masks
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = i * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-        if (whole || m < t.rows) yb[(size_t)(i * 32 + 8 * (v >> 2) + (v & 3)) * Hs] = f32_to_bf16(acc[i][v]);
+        for (int v = 0; v < 16; ++v) yr[(size_t)(8 * (v >> 2) + (v & 3)) * Hs] = bf16_bits(acc[i][v]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (32 * i + 8 * (v >> 2) + 4 * hh + (v & 3) < t.rows)
+            yr[(size_t)(8 * (v >> 2) + (v & 3)) * Hs] = bf16_bits(acc[i][v]);
       }
     }
   };
