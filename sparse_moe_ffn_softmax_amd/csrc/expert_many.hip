@@ -560,14 +560,22 @@ __global__ __launch_bounds__(kManyThreads, 1) void expert_up_mx_kernel(ManyArgs 
 #pragma unroll
     for (int i = 0; i < MTM; ++i) {
       if (i >= mt) break;
-      const bool whole = (i + 1) * 32 <= t.rows;
+      uint16_t* hr = hrow + (size_t)(32 * i) * In;
+      if ((i + 1) * 32 <= t.rows) {  // a scalar branch: whole row tiles need no row test
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float g = acc[i][v];
-        const float upv = shfl_xor_f(g, 8);
-        const int m = i * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-        if ((rl & 15) < 8 && (whole || m < t.rows))
-          hrow[(size_t)(i * 32 + 8 * (v >> 2) + (v & 3)) * In] = f32_to_bf16(silu(g) * upv);
+        for (int v = 0; v < 16; ++v) {
+          const float g = acc[i][v];
+          const float upv = shfl_xor_f(g, 8);
+          if ((rl & 15) < 8) hr[(size_t)(8 * (v >> 2) + (v & 3)) * In] = bf16_bits(silu(g) * upv);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float g = acc[i][v];
+          const float upv = shfl_xor_f(g, 8);
+          if ((rl & 15) < 8 && 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3) < t.rows)
+            hr[(size_t)(8 * (v >> 2) + (v & 3)) * In] = bf16_bits(silu(g) * upv);
+        }
       }
     }
     rc = rn;
