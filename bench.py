@@ -443,8 +443,10 @@ def main():
         # the library's kernel choice: 16-row work tiles run the register-operand
         # kernels (expert_gemm.hip); taller tiles the many-row kernels
         # (expert_many.hip) where their shapes fit, else the LDS-tiled ones
+        tile_rows = next((16 * m for m in (1, 2, 4, 6, 8) if 16 * m >= want), 128)
+        min_rows = {W.BF16: 128, W.FP8: 96}.get(wl.weight_dtype, 32)
         many_dn = (tiled and I == 512 and H % 256 == 0 and Is in (0, I) and wl.act_dtype == W.BF16
-                   and wl.weight_dtype != W.F32)
+                   and wl.weight_dtype != W.F32 and (args.act_fp8 or tile_rows >= min_rows))
         if dom == 2:
             kname, src = (("expert_up_mx_kernel", "expert_many.hip") if args.act_fp8 else
                           ("expert_up_tiled_kernel", "expert_tiled.hip") if tiled else

@@ -107,7 +107,9 @@ hipError_t launch_expert_down_combine(const Plan& p, const cmoe_weights& w, void
 hipError_t launch_expert_tiled(const Plan& p, const cmoe_weights& w, const void* x, bool up,
                                hipStream_t s);
 // mt_max > 1 on 16-bit activations with I = 512 (and Is = 0 or I): persistent
-// kernels on the 32x32 MFMA (expert_many.hip); up = gate/up + SwiGLU, else down
+// kernels on the 32x32 MFMA (expert_many.hip); up = gate/up + SwiGLU (fp8
+// activations only), else down (fp8 activations, or work tiles tall enough for
+// the weight format: bf16 128 rows, fp8 96, 4-bit 32)
 bool expert_many_fits(const Plan& p, bool up);
 hipError_t launch_expert_many(const Plan& p, const cmoe_weights& w, const void* x, bool up, hipStream_t s);
 hipError_t launch_combine(const Plan& p, void* out, hipStream_t s);

@@ -605,7 +605,15 @@ bool expert_many_fits(const Plan& p, bool up) {
   const bool base = p.mt_max > 1 && p.act == CMOE_BF16 && p.y_act && p.wt != CMOE_F32 &&
                     (p.Is == 0 || p.Is == p.I) && p.tile_rows % 32 == 0;
   if (up) return base && p.act8 && mx_up_stages_ok(p.H) && p.I % kUpManyCols == 0;
-  return base && p.I == 128 * kDownManyStages && p.H % kDownManyCols == 0;
+  if (!base || p.I != 128 * kDownManyStages || p.H % kDownManyCols != 0) return false;
+  if (p.act8) return true;  // the fp8-activation down GEMM exists only here
+  // Against the LDS-tiled down kernel (expert_tiled.hip), by weight format and
+  // work-tile height (measured, one MI355X, I = 512, H = 2048): bf16 tiled
+  // 11-15% faster at 32-96 rows, this kernel 12% faster at 128; fp8 tiled
+  // 4-5% faster at 32 and 64 rows, even at 96, this kernel 27% faster at 128;
+  // 4-bit this kernel faster at 64-128 rows
+  const int min_rows = p.wt == CMOE_BF16 ? 128 : p.wt == CMOE_FP8_E4M3 ? 96 : 32;
+  return p.tile_rows >= min_rows;
 }
 
 // Persistent grid: one workgroup per CU, or more when a run of units could

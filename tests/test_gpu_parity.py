@@ -120,6 +120,9 @@ RES = W.Workload("res_bf16", 8, 32, 256, 16, 4, 512, 512, W.BF16, W.BF16, 0.9, s
     (RES.with_(name="res_hot", bias_sigma=3.0, seed=128), "rows"),
     (RES.with_(name="res_live_budget", live_fraction=0.6, expert_budget=6, seed=129), "rows"),
     (RES.with_(name="res_rows8", block_rows=8, num_blocks=32, seed=130), "rows"),
+    # 128-row tiles, where bf16 weights take this kernel too
+    (RES.with_(name="res_bf16_t128", top_k=8, seed=132), "rows"),
+    (RES.with_(name="res_bf16_t128_panels", top_k=8, seed=133), "panels"),
 ], ids=lambda v: v if isinstance(v, str) else v.name)
 def test_resident_down_shapes(wl, layout):
     inp = W.generate(wl)
