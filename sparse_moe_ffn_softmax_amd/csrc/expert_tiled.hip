@@ -39,7 +39,12 @@ namespace cmoe {
 // the 8 waves to share their activation tile's LDS (64 blocks with 4 waves:
 // gate/up 134 -> 171 us).
 __host__ __device__ constexpr int tiled_waves(int mt) { return mt <= 2 ? 4 : 8; }
-__host__ __device__ constexpr int tiled_up_cols(int mt) { return 8 * tiled_waves(mt); }     // h columns per workgroup
+// The gate/up kernel runs 16 waves on 128-row tiles: one activation tile then
+// feeds twice the weight columns (256 and 512 blocks, fp8 weights: 523 -> 442
+// and 968 -> 816 us; 128 blocks bf16 358 -> 329 us, 4-bit 238 -> 227 us),
+// where on 96-row tiles 16 waves were slower (64 blocks fp8: 146 -> 159 us).
+__host__ __device__ constexpr int tiled_up_waves(int mt) { return mt == 8 ? 16 : tiled_waves(mt); }
+__host__ __device__ constexpr int tiled_up_cols(int mt) { return 8 * tiled_up_waves(mt); }  // h columns per workgroup
 __host__ __device__ constexpr int tiled_down_cols(int mt) { return 16 * tiled_waves(mt); }  // y columns per workgroup
 
 struct TiledArgs {
@@ -216,7 +221,7 @@ struct StageOps {
 // first row, so that every load is unconditional); brow: this lane's weight
 // chunk 0 (bchunk0); bsc: its fp8 block scales, one per 128 k, in LDS.  PK:
 // the weights are stored in MFMA panels.
-template <WFmt F, int MT, bool PK>
+template <WFmt F, int MT, bool PK, int NWAVES = tiled_waves(MT)>
 struct TiledGemm : StageOps<F, PK> {
   using Ops = StageOps<F, PK>;
   using Fr = Frag<F>;
@@ -225,10 +230,11 @@ struct TiledGemm : StageOps<F, PK> {
   using BSet = typename Ops::BSet;
   static constexpr int T = 16 * MT;
   static constexpr int KS = Ops::KS, VPR = Ops::VPR, PITCH = Ops::PITCH;
-  static constexpr int NW = tiled_waves(MT);        // waves per workgroup
+  static constexpr int NW = NWAVES;                 // waves per workgroup
   static constexpr int THREADS = 64 * NW;
   static constexpr int RPP = THREADS / VPR;         // rows staged per pass of the workgroup
   static constexpr int AV = T / RPP;                // vectors per thread per stage
+  static_assert(AV * RPP == T, "whole staging passes");
   using Lds = AT[2][T][PITCH];
 
   // MTX: the row tiles that hold rows of this tile (1..MT), a compile-time
@@ -354,8 +360,8 @@ __device__ __forceinline__ void run_rows(int rows, typename G::Lds& As, const ty
 }
 
 template <WFmt F, int MT, bool PK>
-__global__ __launch_bounds__(64 * tiled_waves(MT)) void expert_up_tiled_kernel(TiledArgs a) {
-  using G = TiledGemm<F, MT, PK>;
+__global__ __launch_bounds__(64 * tiled_up_waves(MT)) void expert_up_tiled_kernel(TiledArgs a) {
+  using G = TiledGemm<F, MT, PK, tiled_up_waves(MT)>;
   using AT = typename G::AT;
   using WT = typename G::WT;
   __shared__ typename G::Lds As;
@@ -483,7 +489,7 @@ __global__ __launch_bounds__(64 * tiled_waves(MT)) void expert_down_tiled_kernel
 template <bool kUp, WFmt F, int MT, bool PK>
 static void launch_tiled(const TiledArgs& a, unsigned grid, hipStream_t s) {
   if constexpr (kUp)
-    expert_up_tiled_kernel<F, MT, PK><<<grid, 64 * tiled_waves(MT), 0, s>>>(a);
+    expert_up_tiled_kernel<F, MT, PK><<<grid, 64 * tiled_up_waves(MT), 0, s>>>(a);
   else
     expert_down_tiled_kernel<F, MT, PK><<<grid, 64 * tiled_waves(MT), 0, s>>>(a);
 }

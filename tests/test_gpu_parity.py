@@ -120,9 +120,13 @@ RES = W.Workload("res_bf16", 8, 32, 256, 16, 4, 512, 512, W.BF16, W.BF16, 0.9, s
     (RES.with_(name="res_hot", bias_sigma=3.0, seed=128), "rows"),
     (RES.with_(name="res_live_budget", live_fraction=0.6, expert_budget=6, seed=129), "rows"),
     (RES.with_(name="res_rows8", block_rows=8, num_blocks=32, seed=130), "rows"),
-    # 128-row tiles, where bf16 weights take this kernel too
+    # 128-row tiles, where bf16 weights take this kernel too (and the gate/up
+    # kernel runs 16 waves per workgroup)
     (RES.with_(name="res_bf16_t128", top_k=8, seed=132), "rows"),
     (RES.with_(name="res_bf16_t128_panels", top_k=8, seed=133), "panels"),
+    (RES.with_(name="res_fp8_t128_panels", top_k=8, weight_dtype=W.FP8, seed=134), "panels"),
+    (RES.with_(name="res_fp4_t128", top_k=8, weight_dtype=W.FP4, seed=135), "rows"),
+    (RES.with_(name="res_f32_t128", top_k=8, act_dtype=W.F32, weight_dtype=W.F32, seed=136), "rows"),
 ], ids=lambda v: v if isinstance(v, str) else v.name)
 def test_resident_down_shapes(wl, layout):
     inp = W.generate(wl)
