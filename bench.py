@@ -421,7 +421,9 @@ def main():
     # the library's per-pair down outputs y: fp32, or bf16 when tiles are
     # taller than 16 rows and the activations are bf16 (the workspace plan)
     want = -(-(N * K * 3 // 2) // E)
-    tiled = want > 16
+    # the library's choice of 16-row register kernels against the LDS-tiled ones
+    reg_max = {W.FP8: 2, W.BF16: 8}.get(wl.weight_dtype, 16)
+    tiled = want > reg_max
     ysz = 2 if (tiled and wl.act_dtype == W.BF16) else 4
     dn_bytes = (touched * (H * I * wsz + sc_dn) + (H * Is * wsz + sc_dn_s) + (pairs * I + n_sh * Is) * hsz
                 + (pairs + n_sh) * H * ysz)
@@ -443,7 +445,7 @@ def main():
         # the library's kernel choice: 16-row work tiles run the register-operand
         # kernels (expert_gemm.hip); taller tiles the many-row kernels
         # (expert_many.hip) where their shapes fit, else the LDS-tiled ones
-        tile_rows = next((16 * m for m in (1, 2, 4, 6, 8) if 16 * m >= want), 128)
+        tile_rows = max(next((16 * m for m in (1, 2, 4, 6, 8) if 16 * m >= want), 128), 32 if tiled else 16)
         min_rows = {W.BF16: 128, W.FP8: 96}.get(wl.weight_dtype, 32)
         many_dn = (tiled and I == 512 and H % 256 == 0 and Is in (0, I) and wl.act_dtype == W.BF16
                    and wl.weight_dtype != W.F32 and (args.act_fp8 or tile_rows >= min_rows))

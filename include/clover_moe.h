@@ -203,7 +203,7 @@ typedef struct {
  *                 with bf16 activations, inter 512, shared_inter 0 or 512,
  *                 hidden 512, 1024 or 2048 and calls with many routed rows
  *                 per expert (work tiles of 32 rows or more: N*top_k above
- *                 about 10.7 E routed pairs);
+ *                 about 4/3 E routed pairs);
  *                 other calls return CMOE_ERR_UNSUPPORTED.  Router, routing
  *                 and combine are unchanged.
  */

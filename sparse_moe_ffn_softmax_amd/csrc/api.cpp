@@ -133,6 +133,13 @@ Layout layout(const cmoe_problem& p, int K) {
       L.mt_max = mt;
       break;
     }
+  // 16-row tiles run the register-operand kernels; from a few rows per expert
+  // on, the LDS-tiled kernels with 32-row tiles are faster for fp8 and bf16
+  // weights (measured, H = 2048, 256 experts, top-8: fp8 from 2 blocks of 32
+  // rows, 2-25% faster; bf16 from 6 blocks, 2-11%; 4-bit weights 17-27% slower
+  // there at 2-10 blocks, and so keep the register kernels)
+  const size_t reg_max = p.weight_dtype == CMOE_FP8_E4M3 ? 2 : p.weight_dtype == CMOE_BF16 ? 8 : 16;
+  if (L.mt_max == 1 && want > reg_max) L.mt_max = 2;
   const size_t T = 16 * (size_t)L.mt_max;
   L.max_tiles = (int)(NK / T + (E < NK ? E : NK) + (N + T - 1) / T + 1);
   const size_t hsz = p.act_dtype == CMOE_F32 ? 4 : 2;
@@ -338,7 +345,7 @@ static cmoe_status forward_impl(const cmoe_problem* problem, const cmoe_weights*
     return fail(CMOE_ERR_UNSUPPORTED,
                 "activation_fp8 needs fp8 weights with bf16 activations, inter=512, shared_inter 0 or "
                 "512, hidden 512, 1024 or 2048 and work tiles of 32 rows or more (N*top_k above about "
-                "10.7 per expert); here weight=%d act=%d inter=%d shared_inter=%d hidden=%d, tile rows %d",
+                "4/3 per expert); here weight=%d act=%d inter=%d shared_inter=%d hidden=%d, tile rows %d",
                 p.weight_dtype, p.act_dtype, p.inter, p.shared_inter, p.hidden, plan.tile_rows);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;

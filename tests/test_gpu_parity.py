@@ -280,6 +280,18 @@ def test_blocks16_bf16_full():
     _report("blocks16_bf16", mx, mean, ref)
 
 
+# A few blocks per call: the smallest calls that take the LDS-tiled kernels
+# (32-row tiles mostly holding one or two rows) instead of the register ones
+@pytest.mark.parametrize("name,nb,layout", [
+    ("blocks64_fp8", 2, "panels"), ("blocks64_fp8", 3, "rows"),
+    ("block32_bf16", 6, "panels"), ("block32_bf16", 8, "rows"),
+])
+def test_few_blocks_tiled_full(name, nb, layout):
+    inp = W.generate(W.WORKLOADS[name].with_(name=f"{name}_x{nb}", num_blocks=nb, seed=170 + nb))
+    mx, mean, ref = check(inp, threads=16, dp=cm.upload(inp, layout=layout))
+    _report(f"{name} x{nb} ({layout})", mx, mean, ref)
+
+
 def test_blocks64_fp8_full():
     inp = W.generate(W.WORKLOADS["blocks64_fp8"])
     mx, mean, ref = check(inp, threads=16)

@@ -59,3 +59,12 @@ def test_w8a8_blocks64_full(layout):
     inp = W.generate(W.WORKLOADS["blocks64_fp8"])
     mx, mean, ref = check(inp, threads=16, dp=cm.upload(inp, layout=layout), act_fp8=True)
     _report(f"blocks64_fp8 ({layout})", mx, mean, ref)
+
+
+@pytest.mark.parametrize("nb", [2, 4])
+def test_w8a8_few_blocks_full(nb):
+    """Two and four 32-row blocks at full size: 32-row work tiles that mostly
+    hold one or two rows."""
+    inp = W.generate(W.WORKLOADS["blocks64_fp8"].with_(name=f"blocks64_fp8_x{nb}", num_blocks=nb, seed=180 + nb))
+    mx, mean, ref = check(inp, threads=16, dp=cm.upload(inp, layout="panels"), act_fp8=True)
+    _report(f"blocks64_fp8 x{nb}", mx, mean, ref)
