@@ -292,6 +292,16 @@ def test_few_blocks_tiled_full(name, nb, layout):
     _report(f"{name} x{nb} ({layout})", mx, mean, ref)
 
 
+def test_few_blocks_budget_live_full():
+    """Four fp8 blocks on the LDS-tiled path with an expert budget and 60%
+    of the rows live."""
+    wl = W.WORKLOADS["blocks64_fp8"].with_(name="blocks64_fp8_x4_live_budget", num_blocks=4, live_fraction=0.6,
+                                           expert_budget=48, seed=190)
+    inp = W.generate(wl)
+    mx, mean, ref = check(inp, threads=16, dp=cm.upload(inp, layout="panels"))
+    _report("blocks64_fp8 x4 live 0.6 budget 48", mx, mean, ref)
+
+
 def test_blocks64_fp8_full():
     inp = W.generate(W.WORKLOADS["blocks64_fp8"])
     mx, mean, ref = check(inp, threads=16)
