@@ -259,6 +259,9 @@ def main():
     ap.add_argument("--act-fp8", action="store_true",
                     help="fp8 weights only: MXFP8 activations into the expert GEMMs (W8A8, "
                          "cmoe_options.activation_fp8)")
+    ap.add_argument("--blocks", type=int, default=None,
+                    help="blocks per call (default: the workload's); the workload is then named "
+                         "<workload>@<blocks>")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="copy a device buffer of this many bytes once before the workload: "
                          "a plain copy kernel of known size for calibrating HBM byte counters")
@@ -283,6 +286,8 @@ def main():
         del src, dst
 
     wl = W.WORKLOADS[args.workload]
+    if args.blocks is not None and args.blocks != wl.num_blocks:
+        wl = wl.with_(name=f"{wl.name}@{args.blocks}", num_blocks=args.blocks)
     K = wl.top_k if args.top_k is None else args.top_k
     tau = wl.mass_threshold if args.tau is None else args.tau
     N, H, E, I, Is, B = wl.rows, wl.hidden, wl.num_experts, wl.inter, wl.shared_inter, wl.num_blocks
