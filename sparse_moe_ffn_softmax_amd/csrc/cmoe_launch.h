@@ -11,7 +11,8 @@
 namespace cmoe {
 
 // Rows of one grouped-GEMM work tile: 16 * mt_max, mt_max in {1, 2, 4, 6, 8} MFMA
-// row tiles, chosen per call from the expected rows per expert (see carve()).
+// row tiles, chosen per call from the expected rows per expert and the weight
+// format (layout() in api.cpp).
 constexpr int kMaxTileRows = 128;
 // h columns produced by one expert_up workgroup (one 16-column MFMA tile of 8
 // gate + 8 up columns; the 4 waves split the hidden dimension).

@@ -12,8 +12,10 @@
 //
 // Work decomposition.  The permutation leaves a list of tiles (expert, first
 // pair, row count).  These kernels run the calls whose tiles hold at most 16
-// rows (one MFMA row tile: one block, decode, verification); calls with more
-// rows per expert run the LDS-tiled kernels of expert_tiled.hip.  A
+// rows (one MFMA row tile) and whose experts see only a few rows on average:
+// one block, decode, verification, and a few blocks per call for bf16 and
+// 4-bit weights (fp8 weights move to 32-row tiles from two rows per expert on
+// average).  Other calls run the LDS-tiled kernels of expert_tiled.hip.  A
 // workgroup takes one tile and one slice of output columns:
 //   expert_up   : 4 waves, 8 h columns = one 16-column MFMA tile of 8 gate
 //                 and the matching 8 up columns (SwiGLU pairs lanes l and l+8

@@ -1,5 +1,6 @@
-// expert_tiled.hip -- grouped expert GEMMs for calls that route many rows to
-// each expert (many blocks per call: 16-128 rows per expert tile).
+// expert_tiled.hip -- grouped expert GEMMs for calls that route several rows
+// to each expert (work tiles of 32 to 128 rows; a tile with fewer rows runs
+// only the 16-row MFMA tiles it fills).
 //
 //   expert_up_tiled   : h = silu(X_e W_gate^T) * (X_e W_up^T)
 //   expert_down_tiled : y = h W2_e^T
