@@ -423,13 +423,10 @@ def main():
     # experts (+ shared), x once, h written once
     up_bytes = (touched * (2 * I * H * wsz + sc_up) + (2 * Is * H * wsz + sc_up_s) + N * H * asz
                 + (pairs * I + n_sh * Is) * hsz)
-    # the library's per-pair down outputs y: fp32, or bf16 when tiles are
-    # taller than 16 rows and the activations are bf16 (the workspace plan)
-    want = -(-(N * K * 3 // 2) // E)
-    # the library's choice of 16-row register kernels against the LDS-tiled ones
-    reg_max = {W.FP8: 2, W.BF16: 8}.get(wl.weight_dtype, 16)
-    tiled = want > reg_max
-    ysz = 2 if (tiled and wl.act_dtype == W.BF16) else 4
+    # the library's kernel choice for this call, and the width of its per-pair
+    # down outputs y (fp32, or bf16 on the taller-tile paths)
+    plan = cm.clover_moe_plan_info(dp.problem, K, opts)
+    ysz = plan["y_bytes"]
     dn_bytes = (touched * (H * I * wsz + sc_dn) + (H * Is * wsz + sc_dn_s) + (pairs * I + n_sh * Is) * hsz
                 + (pairs + n_sh) * H * ysz)
     # whole call (weights, router, x in, out)
@@ -447,21 +444,16 @@ def main():
     device_ms = stage_ms.sum(1)
     if dom_bytes is not None:
         achieved = float(dom_bytes.sum() / (stage_ms[:, dom].sum() * 1e-3) / 1e9)
-        # the library's kernel choice: 16-row work tiles run the register-operand
-        # kernels (expert_gemm.hip); taller tiles the many-row kernels
-        # (expert_many.hip) where their shapes fit, else the LDS-tiled ones
-        tile_rows = max(next((16 * m for m in (1, 2, 4, 6, 8) if 16 * m >= want), 128), 32 if tiled else 16)
-        min_rows = {W.BF16: 128, W.FP8: 96}.get(wl.weight_dtype, 32)
-        many_dn = (tiled and I == 512 and H % 256 == 0 and Is in (0, I) and wl.act_dtype == W.BF16
-                   and wl.weight_dtype != W.F32 and (args.act_fp8 or tile_rows >= min_rows))
+        # the kernel of the dominant stage, by the library's own choice
         if dom == 2:
-            kname, src = (("expert_up_mx_kernel", "expert_many.hip") if args.act_fp8 else
-                          ("expert_up_tiled_kernel", "expert_tiled.hip") if tiled else
-                          ("expert_up_kernel", "expert_gemm.hip"))
+            kname, src = {"register": ("expert_up_kernel", "expert_gemm.hip"),
+                          "lds_tiled": ("expert_up_tiled_kernel", "expert_tiled.hip"),
+                          "persistent": ("expert_up_mx_kernel", "expert_many.hip")}[plan["gate_up"]]
         else:
-            kname, src = (("expert_down_many_kernel", "expert_many.hip") if many_dn else
-                          ("expert_down_tiled_kernel", "expert_tiled.hip") if tiled else
-                          ("expert_down_kernel", "expert_gemm.hip"))
+            kname, src = {"register": ("expert_down_kernel", "expert_gemm.hip"),
+                          "lds_tiled": ("expert_down_tiled_kernel", "expert_tiled.hip"),
+                          "persistent": ("expert_down_many_kernel", "expert_many.hip"),
+                          "down_combine": ("expert_down_combine_kernel", "expert_gemm.hip")}[plan["down"]]
         wl_key = wl.name + ("_w8a8" if args.act_fp8 else "")
         traffic = measured_traffic(kname, wl_key, src, args.layout)
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
@@ -520,6 +512,7 @@ def main():
                    "weight_layout": args.layout, "activation_fp8": bool(args.act_fp8)},
         "roofline": roofline,
         "call": {
+            "kernels": plan,
             "device_us_staged": round(float(device_ms.mean() * 1e3), 2),
             "algorithmic_bytes": int(call_bytes.mean()),
             "hbm_gbps": round(call_gbps, 1),

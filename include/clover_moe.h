@@ -287,9 +287,11 @@ cmoe_status clover_moe_block_forward_noalloc(const cmoe_problem* problem, const 
 
 /* Number of kernel stages clover_moe_block_forward queues, in order:
  * 0 router logits, 1 per-block routing (softmax, mass, coreset, top-k, gates;
- * the last block also builds the row permutation and the GEMM work list),
- * 2 gate/up GEMM + SwiGLU, 3 down GEMM, 4 gate-weighted combine with the
- * shared expert. */
+ * a one-block call also builds the row permutation and the GEMM work list in
+ * the same kernel, a call of several blocks in two kernels after it),
+ * 2 gate/up GEMM + SwiGLU (with fp8 activations, after rounding x to MXFP8),
+ * 3 down GEMM, 4 gate-weighted combine with the shared expert (empty when the
+ * down GEMM writes `out` itself, see cmoe_plan_info). */
 #define CLOVER_MOE_NUM_STAGES 5
 
 /* Same operation as clover_moe_block_forward_ex, for profiling: records
@@ -305,6 +307,36 @@ cmoe_status clover_moe_block_forward_staged(const cmoe_problem* problem, const c
                                             const cmoe_routing* routing,
                                             void* workspace, size_t workspace_bytes, void* stream,
                                             void* const* stage_events, int32_t n_events);
+
+/* Which grouped-GEMM kernels a call runs (InfiniLM PR #604, "Benchmark /
+ * Performance Impact": the cost of each phase is measured apart from the
+ * rest; a caller that times the stages of clover_moe_block_forward_staged
+ * learns from this which kernel each stage timed).  Host-only: no device
+ * work and no device needed.  The choice depends only on the problem's
+ * shape and dtypes, top_k and options->activation_fp8. */
+typedef enum {
+    CMOE_GEMM_REGISTER = 0,     /* 16-row work tiles, operands in registers */
+    CMOE_GEMM_LDS_TILED = 1,    /* taller tiles, activation tile staged in LDS */
+    CMOE_GEMM_PERSISTENT = 2,   /* one workgroup per CU, runs of tiles */
+    CMOE_GEMM_DOWN_COMBINE = 3  /* down GEMM and combine in one kernel (few routed pairs) */
+} cmoe_gemm_kind;
+
+typedef struct {
+    int32_t tile_rows;      /* rows of a grouped-GEMM work tile: 16, 32, 64, 96 or 128 */
+    int32_t gate_up;        /* cmoe_gemm_kind of stage 2 */
+    int32_t down;           /* cmoe_gemm_kind of stage 3 */
+    int32_t y_bytes;        /* bytes per element of the per-pair down outputs (2: bf16, 4: fp32) */
+    int32_t kernels;        /* kernels queued per call */
+} cmoe_plan_info;
+
+/* Fills *info for a call of clover_moe_block_forward_ex with these
+ * arguments.  options may be NULL (defaults); its live_rows pointer is not
+ * read.  Errors: those of clover_moe_workspace_size, CMOE_ERR_NULL when info
+ * is NULL, CMOE_ERR_VALUE for an activation_fp8 other than 0 or 1 and
+ * CMOE_ERR_UNSUPPORTED when activation_fp8 = 1 does not cover the call (the
+ * statuses clover_moe_block_forward_ex returns for them). */
+cmoe_status clover_moe_plan_info(const cmoe_problem* problem, int32_t top_k, const cmoe_options* options,
+                                 cmoe_plan_info* info);
 
 /* Rearranges row-major expert weight matrices into MFMA panels
  * (CMOE_LAYOUT_PANELS).  Queued on `stream`; one pass over the bytes, nothing

@@ -25,7 +25,7 @@ LAYOUT_CODES = {"rows": CMOE_LAYOUT_ROWS, "panels": CMOE_LAYOUT_PANELS}
 
 EXPORTED = ("clover_moe_workspace_size", "clover_moe_block_forward", "clover_moe_block_forward_ex",
             "clover_moe_block_forward_staged", "clover_moe_block_forward_noalloc", "clover_moe_pack_weights",
-            "clover_moe_status_string", "clover_moe_last_error")
+            "clover_moe_status_string", "clover_moe_last_error", "clover_moe_plan_info")
 NOALLOC_MAX_WORKSPACE = 128 * 1024 * 1024  # CLOVER_MOE_NOALLOC_MAX_WORKSPACE
 NUM_STAGES = 5
 STAGE_NAMES = ("router", "route_blocks", "expert_up", "expert_down", "combine")
@@ -53,6 +53,15 @@ class cmoe_routing(ctypes.Structure):
 class cmoe_options(ctypes.Structure):
     _fields_ = [("expert_budget", ctypes.c_int32), ("live_rows", ctypes.c_void_p),
                 ("activation_fp8", ctypes.c_int32)]
+
+
+class cmoe_plan_info(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("tile_rows", "gate_up", "down", "y_bytes", "kernels")]
+
+
+CMOE_GEMM_REGISTER, CMOE_GEMM_LDS_TILED, CMOE_GEMM_PERSISTENT, CMOE_GEMM_DOWN_COMBINE = 0, 1, 2, 3
+GEMM_KIND_NAMES = {CMOE_GEMM_REGISTER: "register", CMOE_GEMM_LDS_TILED: "lds_tiled",
+                   CMOE_GEMM_PERSISTENT: "persistent", CMOE_GEMM_DOWN_COMBINE: "down_combine"}
 
 
 class ClovermoeError(RuntimeError):
@@ -99,6 +108,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.clover_moe_status_string.argtypes = [ctypes.c_int]
     L.clover_moe_last_error.restype = ctypes.c_char_p
     L.clover_moe_last_error.argtypes = []
+    L.clover_moe_plan_info.restype = ctypes.c_int
+    L.clover_moe_plan_info.argtypes = [ctypes.POINTER(cmoe_problem), ctypes.c_int32, ctypes.POINTER(cmoe_options),
+                                       ctypes.POINTER(cmoe_plan_info)]
     _lib = L
     return L
 
@@ -114,6 +126,17 @@ def clover_moe_last_error() -> str:
 def _check(status: int):
     if status != CMOE_OK:
         raise ClovermoeError(status, clover_moe_last_error() or clover_moe_status_string(status))
+
+
+def clover_moe_plan_info(problem: cmoe_problem, top_k: int, options=None) -> dict:
+    """The grouped-GEMM kernels a call runs (host-only): tile_rows, gate_up and
+    down (names from GEMM_KIND_NAMES), y_bytes and kernels per call."""
+    info = cmoe_plan_info()
+    _check(load_library().clover_moe_plan_info(ctypes.byref(problem), top_k,
+                                               ctypes.byref(options) if options is not None else None,
+                                               ctypes.byref(info)))
+    return {"tile_rows": info.tile_rows, "gate_up": GEMM_KIND_NAMES[info.gate_up],
+            "down": GEMM_KIND_NAMES[info.down], "y_bytes": info.y_bytes, "kernels": info.kernels}
 
 
 def clover_moe_workspace_size(problem: cmoe_problem, top_k: int) -> int:

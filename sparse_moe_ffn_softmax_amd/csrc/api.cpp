@@ -180,9 +180,8 @@ namespace cmoe {
 
 size_t workspace_bytes(const cmoe_problem& pr, int top_k) { return layout(pr, top_k).total; }
 
-void carve(Plan& p, const cmoe_problem& pr, int K, void* ws, const cmoe_routing* rt) {
-  const Layout L = layout(pr, K);
-  char* base = static_cast<char*>(ws);
+// sizes, dtypes and the work-tile plan; device pointers are left as they are
+static void plan_shape(Plan& p, const cmoe_problem& pr, int K, const Layout& L) {
   p.N = pr.block_rows * pr.num_blocks;
   p.H = pr.hidden;
   p.E = pr.num_experts;
@@ -198,6 +197,16 @@ void carve(Plan& p, const cmoe_problem& pr, int K, void* ws, const cmoe_routing*
   p.max_tiles = L.max_tiles;
   p.mt_max = L.mt_max;
   p.tile_rows = 16 * L.mt_max;
+  p.y_act = L.y_act;
+  p.act8 = 0;
+}
+
+void plan_shape(Plan& p, const cmoe_problem& pr, int K) { plan_shape(p, pr, K, layout(pr, K)); }
+
+void carve(Plan& p, const cmoe_problem& pr, int K, void* ws, const cmoe_routing* rt) {
+  const Layout L = layout(pr, K);
+  plan_shape(p, pr, K, L);
+  char* base = static_cast<char*>(ws);
   p.logits = (rt && rt->logits) ? rt->logits : reinterpret_cast<float*>(base + L.logits);
   p.topk = (rt && rt->topk_idx) ? rt->topk_idx : reinterpret_cast<int32_t*>(base + L.topk);
   p.gates = (rt && rt->gates) ? rt->gates : reinterpret_cast<float*>(base + L.gates);
@@ -211,8 +220,6 @@ void carve(Plan& p, const cmoe_problem& pr, int K, void* ws, const cmoe_routing*
   p.tile_count = reinterpret_cast<int32_t*>(base + L.tile_count);
   p.h = base + L.h;
   p.y = base + L.y;
-  p.y_act = L.y_act;
-  p.act8 = 0;
   p.x8 = L.x8 ? base + L.x8 : nullptr;
   p.coreset_ids = rt ? rt->coreset_ids : nullptr;
   p.coreset_size = rt ? rt->coreset_size : nullptr;
@@ -222,9 +229,54 @@ void carve(Plan& p, const cmoe_problem& pr, int K, void* ws, const cmoe_routing*
   p.out_perm = rt ? rt->perm : nullptr;
 }
 
+bool act8_fits(const Plan& p) {
+  // the MXFP8 buffers exist for fp8 weights with y in the activation dtype
+  return p.wt == CMOE_FP8_E4M3 && p.y_act && expert_many_fits(p, true) && expert_many_fits(p, false);
+}
+
+KernelChoice choose_kernels(const Plan& p) {
+  KernelChoice c;
+  c.fused = down_combine_fits(p);
+  c.up = p.mt_max == 1 ? CMOE_GEMM_REGISTER : expert_many_fits(p, true) ? CMOE_GEMM_PERSISTENT : CMOE_GEMM_LDS_TILED;
+  c.down = c.fused                       ? CMOE_GEMM_DOWN_COMBINE
+           : p.mt_max == 1                ? CMOE_GEMM_REGISTER
+           : expert_many_fits(p, false)   ? CMOE_GEMM_PERSISTENT
+                                          : CMOE_GEMM_LDS_TILED;
+  return c;
+}
+
 }  // namespace cmoe
 
+static cmoe_status act8_unsupported(const cmoe_problem& p, const cmoe::Plan& plan) {
+  return fail(CMOE_ERR_UNSUPPORTED,
+              "activation_fp8 needs fp8 weights with bf16 activations, inter=512, shared_inter 0 or "
+              "512, hidden 512, 1024 or 2048 and work tiles of 32 rows or more (N*top_k above about "
+              "4/3 per expert); here weight=%d act=%d inter=%d shared_inter=%d hidden=%d, tile rows %d",
+              p.weight_dtype, p.act_dtype, p.inter, p.shared_inter, p.hidden, plan.tile_rows);
+}
+
 extern "C" {
+
+cmoe_status clover_moe_plan_info(const cmoe_problem* problem, int32_t top_k, const cmoe_options* options,
+                                 cmoe_plan_info* info) {
+  if (!info) return fail(CMOE_ERR_NULL, "info is NULL");
+  const cmoe_status s = check_problem(problem, top_k);
+  if (s != CMOE_OK) return s;
+  const int act8 = options ? options->activation_fp8 : 0;
+  if (act8 != 0 && act8 != 1) return fail(CMOE_ERR_VALUE, "activation_fp8=%d must be 0 or 1", act8);
+  cmoe::Plan plan{};
+  cmoe::plan_shape(plan, *problem, top_k);
+  plan.act8 = act8;
+  if (act8 && !cmoe::act8_fits(plan)) return act8_unsupported(*problem, plan);
+  const cmoe::KernelChoice kc = cmoe::choose_kernels(plan);
+  info->tile_rows = plan.tile_rows;
+  info->gate_up = kc.up;
+  info->down = kc.down;
+  info->y_bytes = plan.y_act ? 2 : 4;  // y in the (bf16) activation dtype, else fp32
+  // router, routing, [two permutation kernels], [MXFP8 rounding of x], gate/up, down, [combine]
+  info->kernels = 4 + (plan.B > 1 ? 2 : 0) + (act8 ? 1 : 0) + (kc.fused ? 0 : 1);
+  return CMOE_OK;
+}
 
 cmoe_status clover_moe_workspace_size(const cmoe_problem* problem, int32_t top_k, size_t* bytes) {
   if (!bytes) return fail(CMOE_ERR_NULL, "bytes is NULL");
@@ -341,16 +393,12 @@ static cmoe_status forward_impl(const cmoe_problem* problem, const cmoe_weights*
   plan.budget = budget;
   plan.panels = w->layout == CMOE_LAYOUT_PANELS;
   plan.act8 = act8;
-  if (act8 && (!plan.x8 || !cmoe::expert_many_fits(plan, true) || !cmoe::expert_many_fits(plan, false)))
-    return fail(CMOE_ERR_UNSUPPORTED,
-                "activation_fp8 needs fp8 weights with bf16 activations, inter=512, shared_inter 0 or "
-                "512, hidden 512, 1024 or 2048 and work tiles of 32 rows or more (N*top_k above about "
-                "4/3 per expert); here weight=%d act=%d inter=%d shared_inter=%d hidden=%d, tile rows %d",
-                p.weight_dtype, p.act_dtype, p.inter, p.shared_inter, p.hidden, plan.tile_rows);
+  if (act8 && !cmoe::act8_fits(plan)) return act8_unsupported(p, plan);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   // few routed pairs: the down GEMM writes `out` itself (stage 4 is empty)
-  const bool fused = cmoe::down_combine_fits(plan);
+  const cmoe::KernelChoice kc = cmoe::choose_kernels(plan);
+  const bool fused = kc.fused;
   for (int stage = 0; stage <= CLOVER_MOE_NUM_STAGES && e == hipSuccess; ++stage) {
     if (events) {
       e = hipEventRecord(static_cast<hipEvent_t>(events[stage]), st);
@@ -363,15 +411,15 @@ static cmoe_status forward_impl(const cmoe_problem* problem, const cmoe_weights*
         if (e == hipSuccess && plan.B > 1) e = cmoe::launch_permute_blocks(plan, st);
         break;
       case 2:
-        e = plan.mt_max == 1                       ? cmoe::launch_expert_up(plan, *w, x, st)
-            : cmoe::expert_many_fits(plan, true) ? cmoe::launch_expert_many(plan, *w, x, true, st)
-                                                   : cmoe::launch_expert_tiled(plan, *w, x, true, st);
+        e = kc.up == CMOE_GEMM_REGISTER     ? cmoe::launch_expert_up(plan, *w, x, st)
+            : kc.up == CMOE_GEMM_PERSISTENT ? cmoe::launch_expert_many(plan, *w, x, true, st)
+                                            : cmoe::launch_expert_tiled(plan, *w, x, true, st);
         break;
       case 3:
-        e = fused                                   ? cmoe::launch_expert_down_combine(plan, *w, out, st)
-            : plan.mt_max == 1                      ? cmoe::launch_expert_down(plan, *w, st)
-            : cmoe::expert_many_fits(plan, false) ? cmoe::launch_expert_many(plan, *w, x, false, st)
-                                                    : cmoe::launch_expert_tiled(plan, *w, x, false, st);
+        e = kc.down == CMOE_GEMM_DOWN_COMBINE ? cmoe::launch_expert_down_combine(plan, *w, out, st)
+            : kc.down == CMOE_GEMM_REGISTER   ? cmoe::launch_expert_down(plan, *w, st)
+            : kc.down == CMOE_GEMM_PERSISTENT ? cmoe::launch_expert_many(plan, *w, x, false, st)
+                                              : cmoe::launch_expert_tiled(plan, *w, x, false, st);
         break;
       case 4:
         if (!fused) e = cmoe::launch_combine(plan, out, st);

@@ -72,6 +72,17 @@ size_t workspace_bytes(const cmoe_problem& pr, int top_k);
 // Carves the workspace; routing buffers given by the caller replace the
 // workspace copies where the layout is the same.
 void carve(Plan& p, const cmoe_problem& pr, int top_k, void* ws, const cmoe_routing* rt);
+// sizes, dtypes and the work-tile plan only (no workspace, pointers untouched)
+void plan_shape(Plan& p, const cmoe_problem& pr, int top_k);
+// fp8 activations cover the call (buffers planned, both GEMMs have the kernel)
+bool act8_fits(const Plan& p);
+// the kernels of stages 2 and 3 (cmoe_gemm_kind); fused: the down GEMM writes
+// out and stage 4 is empty
+struct KernelChoice {
+  int up, down;
+  bool fused;
+};
+KernelChoice choose_kernels(const Plan& p);
 
 // XCD-aware work mapping for the LDS-tiled grouped GEMMs.  Workgroups are
 // dispatched to the 8 XCDs round-robin by id, and each XCD has its own L2;

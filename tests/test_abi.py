@@ -252,3 +252,57 @@ def test_invalid_pack_calls_rejected(args, expect):
     assert lib.clover_moe_pack_weights(a["src"], a["dst"], a["count"], a["rows"], a["row_bytes"],
                                        a["gate_up"], None) == expect
     assert cm.clover_moe_last_error()
+
+
+# The kernel plan (host-only).  Model shapes: H 2048, 256 experts, top-8,
+# I = Is = 512, blocks of 32 rows unless stated; the mean rows per expert is
+# N*8/256.  Expected: (tile_rows, gate_up, down, y_bytes, kernels per call).
+@pytest.mark.parametrize("pkw,act8,expect", [
+    (dict(), 0, (16, "register", "register", 4, 5)),                                 # one block
+    (dict(block_rows=1), 0, (16, "register", "down_combine", 4, 4)),                 # decode: 9 tiles
+    (dict(block_rows=4), 0, (16, "register", "register", 4, 5)),                     # verify-4: 33 tiles
+    (dict(weight_dtype="fp8_e4m3"), 0, (16, "register", "register", 4, 5)),
+    (dict(weight_dtype="fp8_e4m3", num_blocks=2), 0, (32, "lds_tiled", "lds_tiled", 2, 7)),  # fp8 crossover
+    (dict(num_blocks=5), 0, (16, "register", "register", 4, 7)),
+    (dict(num_blocks=6), 0, (32, "lds_tiled", "lds_tiled", 2, 7)),                   # bf16 crossover
+    (dict(weight_dtype="fp4_e2m1", num_blocks=10), 0, (16, "register", "register", 4, 7)),
+    (dict(weight_dtype="fp4_e2m1", num_blocks=16), 0, (32, "lds_tiled", "persistent", 2, 7)),
+    (dict(num_blocks=64), 0, (96, "lds_tiled", "lds_tiled", 2, 7)),                  # bf16 down: 128 rows
+    (dict(num_blocks=128), 0, (128, "lds_tiled", "persistent", 2, 7)),
+    (dict(weight_dtype="fp8_e4m3", num_blocks=32), 0, (64, "lds_tiled", "lds_tiled", 2, 7)),
+    (dict(weight_dtype="fp8_e4m3", num_blocks=64), 0, (96, "lds_tiled", "persistent", 2, 7)),  # fp8 down: 96
+    (dict(weight_dtype="fp8_e4m3", num_blocks=64), 1, (96, "persistent", "persistent", 2, 8)),
+    (dict(weight_dtype="fp8_e4m3", num_blocks=2), 1, (32, "persistent", "persistent", 2, 8)),
+    (dict(weight_dtype="fp8_e4m3", num_blocks=64, inter=1024), 0, (96, "lds_tiled", "lds_tiled", 2, 7)),
+    (dict(act_dtype="f32", weight_dtype="f32", num_blocks=16), 0, (32, "lds_tiled", "lds_tiled", 4, 7)),
+])
+def test_plan_info_kernel_choice(pkw, act8, expect):
+    opts = cm.make_options(activation_fp8=act8) if act8 else None
+    got = cm.clover_moe_plan_info(problem(**pkw), 8, opts)
+    assert (got["tile_rows"], got["gate_up"], got["down"], got["y_bytes"], got["kernels"]) == expect
+
+
+def test_plan_info_tile_height_follows_mean_rows():
+    # the smallest 16*mt (mt in 1, 2, 4, 6, 8) at or above 1.5x the mean rows per expert
+    for nb, rows in ((16, 32), (24, 64), (32, 64), (40, 64), (48, 96), (64, 96), (80, 128), (512, 128)):
+        assert cm.clover_moe_plan_info(problem(num_blocks=nb), 8)["tile_rows"] == rows, nb
+
+
+@pytest.mark.parametrize("pkw,k,act8,expect", [
+    (dict(block_rows=12), 8, 0, cm.CMOE_ERR_UNSUPPORTED),
+    (dict(num_blocks=0), 8, 0, cm.CMOE_ERR_VALUE),
+    (dict(), 0, 0, cm.CMOE_ERR_VALUE),
+    (dict(), 8, 2, cm.CMOE_ERR_VALUE),
+    (dict(weight_dtype="fp8_e4m3"), 8, 1, cm.CMOE_ERR_UNSUPPORTED),   # 16-row tiles
+    (dict(num_blocks=64), 8, 1, cm.CMOE_ERR_UNSUPPORTED),             # bf16 weights
+])
+def test_plan_info_rejects_what_the_call_rejects(pkw, k, act8, expect):
+    lib = cm.load_library()
+    info = cm.cmoe_plan_info()
+    opts = cm.make_options(activation_fp8=act8)
+    prob = problem(**pkw)
+    assert lib.clover_moe_plan_info(ctypes.byref(prob), k, ctypes.byref(opts), ctypes.byref(info)) == expect
+    assert cm.clover_moe_last_error()
+    if not pkw.get("block_rows") and pkw.get("num_blocks", 1) and k and act8 != 2:
+        assert call_ex(opts, prob=prob, fp8=pkw.get("weight_dtype") == "fp8_e4m3", k=k) == expect
+    assert lib.clover_moe_plan_info(ctypes.byref(problem()), 8, None, None) == cm.CMOE_ERR_NULL
